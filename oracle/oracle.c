@@ -1,0 +1,248 @@
+/*
+ * Plain CPU oracle for the MoE routing path: router, counting-sort dispatch,
+ * weighted combine.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
+ * call this file; only the test suite, the smoke check and the CPU-baseline
+ * leg of the benchmark use it.  It shares no code, header, table or helper
+ * with the HIP library.
+ *
+ * Every floating-point quantity is decoded from its storage bits to IEEE
+ * double and computed in double with naive loops, in the order the method
+ * states it.  Results are rounded once, at the end, to their storage type.
+ * Build with strict IEEE semantics (no -ffast-math, -ffp-contract=off).
+ *
+ * Sources (the pages are cited by title and section):
+ *  [R] "moe-engine: sparse MoE training infrastructure for 10k-GPU clusters"
+ *      (zingnex.cn), section "Fused Triton routing kernel" (核心组件深度解析 ›
+ *      融合Triton路由内核): the gate is tokens @ gate_w, then a softmax over
+ *      the experts, then top-K, then renormalisation of the K kept weights.
+ *      Section "Token conservation check" (Token守恒验证): the per-expert
+ *      dispatch counts sum to N*K.
+ *  [D] "Building a MoE training stack in 10k lines of Python" (yunpan.plus),
+ *      section 8 "Expert-parallel dispatch" (八、专家并行 dispatch), 8.2
+ *      "O(n) counting sort instead of O(n log n) argsort": per-expert
+ *      bincount, prefix sum, then a counting-sort scatter that yields the
+ *      expand index.
+ *  [A] same page, section 6.1 "Model protocol first" (6.1 模型协议先行):
+ *      forward_aggregate takes the expert outputs, the index that undoes the
+ *      dispatch and the top-K weights, and forms the weighted expert output.
+ *
+ * Readings where the pages are silent (each listed in the design notes):
+ *  - the optional per-expert bias is part of the logits, added before the
+ *    softmax;
+ *  - experts are ranked by logit, descending; equal logits go to the lower
+ *    expert index;
+ *  - dispatch keeps no capacity limit and drops nothing; inside one expert's
+ *    segment rows appear in ascending flat slot order n*K+k (stable);
+ *  - combine sums k = 0..K-1 in ascending order and rounds once.
+ *
+ * Return codes: 0 on success, -1 on an argument this oracle does not accept.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_F32 0
+#define ORACLE_BF16 1
+
+/* ---- storage decode / encode (data handling, not the method) ---------- */
+
+/* bf16 is the upper half of an IEEE binary32; widening is exact. */
+static double bf16_to_double(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+static double load_elem(const void *base, int64_t idx, int dtype) {
+  if (dtype == ORACLE_BF16) return bf16_to_double(((const uint16_t *)base)[idx]);
+  return (double)((const float *)base)[idx];
+}
+
+/* Round a double to the nearest bf16, ties to even, in ONE rounding step.
+ * bf16 keeps 8 significant bits (7 stored) and binary32's exponent range;
+ * below 2^-126 its spacing is fixed at 2^-133.  v / q is an exact power-of-two
+ * scaling, and rint() rounds half to even in the default rounding mode. */
+static uint16_t double_to_bf16(double v) {
+  if (isnan(v)) return 0x7FC0;
+  if (v == 0.0) return signbit(v) ? 0x8000 : 0x0000;
+  int e;
+  frexp(v, &e);           /* |v| = m * 2^e with m in [0.5, 1) */
+  int unbiased = e - 1;   /* |v| = m' * 2^unbiased with m' in [1, 2) */
+  double q = unbiased < -126 ? ldexp(1.0, -133) : ldexp(1.0, unbiased - 7);
+  double r = rint(v / q) * q;
+  if (fabs(r) >= ldexp(1.0, 128)) return signbit(v) ? 0xFF80 : 0x7F80;
+  float f = (float)r; /* exact: r has at most 8 significant bits */
+  uint32_t u;
+  memcpy(&u, &f, sizeof u);
+  return (uint16_t)(u >> 16);
+}
+
+/* ---- [R] router -------------------------------------------------------- */
+
+/*
+ * oracle_route: for each token n
+ *   logits[n,e] = sum_h x[n,h] * gate_w[h,e]  (+ bias[e])        (h ascending)
+ *   order experts by (logit desc, index asc); ids[n,0..K-1] = first K
+ *   p[n,e]  = exp(logit[n,e] - max_e logit) / sum_e exp(logit[n,e] - max)
+ *   w[n,k]  = p[n,ids[n,k]] / sum_j p[n,ids[n,j]], rounded once to fp32
+ *   margin[n] = logit of the K-th chosen expert minus the (K+1)-th, or
+ *               +inf when K == E.
+ * x [N,H] and gate_w [H,E] are row-major in `dtype`; bias [E] fp32 or NULL.
+ * logits_out [N,E] (double) and margin [N] (double) may be NULL.
+ */
+int oracle_route(const void *x, const void *gate_w, const float *bias, int64_t N,
+                 int32_t H, int32_t E, int32_t K, int32_t dtype, int32_t *ids,
+                 float *w, double *logits_out, double *margin) {
+  if (N < 0 || H <= 0 || E <= 0 || K < 1 || K > E) return -1;
+  if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return -1;
+  double *logit = (double *)malloc(sizeof(double) * (size_t)E);
+  double *p = (double *)malloc(sizeof(double) * (size_t)E);
+  int32_t *order = (int32_t *)malloc(sizeof(int32_t) * (size_t)E);
+  if (!logit || !p || !order) {
+    free(logit); free(p); free(order);
+    return -1;
+  }
+  for (int64_t n = 0; n < N; ++n) {
+    /* logits: a plain dot product per expert, h in ascending order */
+    for (int32_t e = 0; e < E; ++e) logit[e] = 0.0;
+    for (int32_t h = 0; h < H; ++h) {
+      double xv = load_elem(x, n * (int64_t)H + h, dtype);
+      for (int32_t e = 0; e < E; ++e)
+        logit[e] += xv * load_elem(gate_w, (int64_t)h * E + e, dtype);
+    }
+    if (bias)
+      for (int32_t e = 0; e < E; ++e) logit[e] += (double)bias[e];
+    if (logits_out)
+      for (int32_t e = 0; e < E; ++e) logits_out[n * (int64_t)E + e] = logit[e];
+
+    /* full ordering of the experts by (logit desc, index asc):
+     * insertion sort, which is stable, over indices 0..E-1 */
+    for (int32_t e = 0; e < E; ++e) order[e] = e;
+    for (int32_t i = 1; i < E; ++i) {
+      int32_t cur = order[i];
+      int32_t j = i - 1;
+      while (j >= 0 && logit[order[j]] < logit[cur]) {
+        order[j + 1] = order[j];
+        --j;
+      }
+      order[j + 1] = cur;
+    }
+    for (int32_t k = 0; k < K; ++k) ids[n * K + k] = order[k];
+    if (margin)
+      margin[n] = (K == E) ? INFINITY : logit[order[K - 1]] - logit[order[K]];
+
+    /* softmax over all E experts */
+    double mx = logit[0];
+    for (int32_t e = 1; e < E; ++e)
+      if (logit[e] > mx) mx = logit[e];
+    double z = 0.0;
+    for (int32_t e = 0; e < E; ++e) {
+      p[e] = exp(logit[e] - mx);
+      z += p[e];
+    }
+    for (int32_t e = 0; e < E; ++e) p[e] /= z;
+
+    /* renormalise the K kept probabilities */
+    double s = 0.0;
+    for (int32_t k = 0; k < K; ++k) s += p[order[k]];
+    for (int32_t k = 0; k < K; ++k) w[n * K + k] = (float)(p[order[k]] / s);
+  }
+  free(logit);
+  free(p);
+  free(order);
+  return 0;
+}
+
+/* ---- [D] counting-sort dispatch --------------------------------------- */
+
+/*
+ * oracle_dispatch: ids [N,K] row-major, read as the flat slot list
+ * i = n*K + k.
+ *   counts[e]   = number of slots with ids[i] == e
+ *   offsets[0]  = 0, offsets[e+1] = offsets[e] + counts[e]   (E+1 entries)
+ *   counting sort, slots visited in ascending i:
+ *       r = cursor[ids[i]]++ (cursor starts at offsets),  perm[r] = i,
+ *       inv[i] = r.
+ * Returns -1 if an id lies outside [0,E).
+ */
+int oracle_dispatch(const int32_t *ids, int64_t N, int32_t K, int32_t E,
+                    int32_t *counts, int32_t *offsets, int32_t *perm,
+                    int32_t *inv) {
+  if (N < 0 || K < 1 || E <= 0) return -1;
+  int64_t T = N * (int64_t)K;
+  for (int32_t e = 0; e < E; ++e) counts[e] = 0;
+  for (int64_t i = 0; i < T; ++i) {
+    if (ids[i] < 0 || ids[i] >= E) return -1;
+    counts[ids[i]] += 1;
+  }
+  offsets[0] = 0;
+  for (int32_t e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + counts[e];
+  int32_t *cursor = (int32_t *)malloc(sizeof(int32_t) * (size_t)E);
+  if (!cursor) return -1;
+  for (int32_t e = 0; e < E; ++e) cursor[e] = offsets[e];
+  for (int64_t i = 0; i < T; ++i) {
+    int32_t r = cursor[ids[i]]++;
+    perm[r] = (int32_t)i;
+    inv[i] = r;
+  }
+  free(cursor);
+  return 0;
+}
+
+/*
+ * oracle_permute_rows: x_perm[r,:] = x[perm[r] / K, :] for r in [0, N*K),
+ * a byte copy of rows of `row_bytes` bytes.
+ */
+int oracle_permute_rows(const void *x, int64_t N, int32_t K, int64_t row_bytes,
+                        const int32_t *perm, void *x_perm) {
+  if (N < 0 || K < 1 || row_bytes <= 0) return -1;
+  int64_t T = N * (int64_t)K;
+  const unsigned char *src = (const unsigned char *)x;
+  unsigned char *dst = (unsigned char *)x_perm;
+  for (int64_t r = 0; r < T; ++r) {
+    int64_t n = perm[r] / K;
+    if (n < 0 || n >= N) return -1;
+    memcpy(dst + r * row_bytes, src + n * row_bytes, (size_t)row_bytes);
+  }
+  return 0;
+}
+
+/* ---- [A] weighted combine --------------------------------------------- */
+
+/*
+ * oracle_combine: y [N*K, H] holds the expert outputs in dispatched
+ * (expert-contiguous) row order, inv [N*K] maps slot n*K+k to its row, and
+ * w [N,K] (fp32) are the renormalised gate weights.
+ *   out[n,h] = round( sum_{k=0..K-1} (double)w[n,k] * y[inv[n*K+k], h] )
+ * summed in double with k ascending from 0.0, rounded once to `dtype`
+ * (bf16: nearest, ties to even; fp32: C's double->float conversion).
+ */
+int oracle_combine(const void *y, const int32_t *inv, const float *w, int64_t N,
+                   int32_t H, int32_t K, int32_t dtype, void *out) {
+  if (N < 0 || H <= 0 || K < 1) return -1;
+  if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return -1;
+  int64_t T = N * (int64_t)K;
+  for (int64_t n = 0; n < N; ++n) {
+    for (int32_t h = 0; h < H; ++h) {
+      double acc = 0.0;
+      for (int32_t k = 0; k < K; ++k) {
+        int64_t row = inv[n * K + k];
+        if (row < 0 || row >= T) return -1;
+        acc += (double)w[n * K + k] * load_elem(y, row * H + h, dtype);
+      }
+      if (dtype == ORACLE_BF16)
+        ((uint16_t *)out)[n * (int64_t)H + h] = double_to_bf16(acc);
+      else
+        ((float *)out)[n * (int64_t)H + h] = (float)acc;
+    }
+  }
+  return 0;
+}
+
+/* Exposed for the encode/decode pins only. */
+uint16_t oracle_round_bf16(double v) { return double_to_bf16(v); }
+double oracle_decode_bf16(uint16_t b) { return bf16_to_double(b); }

@@ -1,0 +1,151 @@
+"""numpy front end of the C oracle (test infrastructure only).
+
+Arrays are passed to oracle.c by pointer; all arithmetic happens there, in
+IEEE double.  bf16 tensors travel as their raw uint16 bit patterns, fp32 as
+float32.  See oracle.c for the definitions and the pages they follow:
+  route    - moe-engine page, "Fused Triton routing kernel" section
+  dispatch - PithTrain page, section 8.2 (counting sort instead of argsort)
+  combine  - PithTrain page, section 6.1 (forward_aggregate)
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+# MOE_ORACLE_LIB lets the mutation test load a deliberately broken build of
+# oracle.c to show that the pins catch it.
+_LIB_PATH = os.environ.get("MOE_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+DTYPES = {"f32": 0, "bf16": 1}
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            from . import build as _build
+            _build.build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        P = ctypes.c_void_p
+        i32, i64, dbl = ctypes.c_int32, ctypes.c_int64, ctypes.c_double
+        lib.oracle_route.argtypes = [P, P, P, i64, i32, i32, i32, i32, P, P, P, P]
+        lib.oracle_route.restype = ctypes.c_int
+        lib.oracle_dispatch.argtypes = [P, i64, i32, i32, P, P, P, P]
+        lib.oracle_dispatch.restype = ctypes.c_int
+        lib.oracle_permute_rows.argtypes = [P, i64, i32, i64, P, P]
+        lib.oracle_permute_rows.restype = ctypes.c_int
+        lib.oracle_combine.argtypes = [P, P, P, i64, i32, i32, i32, P]
+        lib.oracle_combine.restype = ctypes.c_int
+        lib.oracle_round_bf16.argtypes = [dbl]
+        lib.oracle_round_bf16.restype = ctypes.c_uint16
+        lib.oracle_decode_bf16.argtypes = [ctypes.c_uint16]
+        lib.oracle_decode_bf16.restype = dbl
+        _lib = lib
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _storage(a, dtype):
+    want = np.uint16 if dtype == "bf16" else np.float32
+    a = np.ascontiguousarray(a)
+    if a.dtype != want:
+        raise TypeError(f"{dtype} data must be passed as {want.__name__}, got {a.dtype}")
+    return a
+
+
+def route(x, gate_w, bias, K, dtype):
+    """Router: logits, top-K ids, renormalised weights, K-th/(K+1)-th margin.
+
+    x [N,H], gate_w [H,E] in `dtype` storage; bias [E] float32 or None.
+    Returns (ids int32 [N,K], w float32 [N,K], logits float64 [N,E],
+    margin float64 [N]).
+    """
+    x = _storage(x, dtype)
+    gate_w = _storage(gate_w, dtype)
+    N, H = x.shape
+    H2, E = gate_w.shape
+    if H2 != H:
+        raise ValueError("gate_w must be [H, E]")
+    if bias is not None:
+        bias = np.ascontiguousarray(bias, dtype=np.float32)
+        if bias.shape != (E,):
+            raise ValueError("bias must be [E]")
+    ids = np.empty((N, K), np.int32)
+    w = np.empty((N, K), np.float32)
+    logits = np.empty((N, E), np.float64)
+    margin = np.empty((N,), np.float64)
+    rc = _load().oracle_route(_ptr(x), _ptr(gate_w), _ptr(bias), N, H, E, K,
+                              DTYPES[dtype], _ptr(ids), _ptr(w), _ptr(logits),
+                              _ptr(margin))
+    if rc != 0:
+        raise ValueError("oracle_route rejected its arguments")
+    return ids, w, logits, margin
+
+
+def dispatch(ids, E):
+    """Counting-sort dispatch metadata.
+
+    ids int32 [N,K].  Returns (counts [E], offsets [E+1], perm [N*K],
+    inv [N*K]), all int32; perm maps dispatched row -> flat slot n*K+k and
+    inv maps slot -> row.
+    """
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    N, K = ids.shape
+    counts = np.empty((E,), np.int32)
+    offsets = np.empty((E + 1,), np.int32)
+    perm = np.empty((N * K,), np.int32)
+    inv = np.empty((N * K,), np.int32)
+    rc = _load().oracle_dispatch(_ptr(ids), N, K, E, _ptr(counts), _ptr(offsets),
+                                 _ptr(perm), _ptr(inv))
+    if rc != 0:
+        raise ValueError("oracle_dispatch rejected its arguments")
+    return counts, offsets, perm, inv
+
+
+def permute_rows(x, perm, K):
+    """x_perm[r] = x[perm[r] // K], a byte copy; x is any 2-D array."""
+    x = np.ascontiguousarray(x)
+    perm = np.ascontiguousarray(perm, dtype=np.int32)
+    N = x.shape[0]
+    out = np.empty((perm.shape[0],) + x.shape[1:], x.dtype)
+    rc = _load().oracle_permute_rows(_ptr(x), N, K, x[0:1].nbytes if N else 1,
+                                     _ptr(perm), _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle_permute_rows rejected its arguments")
+    return out
+
+
+def combine(y, inv, w, dtype):
+    """Weighted combine: out[n] = sum_k w[n,k] * y[inv[n*K+k]], rounded once.
+
+    y [N*K, H] in `dtype` storage, inv int32 [N*K], w float32 [N,K].
+    Returns out [N,H] in `dtype` storage.
+    """
+    y = _storage(y, dtype)
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    inv = np.ascontiguousarray(inv, dtype=np.int32)
+    N, K = w.shape
+    H = y.shape[1]
+    if y.shape[0] != N * K or inv.shape != (N * K,):
+        raise ValueError("y must be [N*K, H] and inv [N*K]")
+    out = np.empty((N, H), y.dtype)
+    rc = _load().oracle_combine(_ptr(y), _ptr(inv), _ptr(w), N, H, K,
+                                DTYPES[dtype], _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle_combine rejected its arguments")
+    return out
+
+
+def round_bf16(v):
+    """One-step nearest-even rounding of a Python float to bf16 bits."""
+    return int(_load().oracle_round_bf16(float(v)))
+
+
+def decode_bf16(bits):
+    """bf16 bit pattern -> float (exact)."""
+    return float(_load().oracle_decode_bf16(int(bits)))

@@ -1,0 +1,366 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+None of these re-types the oracle's own formula: each compares it with a
+closed form, an invariant, a library routine that computes the same defined
+quantity in another way, brute force on tiny inputs, or a hand-derived
+fixture under tests/golden/.  Runs on the CPU (no GPU marker).
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+
+from oracle import oracle as O
+from moe_token_routing_router_amd import inputs as I
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_examples.json")
+
+
+def _golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+def _decode(a, dtype):
+    """Independent widening of the storage bits to float64 for the checks."""
+    if dtype == "f32":
+        return np.asarray(a, np.float32).astype(np.float64)
+    u = np.asarray(a, np.uint16).astype(np.uint32) << np.uint32(16)
+    return u.view(np.float32).astype(np.float64)
+
+
+def _store(a, dtype):
+    a = np.asarray(a, np.float32)
+    return a if dtype == "f32" else I.f32_to_bf16_bits(a)
+
+
+# ---------------------------------------------------------------- bf16 codec
+
+def test_bf16_decode_known_patterns():
+    assert O.decode_bf16(0x3F80) == 1.0
+    assert O.decode_bf16(0xC000) == -2.0
+    assert O.decode_bf16(0x0000) == 0.0
+    assert O.decode_bf16(0x0001) == 2.0 ** -133          # smallest subnormal
+    assert O.decode_bf16(0x7F7F) == (2 - 2 ** -7) * 2.0 ** 127  # largest finite
+    assert O.decode_bf16(0x3E80) == 0.25
+
+
+def test_bf16_round_ties_and_single_rounding():
+    assert O.round_bf16(1.0) == 0x3F80
+    assert O.round_bf16(1 + 2 ** -8) == 0x3F80           # tie -> even (down)
+    assert O.round_bf16(1 + 3 * 2 ** -8) == 0x3F82       # tie -> even (up)
+    assert O.round_bf16(1 + 2 ** -8 + 2 ** -30) == 0x3F81
+    # one rounding step: through float32 first this would tie and go down
+    assert O.round_bf16(1 + 2 ** -8 + 2 ** -40) == 0x3F81
+    assert O.round_bf16(-1.5) == 0xBFC0
+    assert O.round_bf16(2.0 ** -134) == 0x0000           # subnormal tie -> even
+    assert O.round_bf16(3 * 2.0 ** -134) == 0x0002
+    assert O.round_bf16(2.0 ** 130) == 0x7F80            # overflow -> inf
+    assert O.round_bf16(-0.0) == 0x8000
+
+
+def test_bf16_round_matches_generator_rne_on_float32_values():
+    # For values that are already float32, one rounding from double equals the
+    # generator's integer RNE trick on the float32 bits (a different method).
+    rng = np.random.default_rng(7)
+    v = (rng.standard_normal(2000) * np.exp(rng.uniform(-20, 20, 2000))).astype(np.float32)
+    want = I.f32_to_bf16_bits(v)
+    got = np.array([O.round_bf16(float(t)) for t in v], np.uint16)
+    np.testing.assert_array_equal(got, want)
+
+
+# ---------------------------------------------------------------- router
+
+def test_router_hand_examples():
+    g = _golden()
+    for key in ("router_tie", "router_bias"):
+        c = g[key]
+        for dtype in ("f32", "bf16"):
+            x = _store(c["x"], dtype)
+            wg = _store(c["gate_w"], dtype)
+            bias = None if c["bias"] is None else np.asarray(c["bias"], np.float32)
+            ids, w, logits, margin = O.route(x, wg, bias, c["K"], dtype)
+            np.testing.assert_array_equal(ids, c["ids"])
+            np.testing.assert_array_equal(logits, c["logits"])
+            np.testing.assert_allclose(w, c["w"], rtol=0, atol=1e-7)
+            np.testing.assert_array_equal(margin, c["margin"])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("seed", range(6))
+def test_router_logits_match_numpy_matmul(dtype, seed):
+    # P0: logits equal the float64 matrix product (+ bias) from numpy's BLAS.
+    rng = np.random.default_rng(seed)
+    N, H, E = int(rng.integers(1, 40)), int(rng.integers(1, 70)), int(rng.integers(2, 33))
+    K = int(rng.integers(1, E + 1))
+    case = I.random_case(100 + seed, N, H, E, K, dtype, bias=bool(seed % 2), with_y=False)
+    ids, w, logits, margin = O.route(case["x"], case["gate_w"], case["bias"], K, dtype)
+    ref = _decode(case["x"], dtype) @ _decode(case["gate_w"], dtype)
+    if case["bias"] is not None:
+        ref = ref + case["bias"].astype(np.float64)[None, :]
+    np.testing.assert_allclose(logits, ref, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_router_selection_is_stable_argsort_bruteforce(dtype):
+    # P1/P2: ids are the first K of a stable descending argsort of the logits
+    # computed independently by numpy; they are distinct and in range.
+    for seed in range(40):
+        rng = np.random.default_rng(1000 + seed)
+        N, H, E = int(rng.integers(1, 30)), int(rng.integers(1, 50)), int(rng.integers(1, 20))
+        K = int(rng.integers(1, E + 1))
+        case = I.random_case(seed, N, H, E, K, dtype, bias=True, with_y=False)
+        ids, w, logits, margin = O.route(case["x"], case["gate_w"], case["bias"], K, dtype)
+        ref_logits = _decode(case["x"], dtype) @ _decode(case["gate_w"], dtype) \
+            + case["bias"].astype(np.float64)[None, :]
+        order = np.argsort(-ref_logits, axis=1, kind="stable")
+        np.testing.assert_array_equal(ids, order[:, :K])
+        assert ids.min() >= 0 and ids.max() < E
+        for row in ids:
+            assert len(set(row.tolist())) == K
+        srt = -np.sort(-ref_logits, axis=1)
+        want_margin = (srt[:, K - 1] - srt[:, K]) if K < E else np.full(N, np.inf)
+        np.testing.assert_allclose(margin, want_margin, rtol=0, atol=1e-12)
+
+
+def test_router_ties_go_to_lower_index():
+    # duplicated gate columns produce bit-identical logits; the lower index wins
+    rng = np.random.default_rng(3)
+    H, E = 16, 8
+    wg = (rng.standard_normal((H, E)) / 4).astype(np.float32)
+    wg[:, 6] = wg[:, 1]
+    wg[:, 4] = wg[:, 1]
+    x = rng.standard_normal((64, H)).astype(np.float32)
+    ids, w, logits, _ = O.route(x, wg, None, E, "f32")
+    for n in range(64):
+        pos = {int(e): i for i, e in enumerate(ids[n])}
+        assert pos[1] < pos[4] < pos[6]
+        assert pos[6] == pos[1] + 2  # the three tied experts are adjacent
+
+
+@pytest.mark.parametrize("K", [1, 2, 3, 7])
+def test_router_zero_token_closed_form(K):
+    # an all-zero token has all-equal logits: ids 0..K-1, weights exactly 1/K
+    E, H = 7, 12
+    x = np.zeros((3, H), np.float32)
+    wg = np.random.default_rng(0).standard_normal((H, E)).astype(np.float32)
+    ids, w, _, margin = O.route(x, wg, None, K, "f32")
+    np.testing.assert_array_equal(ids, np.tile(np.arange(K), (3, 1)))
+    np.testing.assert_allclose(w, np.float32(1.0 / K), rtol=0, atol=0)
+    if K < E:
+        assert (margin == 0).all()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_router_weight_invariants(dtype):
+    # P4 sum to one, P5 K=1 gives exactly 1, P6 equal softmax over the chosen
+    # logits (closed form of renormalising the full softmax), P7 K=E gives
+    # the full softmax (scipy's routine).
+    for seed in range(20):
+        rng = np.random.default_rng(2000 + seed)
+        N, H, E = int(rng.integers(1, 25)), int(rng.integers(1, 40)), int(rng.integers(1, 17))
+        case = I.random_case(seed, N, H, E, 1, dtype, bias=bool(seed % 3), with_y=False)
+        x, wg, b = case["x"], case["gate_w"], case["bias"]
+        # K=1
+        ids, w, logits, _ = O.route(x, wg, b, 1, dtype)
+        assert (w == 1.0).all()
+        # general K
+        K = int(rng.integers(1, E + 1))
+        ids, w, logits, _ = O.route(x, wg, b, K, dtype)
+        np.testing.assert_allclose(w.astype(np.float64).sum(1), 1.0, rtol=0, atol=1e-6)
+        sel = np.take_along_axis(logits, ids.astype(np.int64), axis=1)
+        closed = scipy.special.softmax(sel, axis=1)
+        np.testing.assert_allclose(w, closed, rtol=0, atol=1e-7)
+        # K=E: full softmax, in the expert order of ids
+        ids, w, logits, _ = O.route(x, wg, b, E, dtype)
+        full = scipy.special.softmax(logits, axis=1)
+        np.testing.assert_allclose(w, np.take_along_axis(full, ids.astype(np.int64), 1),
+                                   rtol=0, atol=1e-7)
+        np.testing.assert_array_equal(np.sort(ids, axis=1), np.tile(np.arange(E), (N, 1)))
+
+
+def test_router_dominant_bias_selects_that_expert():
+    rng = np.random.default_rng(5)
+    N, H, E = 50, 32, 12
+    case = I.random_case(5, N, H, E, 3, "bf16", with_y=False)
+    bias = np.zeros(E, np.float32)
+    bias[9] = 100.0
+    bias[2] = 50.0
+    ids, w, _, _ = O.route(case["x"], case["gate_w"], bias, 3, "bf16")
+    assert (ids[:, 0] == 9).all() and (ids[:, 1] == 2).all()
+    assert (w[:, 0] > 0.999).all()
+
+
+def test_router_rejects_bad_arguments():
+    x = np.zeros((2, 4), np.float32)
+    with pytest.raises(ValueError):
+        O.route(x, np.zeros((4, 3), np.float32), None, 4, "f32")  # K > E
+    with pytest.raises(ValueError):
+        O.route(x, np.zeros((5, 3), np.float32), None, 2, "f32")  # H mismatch
+
+
+# ---------------------------------------------------------------- dispatch
+
+def test_dispatch_hand_examples():
+    g = _golden()
+    for key in ("dispatch_small", "dispatch_empty_expert"):
+        c = g[key]
+        counts, offsets, perm, inv = O.dispatch(np.array(c["ids"], np.int32), c["E"])
+        np.testing.assert_array_equal(counts, c["counts"])
+        np.testing.assert_array_equal(offsets, c["offsets"])
+        np.testing.assert_array_equal(perm, c["perm"])
+        np.testing.assert_array_equal(inv, c["inv"])
+
+
+def test_dispatch_token_conservation_100_seeds():
+    # moe-engine page, 'Token conservation check': over 100 random seeds the
+    # per-expert counts sum to N*K with no violation.
+    for seed in range(100):
+        rng = np.random.default_rng(seed)
+        E = int(rng.integers(1, 65))
+        K = int(rng.integers(1, min(E, 8) + 1))
+        N = int(rng.integers(0, 300))
+        ids = I.random_ids(seed, N, E, K, skew=float(rng.uniform(0, 2)))
+        counts, offsets, perm, inv = O.dispatch(ids, E)
+        assert counts.sum() == N * K
+        np.testing.assert_array_equal(counts, np.bincount(ids.ravel(), minlength=E))
+        assert offsets[0] == 0 and offsets[E] == N * K
+        assert (np.diff(offsets) == counts).all()
+
+
+def test_dispatch_equals_stable_argsort_bruteforce():
+    # P9: the counting sort equals numpy's stable argsort of the flat ids on
+    # hundreds of tiny inputs; inv is the inverse permutation.
+    for seed in range(400):
+        rng = np.random.default_rng(10_000 + seed)
+        E = int(rng.integers(1, 9))
+        K = int(rng.integers(1, min(E, 3) + 1))
+        N = int(rng.integers(0, 65))
+        ids = I.random_ids(seed, N, E, K, skew=float(rng.uniform(0, 3)))
+        counts, offsets, perm, inv = O.dispatch(ids, E)
+        flat = ids.ravel()
+        np.testing.assert_array_equal(perm, np.argsort(flat, kind="stable"))
+        np.testing.assert_array_equal(inv[perm], np.arange(N * K))
+        assert (np.diff(flat[perm]) >= 0).all()
+        for e in range(E):
+            seg = perm[offsets[e]:offsets[e + 1]]
+            assert (np.diff(seg) > 0).all()
+
+
+def test_dispatch_rejects_out_of_range_ids():
+    with pytest.raises(ValueError):
+        O.dispatch(np.array([[0, 4]], np.int32), 4)
+    with pytest.raises(ValueError):
+        O.dispatch(np.array([[-1, 0]], np.int32), 4)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_permute_rows_is_row_gather(dtype):
+    # P10: x_perm[r] is bitwise x[perm[r] // K] (numpy fancy indexing)
+    case = I.random_case(9, 37, 24, 6, 3, dtype, with_y=False)
+    ids = I.random_ids(9, 37, 6, 3)
+    _, _, perm, _ = O.dispatch(ids, 6)
+    xp = O.permute_rows(case["x"], perm, 3)
+    np.testing.assert_array_equal(xp.view(np.uint8), case["x"][perm // 3].view(np.uint8))
+
+
+# ---------------------------------------------------------------- combine
+
+def test_combine_hand_example():
+    c = _golden()["combine_small"]
+    for dtype in ("f32", "bf16"):
+        out = O.combine(_store(c["y"], dtype), np.array(c["inv"], np.int32),
+                        np.array(c["w"], np.float32), dtype)
+        np.testing.assert_array_equal(_decode(out, dtype), c["out"])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_combine_one_hot_is_pure_gather(dtype):
+    # P11: weight 1 on k=0 and 0 elsewhere gives the dispatched row of slot n*K
+    N, H, E, K = 29, 40, 5, 3
+    case = I.random_case(11, N, H, E, K, dtype)
+    ids = I.random_ids(11, N, E, K)
+    _, _, _, inv = O.dispatch(ids, E)
+    w = np.zeros((N, K), np.float32)
+    w[:, 0] = 1.0
+    out = O.combine(case["y"], inv, w, dtype)
+    np.testing.assert_array_equal(out.view(np.uint8), case["y"][inv[0::K]].view(np.uint8))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_round_trip_identity_experts(dtype):
+    # P12: route -> dispatch -> (identity experts: y = x_perm) -> combine
+    # returns x.  With the weights summing to 1 within a few fp32 ulps, every
+    # output element is x times (1 + delta) with |delta| far below half an ulp
+    # of the storage type, so it rounds back to x exactly (bf16); fp32 keeps
+    # a few ulps.
+    for seed in range(5):
+        N, H, E, K = 61, 48, 9, 4
+        case = I.random_case(seed, N, H, E, K, dtype, bias=True, with_y=False)
+        ids, w, _, _ = O.route(case["x"], case["gate_w"], case["bias"], K, dtype)
+        counts, offsets, perm, inv = O.dispatch(ids, E)
+        xp = O.permute_rows(case["x"], perm, K)
+        out = O.combine(xp, inv, w, dtype)
+        if dtype == "bf16":
+            np.testing.assert_array_equal(out, case["x"])
+        else:
+            np.testing.assert_allclose(out, case["x"], rtol=4e-7, atol=0)
+
+
+def test_combine_linear_in_weights_fp32():
+    # P13: with fp32 storage, out(w1 + w2) = out(w1) + out(w2) up to rounding
+    N, H, E, K = 33, 20, 6, 2
+    case = I.random_case(4, N, H, E, K, "f32")
+    ids = I.random_ids(4, N, E, K)
+    _, _, _, inv = O.dispatch(ids, E)
+    rng = np.random.default_rng(4)
+    w1 = rng.uniform(0, 1, (N, K)).astype(np.float32)
+    w2 = rng.uniform(0, 1, (N, K)).astype(np.float32)
+    a = O.combine(case["y"], inv, w1, "f32").astype(np.float64)
+    b = O.combine(case["y"], inv, w2, "f32").astype(np.float64)
+    c = O.combine(case["y"], inv, (w1 + w2).astype(np.float32), "f32").astype(np.float64)
+    np.testing.assert_allclose(c, a + b, rtol=1e-5, atol=1e-5)
+    # scaling all weights by 2 (exact in fp32) scales the output by 2 exactly
+    d = O.combine(case["y"], inv, (2 * w1).astype(np.float32), "f32").astype(np.float64)
+    np.testing.assert_array_equal(d, 2 * a)
+
+
+# ---------------------------------------------------------------- workloads
+
+def test_workload_generator_shapes_and_determinism():
+    d1 = I.make_inputs("small-bf16", with_y=False, n_tokens=64)
+    d2 = I.make_inputs("small-bf16", with_y=True, n_tokens=64)
+    np.testing.assert_array_equal(d1["x"], d2["x"])
+    np.testing.assert_array_equal(d1["gate_w"], d2["gate_w"])
+    assert d2["y"].shape == (128, 1024) and d2["y"].dtype == np.uint16
+    d3 = I.make_inputs("tiny-fp32")
+    assert d3["x"].shape == (512, 256) and d3["x"].dtype == np.float32
+    assert d3["gate_w"].shape == (256, 16)
+    # gate_w ~ N(0, 1/H)
+    g = _decode(I.make_inputs("biased-bf16", with_y=False, n_tokens=1)["gate_w"], "bf16")
+    assert abs(g.std() * math.sqrt(2048) - 1) < 0.02
+
+
+def test_zipf_workload_has_four_dead_experts_and_hot_experts():
+    d = I.make_inputs("zipf128-bf16", with_y=False, n_tokens=1024)
+    assert (d["bias"] == -1e4).sum() == 4
+    ids, w, _, _ = O.route(d["x"], d["gate_w"], d["bias"], 8, "bf16")
+    counts, _, _, _ = O.dispatch(ids, 128)
+    assert (counts == 0).sum() >= 4
+    assert counts[d["bias"] == -1e4].sum() == 0
+    assert counts.max() / counts.mean() > 5
+
+
+def test_combine_rounds_once_to_bf16():
+    # K=2, w = [1 + 2^-8, 2^-10], rows y0 = 1 and y1 = 2^-30: the exact sum is
+    # 1 + 2^-8 + 2^-40, just above the bf16 tie between 1 and 1 + 2^-7, so one
+    # rounding gives 0x3F81.  Rounding through float32 first would land on the
+    # tie and give 0x3F80.
+    y = np.array([[0x3F80], [0x3080]], np.uint16)      # 1.0, 2^-30
+    assert O.decode_bf16(0x3080) == 2.0 ** -30
+    w = np.array([[1 + 2 ** -8, 2 ** -10]], np.float32)
+    out = O.combine(y, np.array([0, 1], np.int32), w, "bf16")
+    assert int(out[0, 0]) == 0x3F81
