@@ -1,0 +1,149 @@
+/*
+ * moe.h -- C ABI of libmoe.so, the MI355X (gfx950) MoE routing path:
+ * route -> counting-sort dispatch -> weighted combine, on one GPU.
+ *
+ * Conventions for every entry point
+ *  - All tensor pointers are DEVICE pointers, row-major, owned by the caller.
+ *    The library never allocates, frees or synchronises; it only enqueues
+ *    kernels on `stream` (a hipStream_t passed as void*, NULL = the null
+ *    stream) and returns.  Outputs are valid once that stream reaches them.
+ *  - Arguments are validated on the host before anything is enqueued; on any
+ *    error nothing is enqueued and a status code is returned.  No entry point
+ *    aborts or throws.
+ *  - Results are bitwise reproducible run to run (integer atomics only, every
+ *    floating-point sum in a fixed order).
+ *  - Sizes: N tokens, H hidden size, E experts, K experts per token,
+ *    T = N*K routed slots; slot i = n*K + k.
+ *  - Limits (MOE_ERR_UNSUPPORTED otherwise): E <= 256, T < 2^31, a row of H
+ *    elements is a multiple of 16 bytes (H % 8 == 0 for bf16, H % 4 == 0 for
+ *    fp32); moe_route additionally needs K <= 16.
+ *  - Alignment (MOE_ERR_MISALIGNED otherwise): x, gate_w, x_perm, y, out and
+ *    the workspaces on 16 bytes; integer and fp32 side arrays on 4 bytes.
+ *
+ * Pages cited (by title and section):
+ *  [R] "moe-engine: sparse MoE training infrastructure for 10k-GPU clusters",
+ *      section "Fused Triton routing kernel" (核心组件深度解析 › 融合Triton路由内核)
+ *      and section "Token conservation check" (Token守恒验证).
+ *  [D] "Building a MoE training stack in 10k lines of Python", section 8.2
+ *      "O(n) counting sort instead of O(n log n) argsort" (8.2 O(n) counting
+ *      sort 替代 O(n log n) argsort).
+ *  [A] same page, section 6.1 "Model protocol first" (6.1 模型协议先行),
+ *      forward_aggregate.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARGUMENT = 1,   /* NULL required pointer, bad size, K > E */
+  MOE_ERR_UNSUPPORTED = 2,        /* outside the limits listed above */
+  MOE_ERR_MISALIGNED = 3,         /* pointer not aligned as listed above */
+  MOE_ERR_WORKSPACE_TOO_SMALL = 4,/* workspace_bytes below the *_workspace_size */
+  MOE_ERR_HIP = 5                 /* a kernel launch reported an error */
+} moe_status_t;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char *moe_status_string(moe_status_t status);
+
+/*
+ * Bytes of device workspace moe_route needs for (H, E, dtype); 0 if none.
+ * (bf16: the gate matrix re-laid out expert-major, padded to a multiple of
+ * 16 experts.)
+ */
+size_t moe_route_workspace_size(int32_t H, int32_t E, moe_dtype_t dtype);
+
+/*
+ * moe_route -- the fused router of [R]: for each token
+ *   logits[n,e] = sum_h x[n,h] * gate_w[h,e] + bias[e]
+ *   ids[n,0..K-1] = the K experts of largest logit, in descending logit
+ *                   order (equal logits: lower expert index first)
+ *   w[n,k] = softmax over all E experts, restricted to the K chosen ones and
+ *            renormalised to sum 1 (equal to the softmax over the K chosen
+ *            logits)
+ * in one pass over x.  The logits never leave the chip.
+ *
+ *   x        [N,H]  dtype    tokens
+ *   gate_w   [H,E]  dtype    gate matrix (tokens @ gate_w)
+ *   bias     [E]    fp32     per-expert logit bias, or NULL for none
+ *   topk_ids [N,K]  int32    out
+ *   topk_w   [N,K]  fp32     out
+ *   counts   [E]    int32    out, optional (NULL to skip): tokens routed to
+ *                            each expert (the dispatch count of [R]'s token
+ *                            conservation check); overwritten, not added to
+ *   workspace >= moe_route_workspace_size(H, E, dtype) bytes (may be NULL
+ *            when that size is 0); contents are scratch
+ * bf16 inputs are multiplied exactly and accumulated in fp32; fp32 inputs
+ * use fp32 fused multiply-adds.  N == 0 is a valid no-op (counts zeroed).
+ */
+moe_status_t moe_route(const void *x, const void *gate_w, const float *bias,
+                       int64_t N, int32_t H, int32_t E, int32_t K,
+                       moe_dtype_t dtype, int32_t *topk_ids, float *topk_w,
+                       int32_t *counts, void *workspace, size_t workspace_bytes,
+                       void *stream);
+
+/*
+ * Bytes of device workspace moe_dispatch needs for (N, E, K).
+ */
+size_t moe_dispatch_workspace_size(int64_t N, int32_t E, int32_t K);
+
+/*
+ * moe_dispatch -- the counting-sort dispatch of [D]: replaces an argsort of
+ * the T expert ids by a histogram, an exclusive prefix sum and a stable
+ * scatter, then copies token rows into expert-contiguous order.
+ *   counts[e]   = #{i : ids[i] == e}                         (sum = N*K)
+ *   offsets[e]  = sum_{e' < e} counts[e'],  offsets[E] = N*K
+ *   inv[i]      = offsets[ids[i]] + #{j < i : ids[j] == ids[i]}
+ *   perm[inv[i]] = i          (row -> slot; token = slot / K, k = slot % K)
+ *   x_perm[inv[i], :] = x[i / K, :]   (bit copy)
+ * No capacity limit: every slot is dispatched.  Inside an expert's segment
+ * rows are in ascending slot order (stable).
+ *
+ *   topk_ids [N,K]   int32  expert ids; PRECONDITION 0 <= id < E and the K
+ *                           ids of a token distinct (not checked)
+ *   x        [N,H]   dtype  token rows (may be NULL iff x_perm is NULL)
+ *   counts   [E]     int32  out
+ *   offsets  [E+1]   int32  out
+ *   perm     [N*K]   int32  out
+ *   inv      [N*K]   int32  out
+ *   x_perm   [N*K,H] dtype  out, or NULL to produce only the index arrays
+ *   workspace >= moe_dispatch_workspace_size(N, E, K) bytes; scratch
+ * N == 0 is a valid call: counts and offsets are zero-filled.
+ */
+moe_status_t moe_dispatch(const int32_t *topk_ids, const void *x, int64_t N,
+                          int32_t H, int32_t E, int32_t K, moe_dtype_t dtype,
+                          int32_t *counts, int32_t *offsets, int32_t *perm,
+                          int32_t *inv, void *x_perm, void *workspace,
+                          size_t workspace_bytes, void *stream);
+
+/*
+ * moe_combine -- the weighted combine of [A] (forward_aggregate without the
+ * residual): un-permutes the expert outputs and sums them per token
+ *   out[n,:] = sum_{k=0..K-1} topk_w[n,k] * y[inv[n*K+k], :]
+ * accumulated in fp32 with k ascending from 0, rounded once to dtype
+ * (bf16: nearest, ties to even).
+ *
+ *   y      [N*K,H] dtype  expert outputs in dispatched (expert-contiguous) order
+ *   inv    [N*K]   int32  slot -> row, as produced by moe_dispatch;
+ *                         PRECONDITION 0 <= inv[i] < N*K (not checked)
+ *   topk_w [N,K]   fp32   gate weights
+ *   out    [N,H]   dtype  out
+ * N == 0 is a valid no-op.
+ */
+moe_status_t moe_combine(const void *y, const int32_t *inv, const float *topk_w,
+                         int64_t N, int32_t H, int32_t K, moe_dtype_t dtype,
+                         void *out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

@@ -1,0 +1,223 @@
+"""ctypes binding of libmoe.so (include/moe.h).
+
+Argument marshalling only: every step of the path runs in the HIP kernels.
+PyTorch supplies device memory and the stream; each call passes
+``tensor.data_ptr()`` and ``torch.cuda.current_stream().cuda_stream``.  The
+binding checks what the C ABI cannot see -- that every tensor is a
+contiguous device tensor of the dtype and size the call implies -- and
+raises :class:`MoeError` on any non-zero status.  There is no fallback: if
+libmoe.so is missing, importing this module's functions fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+
+MOE_F32 = 0
+MOE_BF16 = 1
+
+STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARGUMENT", 2: "MOE_ERR_UNSUPPORTED",
+          3: "MOE_ERR_MISALIGNED", 4: "MOE_ERR_WORKSPACE_TOO_SMALL", 5: "MOE_ERR_HIP"}
+
+EXPORTS = ("moe_status_string", "moe_route_workspace_size", "moe_route",
+           "moe_dispatch_workspace_size", "moe_dispatch", "moe_combine")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)} "
+                         f"({library().moe_status_string(status).decode()})")
+
+
+_lib = None
+
+
+def library() -> ctypes.CDLL:
+    """Load libmoe.so (built by ``python -m moe_token_routing_router_amd.build``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run "
+                              "`python -m moe_token_routing_router_amd.build` first")
+        lib = ctypes.CDLL(LIB_PATH)
+        P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        lib.moe_status_string.argtypes = [ctypes.c_int]
+        lib.moe_status_string.restype = ctypes.c_char_p
+        lib.moe_route_workspace_size.argtypes = [i32, i32, ctypes.c_int]
+        lib.moe_route_workspace_size.restype = sz
+        lib.moe_route.argtypes = [P, P, P, i64, i32, i32, i32, ctypes.c_int, P, P, P, P, sz, P]
+        lib.moe_route.restype = ctypes.c_int
+        lib.moe_dispatch_workspace_size.argtypes = [i64, i32, i32]
+        lib.moe_dispatch_workspace_size.restype = sz
+        lib.moe_dispatch.argtypes = [P, P, i64, i32, i32, i32, ctypes.c_int, P, P, P, P, P, P,
+                                     sz, P]
+        lib.moe_dispatch.restype = ctypes.c_int
+        lib.moe_combine.argtypes = [P, P, P, i64, i32, i32, ctypes.c_int, P, P]
+        lib.moe_combine.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+# ------------------------------------------------------------------ helpers
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.bfloat16:
+        return MOE_BF16
+    if dt == torch.float32:
+        return MOE_F32
+    raise TypeError(f"unsupported dtype {dt}; expected bfloat16 or float32")
+
+
+def _dev(t: Optional[torch.Tensor], name: str, dtype: torch.dtype, numel: int,
+         device: Optional[torch.device] = None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() != numel:
+        raise ValueError(f"{name} has {t.numel()} elements, expected {numel}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise MoeError(fn, status)
+
+
+# ------------------------------------------------------------------ sizes
+
+def moe_route_workspace_size(H: int, E: int, dtype: torch.dtype) -> int:
+    return int(library().moe_route_workspace_size(H, E, _dtype_code(dtype)))
+
+
+def moe_dispatch_workspace_size(N: int, E: int, K: int) -> int:
+    return int(library().moe_dispatch_workspace_size(N, E, K))
+
+
+# ------------------------------------------------------------------ calls
+
+def moe_route(x: torch.Tensor, gate_w: torch.Tensor, bias: Optional[torch.Tensor], K: int,
+              topk_ids: torch.Tensor, topk_w: torch.Tensor,
+              counts: Optional[torch.Tensor] = None,
+              workspace: Optional[torch.Tensor] = None) -> None:
+    """Router: x [N,H] @ gate_w [H,E] (+ bias [E] fp32) -> topk_ids [N,K]
+    int32, topk_w [N,K] fp32, optional counts [E] int32.  workspace is a
+    uint8 device tensor of at least moe_route_workspace_size(H, E, dtype)
+    bytes (None when that size is 0)."""
+    N, H = x.shape
+    E = gate_w.shape[1]
+    if gate_w.shape[0] != H:
+        raise ValueError("gate_w must be [H, E]")
+    dev = x.device
+    dt = _dtype_code(x.dtype)
+    ws = None
+    ws_bytes = 0
+    if workspace is not None:
+        ws = _dev(workspace, "workspace", torch.uint8, workspace.numel(), dev)
+        ws_bytes = workspace.numel()
+    args = (_dev(x, "x", x.dtype, N * H, dev), _dev(gate_w, "gate_w", x.dtype, H * E, dev),
+            _dev(bias, "bias", torch.float32, E, dev), N, H, E, K, dt,
+            _dev(topk_ids, "topk_ids", torch.int32, N * K, dev),
+            _dev(topk_w, "topk_w", torch.float32, N * K, dev),
+            _dev(counts, "counts", torch.int32, E, dev), ws, ws_bytes, _stream(dev))
+    _check("moe_route", library().moe_route(*args))
+
+
+def moe_dispatch(topk_ids: torch.Tensor, x: Optional[torch.Tensor], E: int,
+                 counts: torch.Tensor, offsets: torch.Tensor, perm: torch.Tensor,
+                 inv: torch.Tensor, x_perm: Optional[torch.Tensor],
+                 workspace: torch.Tensor, H: Optional[int] = None,
+                 dtype: Optional[torch.dtype] = None) -> None:
+    """Counting-sort dispatch of topk_ids [N,K]: counts [E], offsets [E+1],
+    perm/inv [N*K] (int32) and, if x_perm is given, x_perm [N*K,H] rows of x.
+    With x and x_perm both None, pass H and dtype explicitly."""
+    N, K = topk_ids.shape
+    dev = topk_ids.device
+    if x is not None:
+        H = x.shape[1]
+        dtype = x.dtype
+    if H is None or dtype is None:
+        raise ValueError("H and dtype are needed when x is None")
+    _check("moe_dispatch", library().moe_dispatch(
+        _dev(topk_ids, "topk_ids", torch.int32, N * K, dev),
+        _dev(x, "x", dtype, N * H, dev), N, H, E, K, _dtype_code(dtype),
+        _dev(counts, "counts", torch.int32, E, dev),
+        _dev(offsets, "offsets", torch.int32, E + 1, dev),
+        _dev(perm, "perm", torch.int32, N * K, dev), _dev(inv, "inv", torch.int32, N * K, dev),
+        _dev(x_perm, "x_perm", dtype, N * K * H, dev),
+        _dev(workspace, "workspace", torch.uint8, workspace.numel(), dev), workspace.numel(),
+        _stream(dev)))
+
+
+def moe_combine(y: torch.Tensor, inv: torch.Tensor, topk_w: torch.Tensor,
+                out: torch.Tensor) -> None:
+    """Weighted combine: out [N,H] = sum_k topk_w[n,k] * y[inv[n*K+k]], with
+    y [N*K,H] in dispatched order."""
+    N, K = topk_w.shape
+    H = y.shape[1]
+    dev = y.device
+    _check("moe_combine", library().moe_combine(
+        _dev(y, "y", y.dtype, N * K * H, dev), _dev(inv, "inv", torch.int32, N * K, dev),
+        _dev(topk_w, "topk_w", torch.float32, N * K, dev), N, H, K, _dtype_code(y.dtype),
+        _dev(out, "out", y.dtype, N * H, dev), _stream(dev)))
+
+
+# ------------------------------------------------------- allocating forms
+
+def route(x: torch.Tensor, gate_w: torch.Tensor, K: int, bias: Optional[torch.Tensor] = None,
+          with_counts: bool = False):
+    """Allocate outputs and run moe_route; returns (ids, w, counts-or-None)."""
+    N, H = x.shape
+    E = gate_w.shape[1]
+    ids = torch.empty((N, K), dtype=torch.int32, device=x.device)
+    w = torch.empty((N, K), dtype=torch.float32, device=x.device)
+    counts = torch.empty((E,), dtype=torch.int32, device=x.device) if with_counts else None
+    nws = moe_route_workspace_size(H, E, x.dtype)
+    ws = torch.empty((nws,), dtype=torch.uint8, device=x.device) if nws else None
+    moe_route(x, gate_w, bias, K, ids, w, counts, ws)
+    return ids, w, counts
+
+
+def dispatch(topk_ids: torch.Tensor, x: Optional[torch.Tensor], E: int, with_rows: bool = True):
+    """Allocate outputs and run moe_dispatch; returns
+    (counts, offsets, perm, inv, x_perm-or-None)."""
+    N, K = topk_ids.shape
+    dev = topk_ids.device
+    counts = torch.empty((E,), dtype=torch.int32, device=dev)
+    offsets = torch.empty((E + 1,), dtype=torch.int32, device=dev)
+    perm = torch.empty((N * K,), dtype=torch.int32, device=dev)
+    inv = torch.empty((N * K,), dtype=torch.int32, device=dev)
+    x_perm = None
+    if with_rows:
+        x_perm = torch.empty((N * K, x.shape[1]), dtype=x.dtype, device=dev)
+    ws = torch.empty((moe_dispatch_workspace_size(N, E, K),), dtype=torch.uint8, device=dev)
+    moe_dispatch(topk_ids, x, E, counts, offsets, perm, inv, x_perm, ws,
+                 H=None if x is not None else 8, dtype=None if x is not None else torch.bfloat16)
+    return counts, offsets, perm, inv, x_perm
+
+
+def combine(y: torch.Tensor, inv: torch.Tensor, topk_w: torch.Tensor) -> torch.Tensor:
+    """Allocate the output and run moe_combine."""
+    N = topk_w.shape[0]
+    out = torch.empty((N, y.shape[1]), dtype=y.dtype, device=y.device)
+    moe_combine(y, inv, topk_w, out)
+    return out

@@ -1,0 +1,126 @@
+// extern "C" entry points of libmoe.so (declared in include/moe.h).
+// Every argument is checked on the host before anything is enqueued; the
+// launchers in route.hip / dispatch.hip / combine.hip assume valid input.
+#include "../../include/moe.h"
+#include "moe_internal.h"
+
+namespace {
+
+constexpr int64_t kMaxSlots = (int64_t)1 << 31;
+
+inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+inline int elem_bytes(moe_dtype_t dt) { return dt == MOE_BF16 ? 2 : 4; }
+
+inline bool valid_dtype(moe_dtype_t dt) { return dt == MOE_F32 || dt == MOE_BF16; }
+
+// H elements of dtype form a whole number of 16-byte vectors
+inline bool row_ok(int32_t H, moe_dtype_t dt) {
+  return ((int64_t)H * elem_bytes(dt)) % 16 == 0;
+}
+
+inline moe_status_t from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status_t status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported size or shape";
+    case MOE_ERR_MISALIGNED: return "misaligned pointer";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP launch error";
+  }
+  return "unknown status";
+}
+
+size_t moe_route_workspace_size(int32_t H, int32_t E, moe_dtype_t dtype) {
+  if (dtype != MOE_BF16 || H <= 0 || E <= 0 || E > moe::kMaxExperts) return 0;
+  return round_up((size_t)moe::route_padded_experts(E) * (size_t)H * 2, 256);
+}
+
+moe_status_t moe_route(const void* x, const void* gate_w, const float* bias, int64_t N, int32_t H,
+                       int32_t E, int32_t K, moe_dtype_t dtype, int32_t* topk_ids, float* topk_w,
+                       int32_t* counts, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!valid_dtype(dtype) || N < 0 || H <= 0 || E <= 0 || K < 1 || K > E)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (N > 0 && (!x || !gate_w || !topk_ids || !topk_w)) return MOE_ERR_INVALID_ARGUMENT;
+  if (E > moe::kMaxExperts || K > moe::kMaxRouteK || N * (int64_t)K >= kMaxSlots ||
+      !row_ok(H, dtype))
+    return MOE_ERR_UNSUPPORTED;
+  if (!aligned(x, 16) || !aligned(gate_w, 16) || !aligned(bias, 4) || !aligned(topk_ids, 4) ||
+      !aligned(topk_w, 4) || !aligned(counts, 4) || !aligned(workspace, 16))
+    return MOE_ERR_MISALIGNED;
+  const size_t need = moe_route_workspace_size(H, E, dtype);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (N == 0) return counts ? from_hip(moe::launch_fill_i32(counts, E, 0, s)) : MOE_OK;
+
+  if (dtype == MOE_BF16) {
+    uint16_t* wgt = reinterpret_cast<uint16_t*>(workspace);
+    hipError_t e = moe::launch_gate_transpose(reinterpret_cast<const uint16_t*>(gate_w), H, E, wgt,
+                                              counts, s);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    return from_hip(moe::launch_route_bf16(reinterpret_cast<const uint16_t*>(x), wgt, bias, N, H,
+                                           E, K, topk_ids, topk_w, counts, s));
+  }
+  if (counts) {
+    hipError_t e = moe::launch_fill_i32(counts, E, 0, s);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  }
+  return from_hip(moe::launch_route_f32(reinterpret_cast<const float*>(x),
+                                        reinterpret_cast<const float*>(gate_w), bias, N, H, E, K,
+                                        topk_ids, topk_w, counts, s));
+}
+
+size_t moe_dispatch_workspace_size(int64_t N, int32_t E, int32_t K) {
+  if (N < 0 || E <= 0 || E > moe::kMaxExperts || K < 1) return 0;
+  const int64_t num_sub = moe::dispatch_num_sub(N);
+  return round_up((size_t)num_sub * (size_t)E * sizeof(int32_t), 256) + 256;
+}
+
+moe_status_t moe_dispatch(const int32_t* topk_ids, const void* x, int64_t N, int32_t H, int32_t E,
+                          int32_t K, moe_dtype_t dtype, int32_t* counts, int32_t* offsets,
+                          int32_t* perm, int32_t* inv, void* x_perm, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  if (!valid_dtype(dtype) || N < 0 || H <= 0 || E <= 0 || K < 1 || K > E)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (!counts || !offsets) return MOE_ERR_INVALID_ARGUMENT;
+  if (N > 0 && (!topk_ids || !perm || !inv || !workspace)) return MOE_ERR_INVALID_ARGUMENT;
+  if (N > 0 && x_perm && !x) return MOE_ERR_INVALID_ARGUMENT;
+  if (E > moe::kMaxExperts || N * (int64_t)K >= kMaxSlots || !row_ok(H, dtype))
+    return MOE_ERR_UNSUPPORTED;
+  if (!aligned(topk_ids, 4) || !aligned(counts, 4) || !aligned(offsets, 4) || !aligned(perm, 4) ||
+      !aligned(inv, 4) || !aligned(x, 16) || !aligned(x_perm, 16) || !aligned(workspace, 16))
+    return MOE_ERR_MISALIGNED;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (N == 0) {
+    hipError_t e = moe::launch_fill_i32(counts, E, 0, s);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    return from_hip(moe::launch_fill_i32(offsets, (int64_t)E + 1, 0, s));
+  }
+  if (workspace_bytes < moe_dispatch_workspace_size(N, E, K)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  return from_hip(moe::launch_dispatch(topk_ids, x, N, (int64_t)H * elem_bytes(dtype), E, K,
+                                       counts, offsets, perm, inv, x_perm,
+                                       reinterpret_cast<int32_t*>(workspace), s));
+}
+
+moe_status_t moe_combine(const void* y, const int32_t* inv, const float* topk_w, int64_t N,
+                         int32_t H, int32_t K, moe_dtype_t dtype, void* out, void* stream) {
+  if (!valid_dtype(dtype) || N < 0 || H <= 0 || K < 1) return MOE_ERR_INVALID_ARGUMENT;
+  if (N > 0 && (!y || !inv || !topk_w || !out)) return MOE_ERR_INVALID_ARGUMENT;
+  if (K > moe::kMaxExperts || N * (int64_t)K >= kMaxSlots || !row_ok(H, dtype))
+    return MOE_ERR_UNSUPPORTED;
+  if (!aligned(y, 16) || !aligned(out, 16) || !aligned(inv, 4) || !aligned(topk_w, 4))
+    return MOE_ERR_MISALIGNED;
+  if (N == 0) return MOE_OK;
+  return from_hip(moe::launch_combine(y, inv, topk_w, N, H, K, dtype == MOE_BF16, out,
+                                      reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

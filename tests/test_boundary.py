@@ -1,0 +1,136 @@
+"""The C-ABI boundary on the CPU: libmoe.so loads, exports every function
+include/moe.h declares, and rejects bad arguments with the documented status
+before enqueuing anything (no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from moe_token_routing_router_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+OK, INVALID, UNSUPPORTED, MISALIGNED, WS_SMALL, HIPERR = range(6)
+F32, BF16 = 0, 1
+
+# Fake, never-dereferenced device addresses: every call below fails host-side
+# validation before any launch.
+A = ctypes.c_void_p(0x7f0000000000)       # 256-aligned
+A2 = ctypes.c_void_p(0x7f0000100000)
+MIS = ctypes.c_void_p(0x7f0000000002)     # not 4- or 16-aligned
+MIS8 = ctypes.c_void_p(0x7f0000000008)    # 4-aligned, not 16-aligned
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from moe_token_routing_router_amd import build
+        build.build()
+    return _lib.library()
+
+
+def test_header_declares_the_three_calls():
+    fns = declared_functions()
+    for f in ("moe_route", "moe_dispatch", "moe_combine"):
+        assert f in fns
+    assert set(_lib.EXPORTS) == set(fns)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for f in declared_functions():
+        assert hasattr(lib, f), f"libmoe.so does not export {f}"
+
+
+def test_status_strings(lib):
+    for s in range(6):
+        assert lib.moe_status_string(s)
+    assert lib.moe_status_string(99) == b"unknown status"
+
+
+def test_workspace_sizes(lib):
+    # bf16 router: expert-major gate padded to a power-of-two multiple of 16
+    assert lib.moe_route_workspace_size(4096, 64, BF16) == 64 * 4096 * 2
+    assert lib.moe_route_workspace_size(2048, 128, BF16) == 128 * 2048 * 2
+    assert lib.moe_route_workspace_size(256, 20, BF16) == 32 * 256 * 2
+    assert lib.moe_route_workspace_size(256, 16, F32) == 0
+    assert lib.moe_route_workspace_size(256, 300, BF16) == 0
+    # dispatch: one int per (expert, sub-chunk of 16 tokens), rounded, + 256
+    assert lib.moe_dispatch_workspace_size(16384, 64, 2) == 1024 * 64 * 4 + 256
+    assert lib.moe_dispatch_workspace_size(17, 3, 2) >= 2 * 3 * 4
+    assert lib.moe_dispatch_workspace_size(-1, 3, 2) == 0
+
+
+def route(lib, x=A, gw=A, bias=None, N=4, H=16, E=8, K=2, dt=BF16, ids=A2, w=A2, counts=None,
+          ws=A, wsb=1 << 20):
+    return lib.moe_route(x, gw, bias, N, H, E, K, dt, ids, w, counts, ws, wsb, None)
+
+
+def test_route_validation(lib):
+    assert route(lib, K=9) == INVALID          # K > E
+    assert route(lib, K=0) == INVALID
+    assert route(lib, N=-1) == INVALID
+    assert route(lib, H=0) == INVALID
+    assert route(lib, dt=7) == INVALID
+    assert route(lib, x=None) == INVALID
+    assert route(lib, ids=None) == INVALID
+    assert route(lib, E=300, K=2) == UNSUPPORTED
+    assert route(lib, E=64, K=17) == UNSUPPORTED  # K > 16 in the router
+    assert route(lib, H=12) == UNSUPPORTED     # 24-byte bf16 rows
+    assert route(lib, H=6, dt=F32) == UNSUPPORTED
+    assert route(lib, N=1 << 30, K=2) == UNSUPPORTED  # N*K >= 2^31
+    assert route(lib, x=MIS8) == MISALIGNED
+    assert route(lib, gw=MIS8) == MISALIGNED
+    assert route(lib, ids=MIS) == MISALIGNED
+    assert route(lib, bias=MIS) == MISALIGNED
+    assert route(lib, ws=None) == WS_SMALL
+    assert route(lib, wsb=16 * 16 * 2 - 1, H=16, E=8) == WS_SMALL
+
+
+def dispatch(lib, ids=A, x=A, N=4, H=16, E=8, K=2, dt=BF16, counts=A2, offsets=A2, perm=A2,
+             inv=A2, xp=A, ws=A, wsb=1 << 20):
+    return lib.moe_dispatch(ids, x, N, H, E, K, dt, counts, offsets, perm, inv, xp, ws, wsb, None)
+
+
+def test_dispatch_validation(lib):
+    assert dispatch(lib, K=9) == INVALID
+    assert dispatch(lib, counts=None) == INVALID
+    assert dispatch(lib, offsets=None) == INVALID
+    assert dispatch(lib, perm=None) == INVALID
+    assert dispatch(lib, x=None) == INVALID    # rows asked for without x
+    assert dispatch(lib, ws=None) == INVALID
+    assert dispatch(lib, E=257, K=2) == UNSUPPORTED
+    assert dispatch(lib, H=4) == UNSUPPORTED
+    assert dispatch(lib, x=MIS8) == MISALIGNED
+    assert dispatch(lib, xp=MIS8) == MISALIGNED
+    assert dispatch(lib, inv=MIS) == MISALIGNED
+    assert dispatch(lib, wsb=8) == WS_SMALL
+
+
+def combine(lib, y=A, inv=A2, w=A2, N=4, H=16, K=2, dt=BF16, out=A):
+    return lib.moe_combine(y, inv, w, N, H, K, dt, out, None)
+
+
+def test_combine_validation(lib):
+    assert combine(lib, K=0) == INVALID
+    assert combine(lib, N=-3) == INVALID
+    assert combine(lib, out=None) == INVALID
+    assert combine(lib, H=4) == UNSUPPORTED
+    assert combine(lib, K=257) == UNSUPPORTED
+    assert combine(lib, y=MIS8) == MISALIGNED
+    assert combine(lib, w=MIS) == MISALIGNED
+    assert combine(lib, N=0) == OK             # empty: nothing to do, nothing enqueued
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    x = torch.zeros((4, 16), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        _lib.route(x, torch.zeros((16, 8), dtype=torch.bfloat16), 2)

@@ -1,0 +1,230 @@
+"""HIP path vs the CPU oracle, through the C ABI, on the GPU.
+
+Every workload runs at its full size (the oracle computes every output of
+every workload in seconds), in the same launch configuration the benchmark
+times, and every output element is compared.  Edge cases cover empty and
+ragged inputs, the size limits and the degenerate cases of the method.
+"""
+import numpy as np
+import pytest
+import torch
+
+from moe_token_routing_router_amd import _lib as L
+from moe_token_routing_router_amd import inputs as I
+from oracle import oracle as O
+from tests.parity import check_combine, check_route, from_dev, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    L.library()  # fails loudly if libmoe.so is missing
+
+
+_cache = {}
+
+
+def workload(name):
+    """Inputs and oracle results of a workload, computed once per session."""
+    if name not in _cache:
+        _cache.clear()  # keep one workload resident at a time (host memory)
+        d = I.make_inputs(name)
+        ids, w, logits, margin = O.route(d["x"], d["gate_w"], d["bias"], d["K"], d["dtype"])
+        counts, offsets, perm, inv = O.dispatch(ids, d["E"])
+        d["o"] = dict(ids=ids, w=w, logits=logits, margin=margin, counts=counts,
+                      offsets=offsets, perm=perm, inv=inv,
+                      x_perm=O.permute_rows(d["x"], perm, d["K"]),
+                      out=O.combine(d["y"], inv, w, d["dtype"]))
+        _cache[name] = d
+    return _cache[name]
+
+
+def gpu_route(d):
+    x, gw = to_dev(d["x"], d["dtype"]), to_dev(d["gate_w"], d["dtype"])
+    b = None if d["bias"] is None else torch.from_numpy(d["bias"]).cuda()
+    ids, w, counts = L.route(x, gw, d["K"], bias=b, with_counts=True)
+    torch.cuda.synchronize()
+    return from_dev(ids), from_dev(w), from_dev(counts)
+
+
+def gpu_dispatch(ids, x, E, dtype):
+    res = L.dispatch(torch.from_numpy(np.ascontiguousarray(ids)).cuda(), to_dev(x, dtype), E)
+    torch.cuda.synchronize()
+    return [from_dev(t) for t in res]
+
+
+WORKLOADS = list(I.WORKLOADS)
+
+
+@pytest.mark.parametrize("name", WORKLOADS)
+def test_route_full_size(name):
+    d = workload(name)
+    o = d["o"]
+    print(f"[route] {name} N={d['N']} H={d['H']} E={d['E']} K={d['K']}", flush=True)
+    ids, w, counts = gpu_route(d)
+    exempt = check_route(ids, w, o["ids"], o["w"], o["logits"], d["K"], d["dtype"])
+    assert exempt <= 0.02 * d["N"]
+    # the router's own dispatch counts: bincount of its ids, summing to N*K
+    np.testing.assert_array_equal(counts, np.bincount(ids.ravel(), minlength=d["E"]))
+    assert counts.sum() == d["N"] * d["K"]
+
+
+@pytest.mark.parametrize("name", WORKLOADS)
+def test_dispatch_full_size_bit_exact(name):
+    d = workload(name)
+    o = d["o"]
+    print(f"[dispatch] {name}", flush=True)
+    counts, offsets, perm, inv, x_perm = gpu_dispatch(o["ids"], d["x"], d["E"], d["dtype"])
+    np.testing.assert_array_equal(counts, o["counts"])
+    np.testing.assert_array_equal(offsets, o["offsets"])
+    np.testing.assert_array_equal(perm, o["perm"])
+    np.testing.assert_array_equal(inv, o["inv"])
+    assert counts.sum() == d["N"] * d["K"]
+    np.testing.assert_array_equal(x_perm.view(np.uint8), o["x_perm"].view(np.uint8))
+
+
+@pytest.mark.parametrize("name", WORKLOADS)
+def test_combine_full_size(name):
+    d = workload(name)
+    o = d["o"]
+    print(f"[combine] {name}", flush=True)
+    out = L.combine(to_dev(d["y"], d["dtype"]), torch.from_numpy(o["inv"]).cuda(),
+                    torch.from_numpy(o["w"]).cuda())
+    torch.cuda.synchronize()
+    check_combine(from_dev(out), o["out"], d["dtype"])
+
+
+@pytest.mark.parametrize("name", WORKLOADS)
+def test_end_to_end_identity_experts(name):
+    # GPU route -> GPU dispatch -> identity experts (y = x_perm) -> GPU combine
+    # gives back x (weights sum to 1; bf16 rounds back exactly).
+    d = workload(name)
+    print(f"[e2e] {name}", flush=True)
+    x = to_dev(d["x"], d["dtype"])
+    gw = to_dev(d["gate_w"], d["dtype"])
+    b = None if d["bias"] is None else torch.from_numpy(d["bias"]).cuda()
+    ids, w, _ = L.route(x, gw, d["K"], bias=b)
+    counts, offsets, perm, inv, x_perm = L.dispatch(ids, x, d["E"])
+    out = L.combine(x_perm, inv, w)
+    torch.cuda.synchronize()
+    # the GPU dispatch of the GPU's own ids equals the oracle's dispatch of them
+    oc, oo, op, oi = O.dispatch(from_dev(ids), d["E"])
+    np.testing.assert_array_equal(from_dev(perm), op)
+    np.testing.assert_array_equal(from_dev(inv), oi)
+    if d["dtype"] == "bf16":
+        np.testing.assert_array_equal(from_dev(out), d["x"])
+    else:
+        np.testing.assert_allclose(from_dev(out), d["x"], rtol=d["K"] * 2.4e-7, atol=0)
+
+
+# ------------------------------------------------------------ edge cases
+
+EDGE = [
+    # (N, H, E, K, dtype, bias)
+    (1, 256, 16, 2, "bf16", False),
+    (17, 128, 16, 2, "bf16", True),       # ragged tail of a 64-token tile
+    (65, 72, 20, 3, "bf16", True),        # H not a multiple of 64, E not a power of 2
+    (100, 8, 4, 4, "bf16", False),        # minimum bf16 row, K == E
+    (37, 4, 5, 1, "f32", True),           # minimum fp32 row, K = 1
+    (129, 520, 256, 16, "bf16", True),    # E and router K at their limits
+    (300, 1024, 256, 8, "bf16", False),
+    (203, 96, 128, 8, "bf16", True),
+    (250, 64, 64, 1, "bf16", False),
+    (1000, 264, 32, 2, "f32", False),
+    (5000, 128, 64, 6, "bf16", True),     # many dispatch sub-chunks
+]
+
+
+@pytest.mark.parametrize("N,H,E,K,dtype,bias", EDGE)
+def test_edge_case_full_chain(N, H, E, K, dtype, bias):
+    print(f"[edge] N={N} H={H} E={E} K={K} {dtype} bias={bias}", flush=True)
+    d = I.random_case(N * 7 + H, N, H, E, K, dtype, bias=bias)
+    ids_o, w_o, logits_o, _ = O.route(d["x"], d["gate_w"], d["bias"], K, dtype)
+    ids, w, counts = gpu_route(d)
+    check_route(ids, w, ids_o, w_o, logits_o, K, dtype)
+    np.testing.assert_array_equal(counts, np.bincount(ids.ravel(), minlength=E))
+    oc, oo, op, oi = O.dispatch(ids_o, E)
+    gc, go, gp, gi, gx = gpu_dispatch(ids_o, d["x"], E, dtype)
+    for a, b in ((gc, oc), (go, oo), (gp, op), (gi, oi)):
+        np.testing.assert_array_equal(a, b)
+    np.testing.assert_array_equal(gx.view(np.uint8), O.permute_rows(d["x"], op, K).view(np.uint8))
+    out = L.combine(to_dev(d["y"], dtype), torch.from_numpy(oi).cuda(),
+                    torch.from_numpy(w_o).cuda())
+    check_combine(from_dev(out), O.combine(d["y"], oi, w_o, dtype), dtype)
+
+
+@pytest.mark.parametrize("skew", [0.0, 1.5, 4.0])
+def test_dispatch_skewed_and_empty_experts(skew):
+    N, H, E, K = 3001, 64, 48, 4
+    print(f"[dispatch-skew] skew={skew}", flush=True)
+    ids = I.random_ids(77, N, E, K, skew=skew)
+    x = I.random_case(77, N, H, 4, 1, "bf16", with_y=False)["x"]
+    oc, oo, op, oi = O.dispatch(ids, E)
+    if skew >= 4.0:
+        assert (oc == 0).any()
+    gc, go, gp, gi, gx = gpu_dispatch(ids, x, E, "bf16")
+    for a, b in ((gc, oc), (go, oo), (gp, op), (gi, oi)):
+        np.testing.assert_array_equal(a, b)
+    np.testing.assert_array_equal(gx, O.permute_rows(x, op, K))
+
+
+def test_dispatch_metadata_only():
+    N, E, K = 999, 40, 3
+    ids = I.random_ids(5, N, E, K)
+    oc, oo, op, oi = O.dispatch(ids, E)
+    res = L.dispatch(torch.from_numpy(ids).cuda(), None, E, with_rows=False)
+    torch.cuda.synchronize()
+    for a, b in zip(res[:4], (oc, oo, op, oi)):
+        np.testing.assert_array_equal(from_dev(a), b)
+    assert res[4] is None
+
+
+def test_empty_inputs():
+    dev = torch.device("cuda")
+    E, K, H = 16, 2, 64
+    x = torch.empty((0, H), dtype=torch.bfloat16, device=dev)
+    gw = torch.zeros((H, E), dtype=torch.bfloat16, device=dev)
+    ids, w, counts = L.route(x, gw, K, with_counts=True)
+    c, o, p, i, xp = L.dispatch(ids, x, E)
+    out = L.combine(xp, i, w)
+    torch.cuda.synchronize()
+    assert ids.shape == (0, K) and out.shape == (0, H)
+    assert (counts == 0).all() and (c == 0).all() and (o == 0).all()
+
+
+def test_out_of_range_indices_are_not_dispatched():
+    # the kernels' own bounds checks: an id outside [0, E) is left out of the
+    # counts, gets inv = -1 and writes no row; combine skips inv = -1
+    N, H, E, K = 40, 64, 8, 2
+    ids = I.random_ids(3, N, E, K)
+    ids[5, 1] = -1
+    ids[9, 0] = E
+    x = I.random_case(3, N, H, 4, 1, "bf16", with_y=False)["x"]
+    gc, go, gp, gi, gx = gpu_dispatch(ids, x, E, "bf16")
+    valid = (ids >= 0) & (ids < E)
+    np.testing.assert_array_equal(gc, np.bincount(ids[valid], minlength=E))
+    assert gi[5 * K + 1] == -1 and gi[9 * K + 0] == -1
+    assert go[E] == N * K - 2
+    w = np.full((N, K), 0.5, np.float32)
+    y = np.concatenate([gx[:go[E]], np.zeros((2, H), np.uint16)])  # 2 rows never written
+    out = L.combine(to_dev(y, "bf16"), torch.from_numpy(gi).cuda(), torch.from_numpy(w).cuda())
+    torch.cuda.synchronize()
+    outn = from_dev(out)
+    xf = I.bf16_bits_to_f32(x)
+    # token 5 keeps only its k=0 row at weight 0.5
+    np.testing.assert_array_equal(outn[5], I.f32_to_bf16_bits(0.5 * xf[5]))
+
+
+def test_bitwise_deterministic():
+    d = workload("small-bf16")
+    a = gpu_route(d)
+    b = gpu_route(d)
+    for u, v in zip(a, b):
+        np.testing.assert_array_equal(u, v)
+    r1 = gpu_dispatch(a[0], d["x"], d["E"], d["dtype"])
+    r2 = gpu_dispatch(a[0], d["x"], d["E"], d["dtype"])
+    for u, v in zip(r1, r2):
+        np.testing.assert_array_equal(u, v)
