@@ -1,0 +1,294 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE routing path on one MI355X: route -> dispatch -> combine.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step is one pass of the whole path over one batch of synthetic input:
+moe_route (x @ gate_w -> top-K -> renormalised weights), moe_dispatch
+(counting sort + row scatter into expert-contiguous order) and moe_combine
+(weighted un-permute of the expert outputs y).  The default workload is
+N=16384 tokens (8 sequences x 2048), H=4096, E=64, K=2, bf16.  Inputs are
+resident in HBM before the timed region; three input sets are rotated so the
+256 MiB Infinity Cache never serves a step the data of the previous step.
+
+Prints ONE JSON line: routed tokens/s (value), per-stage times and
+algorithmic bandwidth, a roofline object for the dominant kernel (timed with
+HIP events on the stream it runs on) and the CPU oracle's throughput on a
+bounded sample of the same workload, timed on this host (cpu_baseline).
+"""
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import platform
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA, TFLOP/s
+N_SETS = 3
+
+
+def algorithmic_bytes(N, H, E, K, b):
+    """Bytes each stage must move (logits never leave the chip; each token
+    row is read once by dispatch)."""
+    T = N * K
+    route = N * H * b + H * E * b + T * 8 + E * 4 + E * 4
+    dispatch = N * H * b + T * H * b + 3 * T * 4 + (2 * E + 1) * 4
+    combine = T * H * b + T * 8 + N * H * b
+    return {"route": route, "dispatch": dispatch, "combine": combine}
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def traffic_record(kernel, workload):
+    """HBM bytes per launch measured with rocprofv3 counters, from the
+    committed summary under profiles/, or None if the kernel source changed
+    since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.md")
+    if not os.path.exists(path):
+        return None
+    src = os.path.join(ROOT, "moe_token_routing_router_amd", "csrc", f"{kernel}.hip")
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16] if os.path.exists(src) else ""
+    for line in open(path):
+        m = re.match(r"\|\s*(\w+)\s*\|\s*([\w\-]+)\s*\|\s*([0-9a-f]+)\s*\|\s*([0-9.]+)\s*\|", line)
+        if m and m.group(1) == kernel and m.group(2) == workload and m.group(3) == sha:
+            return float(m.group(4))
+    return None
+
+
+def cpu_baseline(d, min_seconds):
+    """The oracle as it stands (single-threaded C, fp64), on the whole
+    workload, repeated until at least `min_seconds` have passed."""
+    from oracle import oracle as O
+    t0 = time.perf_counter()
+    passes = 0
+    while True:
+        ids, w, _, _ = O.route(d["x"], d["gate_w"], d["bias"], d["K"], d["dtype"])
+        _, _, perm, inv = O.dispatch(ids, d["E"])
+        O.permute_rows(d["x"], perm, d["K"])
+        O.combine(d["y"], inv, w, d["dtype"])
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            break
+    return {"value": passes * d["N"] / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"full workload (N={d['N']}) route+dispatch+combine x {passes} passes, "
+                      f"{el:.1f} s on 1 thread of {cpu_model()}"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 256 MiB device copy (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from moe_token_routing_router_amd import _lib as L
+    from moe_token_routing_router_amd import inputs as I
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    lib = L.library()
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    wl = I.WORKLOADS[args.workload or I.HEADLINE]
+    N, H, E, K = wl.N, wl.H, wl.E, wl.K
+    T = N * K
+    b = wl.elem_bytes
+    tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    d = I.make_inputs(wl)
+
+    def to_dev(a):
+        if wl.dtype == "bf16":
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    x0 = to_dev(d["x"])
+    y0 = to_dev(d["y"])
+    gw = to_dev(d["gate_w"])
+    bias = None if d["bias"] is None else torch.from_numpy(d["bias"]).to(dev)
+
+    # N_SETS resident input sets (x, y differ; set 0 is the generated data,
+    # the others are row-rotations of it so every set has the same statistics)
+    sets = []
+    for s in range(N_SETS):
+        x = x0 if s == 0 else torch.roll(x0, shifts=997 * s, dims=0).contiguous()
+        y = y0 if s == 0 else torch.roll(y0, shifts=991 * s, dims=0).contiguous()
+        st = dict(x=x, y=y,
+                  ids=torch.empty((N, K), dtype=torch.int32, device=dev),
+                  w=torch.empty((N, K), dtype=torch.float32, device=dev),
+                  counts_r=torch.empty((E,), dtype=torch.int32, device=dev),
+                  counts=torch.empty((E,), dtype=torch.int32, device=dev),
+                  offsets=torch.empty((E + 1,), dtype=torch.int32, device=dev),
+                  perm=torch.empty((T,), dtype=torch.int32, device=dev),
+                  inv=torch.empty((T,), dtype=torch.int32, device=dev),
+                  x_perm=torch.empty((T, H), dtype=tdt, device=dev),
+                  out=torch.empty((N, H), dtype=tdt, device=dev))
+        sets.append(st)
+    rws = torch.empty((max(1, L.moe_route_workspace_size(H, E, tdt)),), dtype=torch.uint8,
+                      device=dev)
+    dws = torch.empty((L.moe_dispatch_workspace_size(N, E, K),), dtype=torch.uint8, device=dev)
+
+    # validate every buffer once through the checked binding
+    for st in sets:
+        L.moe_route(st["x"], gw, bias, K, st["ids"], st["w"], st["counts_r"], rws)
+        L.moe_dispatch(st["ids"], st["x"], E, st["counts"], st["offsets"], st["perm"],
+                       st["inv"], st["x_perm"], dws)
+        L.moe_combine(st["y"], st["inv"], st["w"], st["out"])
+    torch.cuda.synchronize()
+
+    # then call the C ABI directly with the pointers (no per-call Python checks)
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None
+    dt = L.MOE_BF16 if wl.dtype == "bf16" else L.MOE_F32
+    calls = []
+    for st in sets:
+        calls.append((
+            (P(st["x"]), P(gw), P(bias), N, H, E, K, dt, P(st["ids"]), P(st["w"]),
+             P(st["counts_r"]), P(rws), rws.numel(), sp),
+            (P(st["ids"]), P(st["x"]), N, H, E, K, dt, P(st["counts"]), P(st["offsets"]),
+             P(st["perm"]), P(st["inv"]), P(st["x_perm"]), P(dws), dws.numel(), sp),
+            (P(st["y"]), P(st["inv"]), P(st["w"]), N, H, K, dt, P(st["out"]), sp)))
+
+    def step(i):
+        r, dsp, c = calls[i % N_SETS]
+        s1 = lib.moe_route(*r)
+        s2 = lib.moe_dispatch(*dsp)
+        s3 = lib.moe_combine(*c)
+        if s1 or s2 or s3:
+            raise RuntimeError(f"status route={s1} dispatch={s2} combine={s3}")
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region 1: the whole path, K steps, nothing between the launches
+    e_start = torch.cuda.Event(enable_timing=True)
+    e_stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e_start.record(stream)
+    for i in range(args.steps):
+        step(i)
+    e_stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = e_start.elapsed_time(e_stop)
+
+    # timed region 2: each stage on its own, K back-to-back calls (rotating
+    # the input sets) between one pair of HIP events on the launch stream:
+    # the average duration of one call of that stage
+    stage_fn = {"route": lambda i: lib.moe_route(*calls[i % N_SETS][0]),
+                "dispatch": lambda i: lib.moe_dispatch(*calls[i % N_SETS][1]),
+                "combine": lambda i: lib.moe_combine(*calls[i % N_SETS][2])}
+    stage_ms = {}
+    for name, fn in stage_fn.items():
+        for i in range(3):
+            fn(i)
+        a = torch.cuda.Event(enable_timing=True)
+        z = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for i in range(args.steps):
+            fn(i)
+        z.record(stream)
+        torch.cuda.synchronize()
+        stage_ms[name] = a.elapsed_time(z) / args.steps
+    # leave every set's outputs consistent for the check below
+    for i in range(N_SETS):
+        step(i)
+    torch.cuda.synchronize()
+
+    # correctness guard on the last step's outputs (cheap invariants only)
+    last = sets[(args.steps - 1) % N_SETS]
+    cnt = last["counts"].cpu().numpy()
+    assert cnt.sum() == T, "token conservation violated"
+    load = cnt.astype(np.float64)
+
+    alg = algorithmic_bytes(N, H, E, K, b)
+    stages = {}
+    for k, ms in stage_ms.items():
+        stages[k] = {"ms_per_call": round(ms, 5), "alg_MB": round(alg[k] / 1e6, 3),
+                     "alg_GBs": round(alg[k] / ms / 1e6, 1),
+                     "hbm_frac": round(alg[k] / ms / 1e6 / HBM_PEAK_GBS, 4)}
+    r_flops = 2.0 * N * H * E
+    stages["route"]["mfma_util"] = round(
+        r_flops / (stage_ms["route"] * 1e-3) / (BF16_MFMA_PEAK_TFLOPS * 1e12), 4)
+
+    # dominant kernel: combine (one launch per call, the largest per-kernel
+    # time of the path)
+    kern = "combine"
+    avg_ms = stage_ms[kern]
+    achieved = alg[kern] / (avg_ms * 1e-3) / 1e9
+    traffic = traffic_record(kern, wl.name)
+    roofline = {"kernel": "combine_kernel<bf16>" if wl.dtype == "bf16" else "combine_kernel<f32>",
+                "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic, "alg_bytes_per_launch": alg[kern],
+                "avg_launch_ms": round(avg_ms, 5)}
+
+    if args.copy_calibration:
+        a = torch.empty((256 << 20,), dtype=torch.uint8, device=dev)
+        bb = torch.empty_like(a)
+        for _ in range(3):
+            bb.copy_(a)
+        torch.cuda.synchronize()
+
+    ms_per_step = wall * 1e3 / args.steps
+    res = {
+        "metric": "routed tokens/s (route+dispatch+combine)",
+        "value": round(N * args.steps / wall, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": wl.dtype, "data": "synthetic (seeded, resident in HBM, 3 rotating sets)",
+        "config": {"workload": wl.describe(), "N": N, "H": H, "E": E, "K": K,
+                   "bias": wl.bias, "name": wl.name},
+        "pipeline": {"gpu_ms_per_step": round(gpu_ms / args.steps, 5),
+                     "stage_sum_ms": round(sum(stage_ms.values()), 5),
+                     "alg_MB_per_step": round(sum(alg.values()) / 1e6, 3),
+                     "hbm_frac": round(sum(alg.values()) / (gpu_ms / args.steps * 1e-3) / 1e9
+                                       / HBM_PEAK_GBS, 4)},
+        "stages": stages,
+        "load_max_over_mean": round(float(load.max() / load.mean()), 3),
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(d, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -9,56 +9,81 @@
 // owned by one lane, which loads its K source vectors (independent 16-byte
 // loads, all in flight together), accumulates in fp32 with k ascending from
 // 0, rounds once and stores.  No float atomics, so the result is
-// deterministic.  A row index outside [0, N*K) contributes nothing.
+// deterministic.  A row index outside [0, N*K) contributes nothing.  For the
+// common K (1, 2, 4, 8) each lane works on U output vectors at once, so
+// U*K independent row gathers are in flight per lane.
 #include "moe_internal.h"
+
+// Tuning knobs (compile-time; the defaults are the measured best on MI355X).
+#ifndef MOE_COMBINE_TOKENS
+#define MOE_COMBINE_TOKENS 8   // tokens per workgroup
+#endif
+#ifndef MOE_COMBINE_NT
+#define MOE_COMBINE_NT 1       // non-temporal loads of y / stores of out
+#endif
 
 namespace moe {
 
 namespace {
 
-constexpr int kCombineTokens = 8;  // tokens per workgroup
+constexpr int kCombineTokens = MOE_COMBINE_TOKENS;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ u32x4 ld_vec(const u32x4* p) {
+#if MOE_COMBINE_NT
+  return __builtin_nontemporal_load(p);
+#else
+  return *p;
+#endif
+}
+
+__device__ __forceinline__ void st_vec(u32x4* p, u32x4 v) {
+#if MOE_COMBINE_NT
+  __builtin_nontemporal_store(v, p);
+#else
+  *p = v;
+#endif
+}
 
 template <bool BF16>
-__device__ __forceinline__ void fma_vec(float (&acc)[BF16 ? 8 : 4], float w, uint4 v) {
+__device__ __forceinline__ void fma_vec(float (&acc)[BF16 ? 8 : 4], float w, u32x4 v) {
   if constexpr (BF16) {
-    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      acc[2 * j] = fmaf(w, bf16_lo(u[j]), acc[2 * j]);
-      acc[2 * j + 1] = fmaf(w, bf16_hi(u[j]), acc[2 * j + 1]);
+      acc[2 * j] = fmaf(w, bf16_lo(v[j]), acc[2 * j]);
+      acc[2 * j + 1] = fmaf(w, bf16_hi(v[j]), acc[2 * j + 1]);
     }
   } else {
-    acc[0] = fmaf(w, __uint_as_float(v.x), acc[0]);
-    acc[1] = fmaf(w, __uint_as_float(v.y), acc[1]);
-    acc[2] = fmaf(w, __uint_as_float(v.z), acc[2]);
-    acc[3] = fmaf(w, __uint_as_float(v.w), acc[3]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j] = fmaf(w, __uint_as_float(v[j]), acc[j]);
   }
 }
 
 template <bool BF16>
-__device__ __forceinline__ uint4 pack_vec(const float (&acc)[BF16 ? 8 : 4]) {
-  uint4 o;
+__device__ __forceinline__ u32x4 pack_vec(const float (&acc)[BF16 ? 8 : 4]) {
+  u32x4 o;
   if constexpr (BF16) {
-    o.x = pack_bf16x2(acc[0], acc[1]);
-    o.y = pack_bf16x2(acc[2], acc[3]);
-    o.z = pack_bf16x2(acc[4], acc[5]);
-    o.w = pack_bf16x2(acc[6], acc[7]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o[j] = pack_bf16x2(acc[2 * j], acc[2 * j + 1]);
   } else {
-    o.x = __float_as_uint(acc[0]);
-    o.y = __float_as_uint(acc[1]);
-    o.z = __float_as_uint(acc[2]);
-    o.w = __float_as_uint(acc[3]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o[j] = __float_as_uint(acc[j]);
   }
   return o;
 }
 
-template <bool BF16>
-__global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ y,
+// KT > 0: K known at compile time; U output vectors per iteration, so U*KT
+// independent 16-byte gathers are in flight per lane.  KT == 0: any K, one
+// output vector per iteration, gathers in groups of 4.
+template <bool BF16, int KT, int U>
+__global__ __launch_bounds__(256) void combine_kernel(const u32x4* __restrict__ y,
                                                       const int32_t* __restrict__ inv,
                                                       const float* __restrict__ w, int64_t N,
-                                                      int K, int row_vecs,
-                                                      uint4* __restrict__ out) {
+                                                      int Krt, int row_vecs,
+                                                      u32x4* __restrict__ out) {
   constexpr int L = BF16 ? 8 : 4;
+  const int K = KT > 0 ? KT : Krt;
   extern __shared__ int dyn[];  // rows[kCombineTokens*K] then weights
   int* lrow = dyn;
   float* lw = reinterpret_cast<float*>(dyn + kCombineTokens * K);
@@ -74,33 +99,81 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
   __syncthreads();
 
   const int total = ntok * row_vecs;
-  uint4* os = out + n0 * (int64_t)row_vecs;
-  for (int idx = tid; idx < total; idx += 256) {
-    const int tt = idx / row_vecs;
-    const int c = idx - tt * row_vecs;
-    float acc[L];
+  u32x4* os = out + n0 * (int64_t)row_vecs;
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  if constexpr (KT > 0) {
+    for (int base = tid; base < total; base += 256 * U) {
+      u32x4 v[U][KT];
+      int tt[U], c[U];
 #pragma unroll
-    for (int j = 0; j < L; ++j) acc[j] = 0.f;
-    const int* rr = lrow + tt * K;
-    const float* ww = lw + tt * K;
-    int k = 0;
-    // groups of 4 independent gathers in flight
-    for (; k + 4 <= K; k += 4) {
-      uint4 v[4];
+      for (int u = 0; u < U; ++u) {
+        const int idx = min(base + u * 256, total - 1);
+        tt[u] = idx / row_vecs;
+        c[u] = idx - tt[u] * row_vecs;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int rrow = rr[k + u];
-        v[u] = rrow >= 0 ? y[(int64_t)rrow * row_vecs + c] : uint4{0u, 0u, 0u, 0u};
+        for (int k = 0; k < KT; ++k) {
+          const int rrow = lrow[tt[u] * KT + k];
+          v[u][k] = rrow >= 0 ? ld_vec(y + (int64_t)rrow * row_vecs + c[u]) : zero;
+        }
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (rr[k + u] >= 0) fma_vec<BF16>(acc, ww[k + u], v[u]);
+      for (int u = 0; u < U; ++u) {
+        float acc[L];
+#pragma unroll
+        for (int j = 0; j < L; ++j) acc[j] = 0.f;
+#pragma unroll
+        for (int k = 0; k < KT; ++k)
+          if (lrow[tt[u] * KT + k] >= 0) fma_vec<BF16>(acc, lw[tt[u] * KT + k], v[u][k]);
+        if (base + u * 256 < total) st_vec(os + (int64_t)tt[u] * row_vecs + c[u], pack_vec<BF16>(acc));
+      }
     }
-    for (; k < K; ++k) {
-      const int rrow = rr[k];
-      if (rrow >= 0) fma_vec<BF16>(acc, ww[k], y[(int64_t)rrow * row_vecs + c]);
+  } else {
+    for (int idx = tid; idx < total; idx += 256) {
+      const int tt = idx / row_vecs;
+      const int c = idx - tt * row_vecs;
+      float acc[L];
+#pragma unroll
+      for (int j = 0; j < L; ++j) acc[j] = 0.f;
+      const int* rr = lrow + tt * K;
+      const float* ww = lw + tt * K;
+      int k = 0;
+      for (; k + 4 <= K; k += 4) {
+        u32x4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          v[u] = rr[k + u] >= 0 ? ld_vec(y + (int64_t)rr[k + u] * row_vecs + c) : zero;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (rr[k + u] >= 0) fma_vec<BF16>(acc, ww[k + u], v[u]);
+      }
+      for (; k < K; ++k)
+        if (rr[k] >= 0) fma_vec<BF16>(acc, ww[k], ld_vec(y + (int64_t)rr[k] * row_vecs + c));
+      st_vec(os + (int64_t)tt * row_vecs + c, pack_vec<BF16>(acc));
     }
-    os[(int64_t)tt * row_vecs + c] = pack_vec<BF16>(acc);
+  }
+}
+
+template <bool BF16, int KT, int U>
+hipError_t launch_k(const void* y, const int32_t* inv, const float* w, int64_t N, int H, int K,
+                    void* out, hipStream_t s) {
+  const int64_t blocks = (N + kCombineTokens - 1) / kCombineTokens;
+  const int row_vecs = BF16 ? H / 8 : H / 4;
+  const size_t dyn = (sizeof(int) + sizeof(float)) * (size_t)kCombineTokens * K;
+  hipLaunchKernelGGL((combine_kernel<BF16, KT, U>), dim3((unsigned)blocks), dim3(256), dyn, s,
+                     reinterpret_cast<const u32x4*>(y), inv, w, N, K, row_vecs,
+                     reinterpret_cast<u32x4*>(out));
+  return hipGetLastError();
+}
+
+template <bool BF16>
+hipError_t launch_dtype(const void* y, const int32_t* inv, const float* w, int64_t N, int H,
+                        int K, void* out, hipStream_t s) {
+  switch (K) {
+    case 1: return launch_k<BF16, 1, 8>(y, inv, w, N, H, K, out, s);
+    case 2: return launch_k<BF16, 2, 4>(y, inv, w, N, H, K, out, s);
+    case 4: return launch_k<BF16, 4, 2>(y, inv, w, N, H, K, out, s);
+    case 8: return launch_k<BF16, 8, 2>(y, inv, w, N, H, K, out, s);
+    default: return launch_k<BF16, 0, 1>(y, inv, w, N, H, K, out, s);
   }
 }
 
@@ -108,18 +181,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
 
 hipError_t launch_combine(const void* y, const int32_t* inv, const float* w, int64_t N, int H,
                           int K, bool bf16, void* out, hipStream_t s) {
-  const int64_t blocks = (N + kCombineTokens - 1) / kCombineTokens;
-  const int row_vecs = bf16 ? H / 8 : H / 4;
-  const size_t dyn = (sizeof(int) + sizeof(float)) * (size_t)kCombineTokens * K;
-  if (bf16)
-    hipLaunchKernelGGL(combine_kernel<true>, dim3((unsigned)blocks), dim3(256), dyn, s,
-                       reinterpret_cast<const uint4*>(y), inv, w, N, K, row_vecs,
-                       reinterpret_cast<uint4*>(out));
-  else
-    hipLaunchKernelGGL(combine_kernel<false>, dim3((unsigned)blocks), dim3(256), dyn, s,
-                       reinterpret_cast<const uint4*>(y), inv, w, N, K, row_vecs,
-                       reinterpret_cast<uint4*>(out));
-  return hipGetLastError();
+  return bf16 ? launch_dtype<true>(y, inv, w, N, H, K, out, s)
+              : launch_dtype<false>(y, inv, w, N, H, K, out, s);
 }
 
 }  // namespace moe

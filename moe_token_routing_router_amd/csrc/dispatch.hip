@@ -25,9 +25,35 @@
 // inv entry is -1 and no row is written for it (no out-of-range access).
 #include "moe_internal.h"
 
+// Tuning knobs (compile-time; the defaults are the measured best on MI355X).
+#ifndef MOE_SCATTER_U
+#define MOE_SCATTER_U 4        // row vectors loaded per lane before their stores
+#endif
+#ifndef MOE_SCATTER_NT
+#define MOE_SCATTER_NT 0       // non-temporal loads of x / stores of x_perm
+#endif
+
 namespace moe {
 
 namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ u32x4 ld_row(const u32x4* p) {
+#if MOE_SCATTER_NT
+  return __builtin_nontemporal_load(p);
+#else
+  return *p;
+#endif
+}
+
+__device__ __forceinline__ void st_row(u32x4* p, u32x4 v) {
+#if MOE_SCATTER_NT
+  __builtin_nontemporal_store(v, p);
+#else
+  *p = v;
+#endif
+}
 
 // Exclusive scan of one int per thread over a 256-thread block.
 // `lds` needs 4 ints.  Returns the exclusive prefix; *total gets the sum.
@@ -97,7 +123,7 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
     const int32_t* __restrict__ ids, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ blockcnt, int64_t N, int K, int E, int num_sub,
     int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv,
-    const uint4* __restrict__ x, uint4* __restrict__ x_perm, int row_vecs) {
+    const u32x4* __restrict__ x, u32x4* __restrict__ x_perm, int row_vecs) {
   extern __shared__ int dyn[];  // sid[S] then dst[S], S = kDispatchTokens*K
   __shared__ int off[kMaxExperts];
   __shared__ int scan_lds[4];
@@ -143,15 +169,15 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
 
   // copy: flat index over (token, 16-byte column); each row is read once and
   // stored to its K dispatched rows.  U loads are issued before their stores.
-  constexpr int U = 4;
+  constexpr int U = MOE_SCATTER_U;
   const int total = ntok * row_vecs;
-  const uint4* xs = x + n0 * (int64_t)row_vecs;
+  const u32x4* xs = x + n0 * (int64_t)row_vecs;
   for (int base = tid; base < total; base += 256 * U) {
-    uint4 v[U];
+    u32x4 v[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int idx = min(base + u * 256, total - 1);
-      v[u] = xs[idx];  // idx < ntok * row_vecs: token idx / row_vecs of this block
+      v[u] = ld_row(xs + idx);  // idx < ntok * row_vecs: token idx / row_vecs of this block
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -162,7 +188,7 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
         const int* dd = dst + tt * K;
         for (int k = 0; k < K; ++k) {
           const int d = dd[k];
-          if (d >= 0) x_perm[(int64_t)d * row_vecs + c] = v[u];
+          if (d >= 0) st_row(x_perm + (int64_t)d * row_vecs + c, v[u]);
         }
       }
     }
@@ -188,7 +214,7 @@ hipError_t launch_dispatch(const int32_t* ids, const void* x, int64_t N, int64_t
   const size_t dyn = sizeof(int) * 2 * (size_t)kDispatchTokens * K;
   hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(num_sub), dim3(256), dyn, s, ids, counts,
                      blockcnt, N, K, E, num_sub, offsets, perm, inv,
-                     reinterpret_cast<const uint4*>(x), reinterpret_cast<uint4*>(x_perm),
+                     reinterpret_cast<const u32x4*>(x), reinterpret_cast<u32x4*>(x_perm),
                      (int)(row_bytes / 16));
   return hipGetLastError();
 }

@@ -10,7 +10,10 @@ namespace moe {
 // ---- limits -------------------------------------------------------------
 constexpr int kMaxExperts = 256;     // selection range of the fused router
 constexpr int kMaxRouteK = 16;       // one 16-lane group keeps one pick per lane
-constexpr int kDispatchTokens = 16;  // tokens per dispatch sub-chunk
+#ifndef MOE_DISPATCH_TOKENS
+#define MOE_DISPATCH_TOKENS 16
+#endif
+constexpr int kDispatchTokens = MOE_DISPATCH_TOKENS;  // tokens per dispatch sub-chunk
 
 // ---- vector types -------------------------------------------------------
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -35,6 +38,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // ---- launchers (each validates nothing: the C ABI layer has done it) -----
 // Router.  wgt is the expert-major padded gate (bf16 path only).
 int route_padded_experts(int E);
+int route_gate_stride(int H);  // row stride (elements) of the expert-major gate
 hipError_t launch_gate_transpose(const uint16_t* gate_w, int H, int E, uint16_t* wgt,
                                  int32_t* counts, hipStream_t s);
 hipError_t launch_route_bf16(const uint16_t* x, const uint16_t* wgt, const float* bias,

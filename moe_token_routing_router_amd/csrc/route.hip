@@ -25,11 +25,32 @@
 // logits the full-E softmax denominator cancels and is not formed.
 #include "moe_internal.h"
 
+// Tuning knobs (compile-time; the defaults are the measured best on MI355X).
+#ifndef MOE_ROUTE_NW
+#define MOE_ROUTE_NW 4       // waves per workgroup, splitting H
+#endif
+#ifndef MOE_ROUTE_MT64
+#define MOE_ROUTE_MT64 4     // 16-token M-tiles per workgroup for E <= 64
+#endif
+#ifndef MOE_ROUTE_MT128
+#define MOE_ROUTE_MT128 2    // ... for 64 < E <= 128
+#endif
+#ifndef MOE_ROUTE_ROTATE
+#define MOE_ROUTE_ROTATE 1   // stagger each workgroup's first H step
+#endif
+#ifndef MOE_ROUTE_DEPTH
+#define MOE_ROUTE_DEPTH 2    // steps of register prefetch (1 or 2) for E <= 64
+#endif
+#ifndef MOE_GATE_PAD
+#define MOE_GATE_PAD 128     // elements of padding per expert-major gate row
+#endif
+
 namespace moe {
 
 namespace {
 
 constexpr int kSentinel = 0x7fffffff;
+constexpr int kGatePad = MOE_GATE_PAD;
 
 // K rounds of arg-max over one token's logits held by a 16-lane group, then
 // w_k = exp(l_k - l_0) / sum_j exp(l_j - l_0) for the K picks.  Lane r keeps
@@ -84,7 +105,9 @@ __device__ __forceinline__ void select_topk_store(const float (&v)[NT], int r, i
   }
 }
 
-__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) {
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4 u) {
   return __builtin_bit_cast(bf16x8_t, u);
 }
 
@@ -98,9 +121,9 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) {
 // (lane group, element) -> h map, so each MFMA sums over 32 distinct h and
 // every h in [h0, h0+64) is covered once.  Accumulator element i of lane l
 // is D[4g + i][r]: token 16m + 4g + i, expert 16q + r.
-template <int NT, int MT, int NW>
+template <int NT, int MT, int NW, int D>
 __global__ __launch_bounds__(NW * 64) void route_bf16_kernel(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wgt,
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wgt, int ldw,
     const float* __restrict__ bias, int64_t N, int H, int E, int K, int32_t* __restrict__ ids,
     float* __restrict__ topw, int32_t* __restrict__ counts) {
   constexpr int BM = 16 * MT;
@@ -130,7 +153,7 @@ __global__ __launch_bounds__(NW * 64) void route_bf16_kernel(
   }
   const uint16_t* brow[NT];
 #pragma unroll
-  for (int q = 0; q < NT; ++q) brow[q] = wgt + (int64_t)(16 * q + r) * H + 16 * g;
+  for (int q = 0; q < NT; ++q) brow[q] = wgt + (int64_t)(16 * q + r) * ldw + 16 * g;
 
   f32x4_t acc[MT][NT];
 #pragma unroll
@@ -141,49 +164,136 @@ __global__ __launch_bounds__(NW * 64) void route_bf16_kernel(
   const int nss = (H + 63) >> 6;
   const int s_begin = (wid * nss) / NW;
   const int s_end = ((wid + 1) * nss) / NW;
-  const uint4 zero = {0u, 0u, 0u, 0u};
 
-  uint4 a0[MT], a1[MT], b0[NT], b1[NT];
-  auto load = [&](int s) {
-    const int h = s * 64;          // this lane's columns: h + 16g + [0, 16)
-    const int hl = h + 16 * g;
-    const bool ok0 = hl < H;       // H % 8 == 0: each 8-wide half is all in or all out
-    const bool ok1 = hl + 8 < H;
+  // One 64-wide step of h: per lane 2 x 16 bytes of each of its MT token rows
+  // and NT expert rows.  Full steps use plain 16-byte loads that stay in
+  // flight until the MFMAs consume them; only a ragged last step
+  // (H % 64 != 0) takes the masked path, where a half beyond H reads column 0
+  // of its row and is replaced by zeros.
+  struct Buf {
+    u32x4 a0[MT], a1[MT], b0[NT], b1[NT];
+  };
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  auto load = [&](Buf& bf, int s) {
+    const int o = s * 64;
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
-      a0[m] = ok0 ? *reinterpret_cast<const uint4*>(arow[m] + h) : zero;
-      a1[m] = ok1 ? *reinterpret_cast<const uint4*>(arow[m] + h + 8) : zero;
+      bf.a0[m] = *reinterpret_cast<const u32x4*>(arow[m] + o);
+      bf.a1[m] = *reinterpret_cast<const u32x4*>(arow[m] + o + 8);
     }
 #pragma unroll
     for (int q = 0; q < NT; ++q) {
-      b0[q] = ok0 ? *reinterpret_cast<const uint4*>(brow[q] + h) : zero;
-      b1[q] = ok1 ? *reinterpret_cast<const uint4*>(brow[q] + h + 8) : zero;
+      bf.b0[q] = *reinterpret_cast<const u32x4*>(brow[q] + o);
+      bf.b1[q] = *reinterpret_cast<const u32x4*>(brow[q] + o + 8);
     }
   };
-
-  if (s_begin < s_end) load(s_begin);
-  for (int s = s_begin; s < s_end; ++s) {
-    uint4 c0[MT], c1[MT], d0[NT], d1[NT];
+  auto load_masked = [&](Buf& bf, int s) {
+    const int hl = s * 64 + 16 * g;  // this lane's columns: hl + [0, 16)
+    const bool ok0 = hl < H;         // H % 8 == 0: each 8-wide half is all in or all out
+    const bool ok1 = hl + 8 < H;
+    const int o0 = ok0 ? s * 64 : -16 * g;
+    const int o1 = ok1 ? s * 64 + 8 : -16 * g;
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
-      c0[m] = a0[m];
-      c1[m] = a1[m];
+      const u32x4 v0 = *reinterpret_cast<const u32x4*>(arow[m] + o0);
+      const u32x4 v1 = *reinterpret_cast<const u32x4*>(arow[m] + o1);
+      bf.a0[m] = ok0 ? v0 : zero;
+      bf.a1[m] = ok1 ? v1 : zero;
     }
 #pragma unroll
     for (int q = 0; q < NT; ++q) {
-      d0[q] = b0[q];
-      d1[q] = b1[q];
+      const u32x4 v0 = *reinterpret_cast<const u32x4*>(brow[q] + o0);
+      const u32x4 v1 = *reinterpret_cast<const u32x4*>(brow[q] + o1);
+      bf.b0[q] = ok0 ? v0 : zero;
+      bf.b1[q] = ok1 ? v1 : zero;
     }
-    if (s + 1 < s_end) load(s + 1);  // next step's loads overlap this step's MFMAs
+  };
+  // MT*NT independent accumulators: consecutive MFMAs never depend on each
+  // other
+  auto mma = [&](const Buf& bf) {
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
-      for (int q = 0; q < NT; ++q) {
-        acc[m][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(c0[m]), as_bf16x8(d0[q]),
+      for (int q = 0; q < NT; ++q)
+        acc[m][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(bf.a0[m]), as_bf16x8(bf.b0[q]),
                                                             acc[m][q], 0, 0, 0);
-        acc[m][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(c1[m]), as_bf16x8(d1[q]),
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int q = 0; q < NT; ++q)
+        acc[m][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(bf.a1[m]), as_bf16x8(bf.b1[q]),
                                                             acc[m][q], 0, 0, 0);
+  };
+
+  // Each workgroup walks its H range starting at a different step (rotated
+  // by the workgroup index), so that at any moment the resident workgroups
+  // read different column windows of their rows: all rows are H*2 bytes
+  // apart, and reading the same window of every row at once would load only
+  // a few memory channels.
+  const int nfull = H >> 6;  // steps with all 64 columns inside H
+  const int s_stop = s_end < nfull ? s_end : nfull;
+  const int cnt = s_stop > s_begin ? s_stop - s_begin : 0;
+  const int rot = (MOE_ROUTE_ROTATE && cnt > 0) ? (int)(blockIdx.x % (unsigned)cnt) : 0;
+  auto step_of = [&](int i) {
+    int s = s_begin + rot + i;
+    return s >= s_stop ? s - cnt : s;
+  };
+  // Software pipeline over register buffers.  The loop bodies have no
+  // branches (a branch there makes the compiler drain every outstanding load
+  // at the loop head): the prefetch is always issued, clamped to the last
+  // step, so the final iterations reload a step that is already cached.
+  // Software pipeline over register buffers.  The loop bodies have no
+  // branches (a branch there makes the compiler drain every outstanding load
+  // at the loop head): the prefetch is always issued, clamped to the last
+  // step, so the final iterations reload a step that is already cached.  A
+  // scheduling barrier after each prefetch keeps its loads ahead of the
+  // MFMAs, which then wait only for their own (older) loads.
+  if (cnt > 0) {
+    const int last = cnt - 1;
+    if constexpr (D >= 2) {
+      // three buffers: two steps of loads in flight during each step's MFMAs
+      Buf p0, p1, p2;
+      load(p0, step_of(0));
+      load(p1, step_of(min(1, last)));
+      int i = 0;
+      for (; i + 3 <= cnt; i += 3) {
+        load(p2, step_of(i + 2));
+        __builtin_amdgcn_sched_barrier(0);
+        mma(p0);
+        __builtin_amdgcn_sched_barrier(0);
+        load(p0, step_of(min(i + 3, last)));
+        __builtin_amdgcn_sched_barrier(0);
+        mma(p1);
+        __builtin_amdgcn_sched_barrier(0);
+        load(p1, step_of(min(i + 4, last)));
+        __builtin_amdgcn_sched_barrier(0);
+        mma(p2);
+        __builtin_amdgcn_sched_barrier(0);
       }
+      if (cnt - i >= 1) mma(p0);
+      if (cnt - i >= 2) mma(p1);
+    } else {
+      // two buffers: one step of loads in flight during each step's MFMAs
+      Buf p, q;
+      load(p, step_of(0));
+      int i = 0;
+      for (; i + 2 <= cnt; i += 2) {
+        load(q, step_of(i + 1));
+        __builtin_amdgcn_sched_barrier(0);
+        mma(p);
+        __builtin_amdgcn_sched_barrier(0);
+        load(p, step_of(min(i + 2, last)));
+        __builtin_amdgcn_sched_barrier(0);
+        mma(q);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (i < cnt) mma(p);
+    }
+  }
+  if (s_end > nfull && nfull >= s_begin) {  // the ragged last step, if this wave owns it
+    Buf t;
+    load_masked(t, nfull);
+    mma(t);
   }
 
 #pragma unroll
@@ -272,29 +382,50 @@ __global__ __launch_bounds__(256) void route_f32_kernel(const float* __restrict_
 }
 
 // ------------------------------------------------------- gate re-layout
-// wgt[e][h] = gate_w[h][e] for e < E, 0 for E <= e < EP; 64x64 tiles through
-// LDS.  Block (0,0) also zeroes counts (the router then adds into it).
-__global__ __launch_bounds__(256) void gate_transpose_kernel(const uint16_t* __restrict__ gate_w,
-                                                             int H, int E, int EP,
-                                                             uint16_t* __restrict__ wgt,
-                                                             int32_t* __restrict__ counts) {
-  __shared__ uint16_t tile[64][66];
-  const int h0 = blockIdx.x * 64;
-  const int e0 = blockIdx.y * 64;
-  const int tid = threadIdx.x;
-  for (int i = tid; i < 64 * 64; i += 256) {
-    const int hh = i >> 6, ee = i & 63;
-    const int h = h0 + hh, e = e0 + ee;
-    tile[hh][ee] = (h < H && e < E) ? gate_w[(int64_t)h * E + e] : (uint16_t)0;
+// wgt[e][h] = gate_w[h][e] for e < E and 0 for E <= e < EP, rows ldw
+// elements apart (ldw = H + kGatePad: the pad staggers the rows over the
+// memory channels).  Each thread moves one 8(h) x 8(e) block: eight 16-byte
+// loads, a register transpose, eight 16-byte stores; consecutive threads take
+// consecutive h blocks so the stores are contiguous.  Thread 0.. also zero
+// `counts` (the router then adds into it).
+__global__ __launch_bounds__(64) void gate_transpose_kernel(const uint16_t* __restrict__ gate_w,
+                                                            int H, int E, int EP, int ldw,
+                                                            uint16_t* __restrict__ wgt,
+                                                            int32_t* __restrict__ counts) {
+  const int64_t idx = (int64_t)blockIdx.x * 64 + threadIdx.x;
+  if (counts && idx < E) counts[idx] = 0;
+  const int nhb = H / 8;
+  if (idx >= (int64_t)nhb * (EP / 8)) return;
+  const int eb = (int)(idx / nhb);
+  const int hb = (int)(idx - (int64_t)eb * nhb);
+  const int h0 = hb * 8, e0 = eb * 8;
+  uint32_t v[8][4];  // v[i] = 8 bf16 of gate row h0+i, experts e0..e0+7 (2 per word)
+  const bool vec = (E % 8 == 0) && (e0 + 8 <= E);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint16_t* src = gate_w + (int64_t)(h0 + i) * E + e0;
+    if (vec) {
+      const uint4 u = *reinterpret_cast<const uint4*>(src);
+      v[i][0] = u.x; v[i][1] = u.y; v[i][2] = u.z; v[i][3] = u.w;
+    } else {
+      uint16_t t[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) t[j] = (e0 + j < E) ? src[j] : (uint16_t)0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[i][j] = (uint32_t)t[2 * j] | ((uint32_t)t[2 * j + 1] << 16);
+    }
   }
-  __syncthreads();
-  for (int i = tid; i < 64 * 64; i += 256) {
-    const int ee = i >> 6, hh = i & 63;
-    const int h = h0 + hh, e = e0 + ee;
-    if (h < H && e < EP) wgt[(int64_t)e * H + h] = tile[hh][ee];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {  // expert e0+j: its 8 values of h0..h0+7
+    uint32_t o[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const uint32_t lo = (v[2 * p][j >> 1] >> (16 * (j & 1))) & 0xffffu;
+      const uint32_t hi = (v[2 * p + 1][j >> 1] >> (16 * (j & 1))) & 0xffffu;
+      o[p] = lo | (hi << 16);
+    }
+    *reinterpret_cast<uint4*>(wgt + (int64_t)(e0 + j) * ldw + h0) = uint4{o[0], o[1], o[2], o[3]};
   }
-  if (counts && blockIdx.x == 0 && blockIdx.y == 0)
-    for (int e = tid; e < E; e += 256) counts[e] = 0;
 }
 
 __global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
@@ -302,14 +433,13 @@ __global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
   if (i < n) p[i] = v;
 }
 
-template <int NT, int MT>
+template <int NT, int MT, int NW = MOE_ROUTE_NW, int D = (NT <= 4 ? MOE_ROUTE_DEPTH : 1)>
 hipError_t launch_bf16_nt(const uint16_t* x, const uint16_t* wgt, const float* bias, int64_t N,
                           int H, int E, int K, int32_t* ids, float* w, int32_t* counts,
                           hipStream_t s) {
-  constexpr int NW = 4;
   const int64_t blocks = (N + 16 * MT - 1) / (16 * MT);
-  hipLaunchKernelGGL((route_bf16_kernel<NT, MT, NW>), dim3((unsigned)blocks), dim3(NW * 64), 0,
-                     s, x, wgt, bias, N, H, E, K, ids, w, counts);
+  hipLaunchKernelGGL((route_bf16_kernel<NT, MT, NW, D>), dim3((unsigned)blocks), dim3(NW * 64), 0,
+                     s, x, wgt, route_gate_stride(H), bias, N, H, E, K, ids, w, counts);
   return hipGetLastError();
 }
 
@@ -337,11 +467,15 @@ hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s) {
   return hipGetLastError();
 }
 
+int route_gate_stride(int H) { return H + kGatePad; }
+
 hipError_t launch_gate_transpose(const uint16_t* gate_w, int H, int E, uint16_t* wgt,
                                  int32_t* counts, hipStream_t s) {
   const int EP = route_padded_experts(E);
-  dim3 grid((unsigned)((H + 63) / 64), (unsigned)((EP + 63) / 64));
-  hipLaunchKernelGGL(gate_transpose_kernel, grid, dim3(256), 0, s, gate_w, H, E, EP, wgt, counts);
+  int64_t threads = (int64_t)(H / 8) * (EP / 8);
+  if (threads < E) threads = E;
+  hipLaunchKernelGGL(gate_transpose_kernel, dim3((unsigned)((threads + 63) / 64)), dim3(64), 0, s,
+                     gate_w, H, E, EP, route_gate_stride(H), wgt, counts);
   return hipGetLastError();
 }
 
@@ -351,9 +485,9 @@ hipError_t launch_route_bf16(const uint16_t* x, const uint16_t* wgt, const float
   switch (route_padded_experts(E)) {
     case 16: return launch_bf16_nt<1, 4>(x, wgt, bias, N, H, E, K, ids, w, counts, s);
     case 32: return launch_bf16_nt<2, 4>(x, wgt, bias, N, H, E, K, ids, w, counts, s);
-    case 64: return launch_bf16_nt<4, 4>(x, wgt, bias, N, H, E, K, ids, w, counts, s);
-    case 128: return launch_bf16_nt<8, 2>(x, wgt, bias, N, H, E, K, ids, w, counts, s);
-    case 256: return launch_bf16_nt<16, 1>(x, wgt, bias, N, H, E, K, ids, w, counts, s);
+    case 64: return launch_bf16_nt<4, MOE_ROUTE_MT64>(x, wgt, bias, N, H, E, K, ids, w, counts, s);
+    case 128: return launch_bf16_nt<8, MOE_ROUTE_MT128>(x, wgt, bias, N, H, E, K, ids, w, counts, s);
+    case 256: return launch_bf16_nt<16, 1, 4>(x, wgt, bias, N, H, E, K, ids, w, counts, s);
   }
   return hipErrorInvalidValue;
 }

@@ -305,7 +305,7 @@ def test_round_trip_identity_experts(dtype):
         xp = O.permute_rows(case["x"], perm, K)
         out = O.combine(xp, inv, w, dtype)
         if dtype == "bf16":
-            np.testing.assert_array_equal(out, case["x"])
+            np.testing.assert_array_equal(_decode(out, dtype), _decode(case["x"], dtype))
         else:
             np.testing.assert_allclose(out, case["x"], rtol=4e-7, atol=0)
 
@@ -364,3 +364,10 @@ def test_combine_rounds_once_to_bf16():
     w = np.array([[1 + 2 ** -8, 2 ** -10]], np.float32)
     out = O.combine(y, np.array([0, 1], np.int32), w, "bf16")
     assert int(out[0, 0]) == 0x3F81
+
+
+def test_combine_negative_zero_row_sums_to_positive_zero():
+    # IEEE: the sum starts from +0, and +0 + (-0) = +0
+    y = np.array([[0x8000, 0x3F80], [0x8000, 0x3F80]], np.uint16)
+    out = O.combine(y, np.array([0, 1], np.int32), np.array([[0.5, 0.5]], np.float32), "bf16")
+    assert out[0, 0] == 0x0000 and out[0, 1] == 0x3F80
