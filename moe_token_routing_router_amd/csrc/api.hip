@@ -41,8 +41,7 @@ const char* moe_status_string(moe_status_t status) {
 
 size_t moe_route_workspace_size(int32_t H, int32_t E, moe_dtype_t dtype) {
   if (dtype != MOE_BF16 || H <= 0 || E <= 0 || E > moe::kMaxExperts) return 0;
-  return round_up((size_t)moe::route_padded_experts(E) * (size_t)moe::route_gate_stride(H) * 2,
-                  256);
+  return round_up((size_t)moe::route_padded_experts(E) * (size_t)moe::route_gate_rows(H) * 2, 256);
 }
 
 moe_status_t moe_route(const void* x, const void* gate_w, const float* bias, int64_t N, int32_t H,

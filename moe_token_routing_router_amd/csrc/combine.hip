@@ -16,10 +16,13 @@
 
 // Tuning knobs (compile-time; the defaults are the measured best on MI355X).
 #ifndef MOE_COMBINE_TOKENS
-#define MOE_COMBINE_TOKENS 8   // tokens per workgroup
+#define MOE_COMBINE_TOKENS 1   // tokens per workgroup
 #endif
-#ifndef MOE_COMBINE_NT
-#define MOE_COMBINE_NT 1       // non-temporal loads of y / stores of out
+#ifndef MOE_COMBINE_NT_LOAD
+#define MOE_COMBINE_NT_LOAD 1   // non-temporal loads of y (each row is read once)
+#endif
+#ifndef MOE_COMBINE_NT_STORE
+#define MOE_COMBINE_NT_STORE 1  // non-temporal stores of out
 #endif
 
 namespace moe {
@@ -31,7 +34,7 @@ constexpr int kCombineTokens = MOE_COMBINE_TOKENS;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ u32x4 ld_vec(const u32x4* p) {
-#if MOE_COMBINE_NT
+#if MOE_COMBINE_NT_LOAD
   return __builtin_nontemporal_load(p);
 #else
   return *p;
@@ -39,7 +42,7 @@ __device__ __forceinline__ u32x4 ld_vec(const u32x4* p) {
 }
 
 __device__ __forceinline__ void st_vec(u32x4* p, u32x4 v) {
-#if MOE_COMBINE_NT
+#if MOE_COMBINE_NT_STORE
   __builtin_nontemporal_store(v, p);
 #else
   *p = v;

@@ -29,8 +29,11 @@
 #ifndef MOE_SCATTER_U
 #define MOE_SCATTER_U 4        // row vectors loaded per lane before their stores
 #endif
-#ifndef MOE_SCATTER_NT
-#define MOE_SCATTER_NT 0       // non-temporal loads of x / stores of x_perm
+#ifndef MOE_SCATTER_NT_LOAD
+#define MOE_SCATTER_NT_LOAD 1  // non-temporal loads of x
+#endif
+#ifndef MOE_SCATTER_NT_STORE
+#define MOE_SCATTER_NT_STORE 1 // non-temporal stores of x_perm (keeps them out of L2/MALL)
 #endif
 
 namespace moe {
@@ -40,7 +43,7 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ u32x4 ld_row(const u32x4* p) {
-#if MOE_SCATTER_NT
+#if MOE_SCATTER_NT_LOAD
   return __builtin_nontemporal_load(p);
 #else
   return *p;
@@ -48,7 +51,7 @@ __device__ __forceinline__ u32x4 ld_row(const u32x4* p) {
 }
 
 __device__ __forceinline__ void st_row(u32x4* p, u32x4 v) {
-#if MOE_SCATTER_NT
+#if MOE_SCATTER_NT_STORE
   __builtin_nontemporal_store(v, p);
 #else
   *p = v;

@@ -36,9 +36,9 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 // ---- launchers (each validates nothing: the C ABI layer has done it) -----
-// Router.  wgt is the expert-major padded gate (bf16 path only).
+// Router.  wgt is the fragment-major packed gate (bf16 path only).
 int route_padded_experts(int E);
-int route_gate_stride(int H);  // row stride (elements) of the expert-major gate
+int route_gate_rows(int H);  // H rounded up to whole 64-wide steps (packed gate)
 hipError_t launch_gate_transpose(const uint16_t* gate_w, int H, int E, uint16_t* wgt,
                                  int32_t* counts, hipStream_t s);
 hipError_t launch_route_bf16(const uint16_t* x, const uint16_t* wgt, const float* bias,

@@ -27,22 +27,19 @@
 
 // Tuning knobs (compile-time; the defaults are the measured best on MI355X).
 #ifndef MOE_ROUTE_NW
-#define MOE_ROUTE_NW 4       // waves per workgroup, splitting H
+#define MOE_ROUTE_NW 8       // waves per workgroup, splitting H (E <= 64)
 #endif
 #ifndef MOE_ROUTE_MT64
 #define MOE_ROUTE_MT64 4     // 16-token M-tiles per workgroup for E <= 64
 #endif
 #ifndef MOE_ROUTE_MT128
-#define MOE_ROUTE_MT128 2    // ... for 64 < E <= 128
+#define MOE_ROUTE_MT128 4    // ... for 64 < E <= 128 (4 waves per workgroup)
 #endif
 #ifndef MOE_ROUTE_ROTATE
 #define MOE_ROUTE_ROTATE 1   // stagger each workgroup's first H step
 #endif
 #ifndef MOE_ROUTE_DEPTH
-#define MOE_ROUTE_DEPTH 2    // steps of register prefetch (1 or 2) for E <= 64
-#endif
-#ifndef MOE_GATE_PAD
-#define MOE_GATE_PAD 128     // elements of padding per expert-major gate row
+#define MOE_ROUTE_DEPTH 1    // steps of register prefetch (1 or 2) for E <= 64
 #endif
 
 namespace moe {
@@ -50,7 +47,8 @@ namespace moe {
 namespace {
 
 constexpr int kSentinel = 0x7fffffff;
-constexpr int kGatePad = MOE_GATE_PAD;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // K rounds of arg-max over one token's logits held by a 16-lane group, then
 // w_k = exp(l_k - l_0) / sum_j exp(l_j - l_0) for the K picks.  Lane r keeps
@@ -105,32 +103,44 @@ __device__ __forceinline__ void select_topk_store(const float (&v)[NT], int r, i
   }
 }
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4 u) {
   return __builtin_bit_cast(bf16x8_t, u);
 }
 
 // ---------------------------------------------------------------- bf16 MFMA
-// Grid: ceil(N / BM) workgroups of NW waves.  Each lane (r = lane%16,
-// g = lane/16) loads, per 64-wide step of h, 32 contiguous bytes of a token
-// row (A operand) and of an expert row of wgt (B operand):
-//   A[r][8g + j] = x[t0 + 16m + r][h0 + 16g + j]        (first MFMA)
-//   A[r][8g + j] = x[t0 + 16m + r][h0 + 16g + 8 + j]    (second MFMA)
-// and the same h for B from wgt[16q + r][...].  Both operands use the same
-// (lane group, element) -> h map, so each MFMA sums over 32 distinct h and
-// every h in [h0, h0+64) is covered once.  Accumulator element i of lane l
-// is D[4g + i][r]: token 16m + 4g + i, expert 16q + r.
+// Grid: ceil(N / BM) workgroups of NW waves, BM = 16*MT tokens each.  The NW
+// waves split H into contiguous ranges of 64-wide steps; every wave computes
+// fp32 partial logits of all BM tokens x EP experts over its range.
+//
+// A operand (token rows): per step, the wave's BM x 64 tile is read with
+// coalesced 16-byte loads (8 lanes cover one 128-byte row segment), written
+// to the wave's own LDS tile with an XOR swizzle (16-byte chunk c of row r is
+// stored at chunk c ^ (r & 7)) and read back in MFMA layout; the swizzle makes
+// both the writes and the fragment reads free of bank conflicts.
+// B operand (gate): the gate has been packed fragment-major by
+// gate_pack_kernel, so the B fragment of (step, expert tile q, half hf) is
+// one contiguous 1 KiB block -- lane l loads bytes [16l, 16l+16).
+//
+// MFMA v_mfma_f32_16x16x32_bf16, lane l = 16g + r:
+//   A[r][8g + j] = x[token 16m + r][h0 + 16g + 8hf + j]   (half hf = 0, 1)
+//   B[8g + j][r] = gate[h0 + 16g + 8hf + j][expert 16q + r]
+// both operands use the same (g, j) -> h map, so each MFMA pair sums h over
+// [h0, h0 + 64) once.  Accumulator element i of lane l is D[4g + i][r]:
+// token 16m + 4g + i, expert 16q + r.
 template <int NT, int MT, int NW, int D>
 __global__ __launch_bounds__(NW * 64) void route_bf16_kernel(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wgt, int ldw,
+    const uint16_t* __restrict__ x, const u32x4* __restrict__ gfrag,
     const float* __restrict__ bias, int64_t N, int H, int E, int K, int32_t* __restrict__ ids,
     float* __restrict__ topw, int32_t* __restrict__ counts) {
   constexpr int BM = 16 * MT;
   constexpr int EP = 16 * NT;
   constexpr int ROWP = EP + 4;
+  constexpr int ALD = BM / 8;  // A load instructions per step (8 rows x 128 B each)
+  constexpr int TILE = BM * 128;
+  constexpr int SMEM_A = NW * TILE;
+  constexpr int SMEM_P = NW * BM * ROWP * 4;
   static_assert(BM % (4 * NW) == 0, "epilogue maps 4 tokens per wave per pass");
-  __shared__ float part[NW][BM][ROWP];
+  __shared__ __align__(16) char smem[SMEM_A > SMEM_P ? SMEM_A : SMEM_P];
   __shared__ int hist[EP];
 
   const int tid = threadIdx.x;
@@ -144,16 +154,29 @@ __global__ __launch_bounds__(NW * 64) void route_bf16_kernel(
     for (int e = tid; e < EP; e += NW * 64) hist[e] = 0;
   }
 
-  const uint16_t* arow[MT];
+  // coalesced A loads: instruction j, lane -> (row 8j + lane/8, chunk lane%8)
+  const int lrow = lane >> 3;
+  const int lch = lane & 7;
+  const uint16_t* aptr[ALD];
+  int wofs[ALD];
 #pragma unroll
-  for (int m = 0; m < MT; ++m) {
-    int64_t t = t0 + 16 * m + r;
+  for (int j = 0; j < ALD; ++j) {
+    const int row = 8 * j + lrow;
+    int64_t t = t0 + row;
     if (t > N - 1) t = N - 1;  // tail rows recompute the last token; never stored
-    arow[m] = x + t * H + 16 * g;
+    aptr[j] = x + t * H + 8 * lch;
+    wofs[j] = row * 128 + ((lch ^ (row & 7)) << 4);
   }
-  const uint16_t* brow[NT];
+  // MFMA fragment reads: tile m, half hf -> (row 16m + r, chunk 2g + hf)
+  int rofs[MT][2];
 #pragma unroll
-  for (int q = 0; q < NT; ++q) brow[q] = wgt + (int64_t)(16 * q + r) * ldw + 16 * g;
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const int row = 16 * m + r;
+      rofs[m][hf] = row * 128 + (((2 * g + hf) ^ (row & 7)) << 4);
+    }
+  char* tile = smem + wid * TILE;
 
   f32x4_t acc[MT][NT];
 #pragma unroll
@@ -165,71 +188,68 @@ __global__ __launch_bounds__(NW * 64) void route_bf16_kernel(
   const int s_begin = (wid * nss) / NW;
   const int s_end = ((wid + 1) * nss) / NW;
 
-  // One 64-wide step of h: per lane 2 x 16 bytes of each of its MT token rows
-  // and NT expert rows.  Full steps use plain 16-byte loads that stay in
-  // flight until the MFMAs consume them; only a ragged last step
-  // (H % 64 != 0) takes the masked path, where a half beyond H reads column 0
-  // of its row and is replaced by zeros.
   struct Buf {
-    u32x4 a0[MT], a1[MT], b0[NT], b1[NT];
+    u32x4 a[ALD];
+    u32x4 b[NT][2];
   };
-  const u32x4 zero = {0u, 0u, 0u, 0u};
+  // Full steps: plain 16-byte loads that stay in flight until consumed.
   auto load = [&](Buf& bf, int s) {
-    const int o = s * 64;
 #pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      bf.a0[m] = *reinterpret_cast<const u32x4*>(arow[m] + o);
-      bf.a1[m] = *reinterpret_cast<const u32x4*>(arow[m] + o + 8);
-    }
+    for (int j = 0; j < ALD; ++j) bf.a[j] = *reinterpret_cast<const u32x4*>(aptr[j] + s * 64);
+    const u32x4* gb = gfrag + (size_t)s * NT * 128 + lane;
 #pragma unroll
     for (int q = 0; q < NT; ++q) {
-      bf.b0[q] = *reinterpret_cast<const u32x4*>(brow[q] + o);
-      bf.b1[q] = *reinterpret_cast<const u32x4*>(brow[q] + o + 8);
+      bf.b[q][0] = gb[(2 * q) * 64];
+      bf.b[q][1] = gb[(2 * q + 1) * 64];
     }
   };
+  // A ragged last step (H % 64 != 0): chunks beyond H read column 0 of
+  // their row and are replaced by zeros (the packed gate is zero there).
+  const u32x4 zero = {0u, 0u, 0u, 0u};
   auto load_masked = [&](Buf& bf, int s) {
-    const int hl = s * 64 + 16 * g;  // this lane's columns: hl + [0, 16)
-    const bool ok0 = hl < H;         // H % 8 == 0: each 8-wide half is all in or all out
-    const bool ok1 = hl + 8 < H;
-    const int o0 = ok0 ? s * 64 : -16 * g;
-    const int o1 = ok1 ? s * 64 + 8 : -16 * g;
+    const bool ok = s * 64 + 8 * lch < H;  // H % 8 == 0: a chunk is all in or all out
+    const int o = ok ? s * 64 : -8 * lch;
 #pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      const u32x4 v0 = *reinterpret_cast<const u32x4*>(arow[m] + o0);
-      const u32x4 v1 = *reinterpret_cast<const u32x4*>(arow[m] + o1);
-      bf.a0[m] = ok0 ? v0 : zero;
-      bf.a1[m] = ok1 ? v1 : zero;
+    for (int j = 0; j < ALD; ++j) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(aptr[j] + o);
+      bf.a[j] = ok ? v : zero;
     }
+    const u32x4* gb = gfrag + (size_t)s * NT * 128 + lane;
 #pragma unroll
     for (int q = 0; q < NT; ++q) {
-      const u32x4 v0 = *reinterpret_cast<const u32x4*>(brow[q] + o0);
-      const u32x4 v1 = *reinterpret_cast<const u32x4*>(brow[q] + o1);
-      bf.b0[q] = ok0 ? v0 : zero;
-      bf.b1[q] = ok1 ? v1 : zero;
+      bf.b[q][0] = gb[(2 * q) * 64];
+      bf.b[q][1] = gb[(2 * q + 1) * 64];
     }
   };
-  // MT*NT independent accumulators: consecutive MFMAs never depend on each
-  // other
+  // A tile through the wave's LDS tile, then MT*NT*2 MFMAs; consecutive
+  // MFMAs never depend on each other.  LDS operations of one wave complete in
+  // issue order, so each read sees the writes before it and the next step's
+  // writes follow this step's reads; the empty asm keeps the compiler from
+  // reordering them.
   auto mma = [&](const Buf& bf) {
 #pragma unroll
-    for (int m = 0; m < MT; ++m)
-#pragma unroll
-      for (int q = 0; q < NT; ++q)
-        acc[m][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(bf.a0[m]), as_bf16x8(bf.b0[q]),
-                                                            acc[m][q], 0, 0, 0);
+    for (int j = 0; j < ALD; ++j) *reinterpret_cast<u32x4*>(tile + wofs[j]) = bf.a[j];
+    asm volatile("" ::: "memory");
+    u32x4 af[MT][2];
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
-      for (int q = 0; q < NT; ++q)
-        acc[m][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(bf.a1[m]), as_bf16x8(bf.b1[q]),
-                                                            acc[m][q], 0, 0, 0);
+      for (int hf = 0; hf < 2; ++hf)
+        af[m][hf] = *reinterpret_cast<const u32x4*>(tile + rofs[m][hf]);
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int q = 0; q < NT; ++q)
+          acc[m][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              as_bf16x8(af[m][hf]), as_bf16x8(bf.b[q][hf]), acc[m][q], 0, 0, 0);
   };
 
-  // Each workgroup walks its H range starting at a different step (rotated
-  // by the workgroup index), so that at any moment the resident workgroups
-  // read different column windows of their rows: all rows are H*2 bytes
-  // apart, and reading the same window of every row at once would load only
-  // a few memory channels.
+  // Each workgroup walks its range starting at a different step (rotated by
+  // the workgroup index), so the resident workgroups read different column
+  // windows of their rows at any moment.
   const int nfull = H >> 6;  // steps with all 64 columns inside H
   const int s_stop = s_end < nfull ? s_end : nfull;
   const int cnt = s_stop > s_begin ? s_stop - s_begin : 0;
@@ -241,17 +261,12 @@ __global__ __launch_bounds__(NW * 64) void route_bf16_kernel(
   // Software pipeline over register buffers.  The loop bodies have no
   // branches (a branch there makes the compiler drain every outstanding load
   // at the loop head): the prefetch is always issued, clamped to the last
-  // step, so the final iterations reload a step that is already cached.
-  // Software pipeline over register buffers.  The loop bodies have no
-  // branches (a branch there makes the compiler drain every outstanding load
-  // at the loop head): the prefetch is always issued, clamped to the last
   // step, so the final iterations reload a step that is already cached.  A
   // scheduling barrier after each prefetch keeps its loads ahead of the
   // MFMAs, which then wait only for their own (older) loads.
   if (cnt > 0) {
     const int last = cnt - 1;
     if constexpr (D >= 2) {
-      // three buffers: two steps of loads in flight during each step's MFMAs
       Buf p0, p1, p2;
       load(p0, step_of(0));
       load(p1, step_of(min(1, last)));
@@ -273,7 +288,6 @@ __global__ __launch_bounds__(NW * 64) void route_bf16_kernel(
       if (cnt - i >= 1) mma(p0);
       if (cnt - i >= 2) mma(p1);
     } else {
-      // two buffers: one step of loads in flight during each step's MFMAs
       Buf p, q;
       load(p, step_of(0));
       int i = 0;
@@ -296,6 +310,10 @@ __global__ __launch_bounds__(NW * 64) void route_bf16_kernel(
     mma(t);
   }
 
+  // partial logits of all waves -> LDS (reusing the A tiles), summed in a
+  // fixed order
+  __syncthreads();
+  float(*part)[BM][ROWP] = reinterpret_cast<float(*)[BM][ROWP]>(smem);
 #pragma unroll
   for (int m = 0; m < MT; ++m)
 #pragma unroll
@@ -310,11 +328,11 @@ __global__ __launch_bounds__(NW * 64) void route_bf16_kernel(
 #pragma unroll
     for (int q = 0; q < NT; ++q) {
       const int e = 16 * q + r;
-      float s = part[0][tl][e];
+      float sum = part[0][tl][e];
 #pragma unroll
-      for (int w = 1; w < NW; ++w) s += part[w][tl][e];
-      if (bias && e < E) s += bias[e];
-      v[q] = s;
+      for (int w = 1; w < NW; ++w) sum += part[w][tl][e];
+      if (bias && e < E) sum += bias[e];
+      v[q] = sum;
     }
     select_topk_store<NT>(v, r, E, K, t, t < N, ids, topw, counts ? hist : nullptr);
   }
@@ -382,19 +400,21 @@ __global__ __launch_bounds__(256) void route_f32_kernel(const float* __restrict_
 }
 
 // ------------------------------------------------------- gate re-layout
-// wgt[e][h] = gate_w[h][e] for e < E and 0 for E <= e < EP, rows ldw
-// elements apart (ldw = H + kGatePad: the pad staggers the rows over the
-// memory channels).  Each thread moves one 8(h) x 8(e) block: eight 16-byte
-// loads, a register transpose, eight 16-byte stores; consecutive threads take
-// consecutive h blocks so the stores are contiguous.  Thread 0.. also zero
+// Packs gate_w [H,E] fragment-major for route_bf16_kernel: for step s (64
+// values of h), expert tile q (16 experts) and half hf, a 1 KiB block whose
+// 16 bytes at lane l = 16g + r hold gate[h0 .. h0+8][16q + r] with
+// h0 = 64s + 16g + 8hf -- exactly one MFMA B fragment.  Values with h >= H or
+// e >= E are zero, so the router needs no masking on this operand.
+// Each thread moves one 8(h) x 8(e) block: eight 16-byte row loads, a
+// register transpose, eight 16-byte stores.  Threads 0..E-1 also zero
 // `counts` (the router then adds into it).
-__global__ __launch_bounds__(64) void gate_transpose_kernel(const uint16_t* __restrict__ gate_w,
-                                                            int H, int E, int EP, int ldw,
-                                                            uint16_t* __restrict__ wgt,
-                                                            int32_t* __restrict__ counts) {
+__global__ __launch_bounds__(64) void gate_pack_kernel(const uint16_t* __restrict__ gate_w, int H,
+                                                       int E, int EP, int HP,
+                                                       u32x4* __restrict__ gfrag,
+                                                       int32_t* __restrict__ counts) {
   const int64_t idx = (int64_t)blockIdx.x * 64 + threadIdx.x;
   if (counts && idx < E) counts[idx] = 0;
-  const int nhb = H / 8;
+  const int nhb = HP / 8;  // 8-row blocks of h, including the zero padding up to HP
   if (idx >= (int64_t)nhb * (EP / 8)) return;
   const int eb = (int)(idx / nhb);
   const int hb = (int)(idx - (int64_t)eb * nhb);
@@ -403,10 +423,15 @@ __global__ __launch_bounds__(64) void gate_transpose_kernel(const uint16_t* __re
   const bool vec = (E % 8 == 0) && (e0 + 8 <= E);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const uint16_t* src = gate_w + (int64_t)(h0 + i) * E + e0;
+    const int h = h0 + i;
+    if (h >= H) {
+      v[i][0] = v[i][1] = v[i][2] = v[i][3] = 0u;
+      continue;
+    }
+    const uint16_t* src = gate_w + (int64_t)h * E + e0;
     if (vec) {
-      const uint4 u = *reinterpret_cast<const uint4*>(src);
-      v[i][0] = u.x; v[i][1] = u.y; v[i][2] = u.z; v[i][3] = u.w;
+      const u32x4 u = *reinterpret_cast<const u32x4*>(src);
+      v[i][0] = u[0]; v[i][1] = u[1]; v[i][2] = u[2]; v[i][3] = u[3];
     } else {
       uint16_t t[8];
 #pragma unroll
@@ -415,16 +440,22 @@ __global__ __launch_bounds__(64) void gate_transpose_kernel(const uint16_t* __re
       for (int j = 0; j < 4; ++j) v[i][j] = (uint32_t)t[2 * j] | ((uint32_t)t[2 * j + 1] << 16);
     }
   }
+  const int s = h0 >> 6;
+  const int g = (h0 >> 4) & 3;
+  const int hf = (h0 >> 3) & 1;
+  const int NTL = EP / 16;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {  // expert e0+j: its 8 values of h0..h0+7
-    uint32_t o[4];
+    const int e = e0 + j;
+    u32x4 o;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const uint32_t lo = (v[2 * p][j >> 1] >> (16 * (j & 1))) & 0xffffu;
       const uint32_t hi = (v[2 * p + 1][j >> 1] >> (16 * (j & 1))) & 0xffffu;
       o[p] = lo | (hi << 16);
     }
-    *reinterpret_cast<uint4*>(wgt + (int64_t)(e0 + j) * ldw + h0) = uint4{o[0], o[1], o[2], o[3]};
+    const int q = e >> 4;
+    gfrag[((int64_t)(s * NTL + q) * 2 + hf) * 64 + 16 * g + (e & 15)] = o;
   }
 }
 
@@ -433,13 +464,14 @@ __global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
   if (i < n) p[i] = v;
 }
 
-template <int NT, int MT, int NW = MOE_ROUTE_NW, int D = (NT <= 4 ? MOE_ROUTE_DEPTH : 1)>
+template <int NT, int MT, int NW = (NT <= 4 ? MOE_ROUTE_NW : 4),
+          int D = (NT <= 4 ? MOE_ROUTE_DEPTH : 1)>
 hipError_t launch_bf16_nt(const uint16_t* x, const uint16_t* wgt, const float* bias, int64_t N,
                           int H, int E, int K, int32_t* ids, float* w, int32_t* counts,
                           hipStream_t s) {
   const int64_t blocks = (N + 16 * MT - 1) / (16 * MT);
   hipLaunchKernelGGL((route_bf16_kernel<NT, MT, NW, D>), dim3((unsigned)blocks), dim3(NW * 64), 0,
-                     s, x, wgt, route_gate_stride(H), bias, N, H, E, K, ids, w, counts);
+                     s, x, reinterpret_cast<const u32x4*>(wgt), bias, N, H, E, K, ids, w, counts);
   return hipGetLastError();
 }
 
@@ -467,15 +499,16 @@ hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s) {
   return hipGetLastError();
 }
 
-int route_gate_stride(int H) { return H + kGatePad; }
+int route_gate_rows(int H) { return (H + 63) / 64 * 64; }
 
 hipError_t launch_gate_transpose(const uint16_t* gate_w, int H, int E, uint16_t* wgt,
                                  int32_t* counts, hipStream_t s) {
   const int EP = route_padded_experts(E);
-  int64_t threads = (int64_t)(H / 8) * (EP / 8);
+  const int HP = route_gate_rows(H);
+  int64_t threads = (int64_t)(HP / 8) * (EP / 8);
   if (threads < E) threads = E;
-  hipLaunchKernelGGL(gate_transpose_kernel, dim3((unsigned)((threads + 63) / 64)), dim3(64), 0, s,
-                     gate_w, H, E, EP, route_gate_stride(H), wgt, counts);
+  hipLaunchKernelGGL(gate_pack_kernel, dim3((unsigned)((threads + 63) / 64)), dim3(64), 0, s,
+                     gate_w, H, E, EP, HP, reinterpret_cast<u32x4*>(wgt), counts);
   return hipGetLastError();
 }
 
