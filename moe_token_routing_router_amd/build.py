@@ -13,6 +13,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe.so")
+INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
 
 
@@ -26,7 +27,7 @@ def hipcc() -> str:
 def build(verbose: bool = False) -> str:
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-           "-Wall", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-Wall", "-I", INCLUDE, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
            "-o", LIB + ".tmp"] + srcs
     if verbose:
         print(" ".join(cmd), flush=True)

@@ -1,7 +1,7 @@
 // extern "C" entry points of libmoe.so (declared in include/moe.h).
 // Every argument is checked on the host before anything is enqueued; the
 // launchers in route.hip / dispatch.hip / combine.hip assume valid input.
-#include "../../include/moe.h"
+#include "moe.h"
 #include "moe_internal.h"
 
 namespace {

@@ -29,6 +29,9 @@
 #ifndef MOE_ROUTE_NW
 #define MOE_ROUTE_NW 8       // waves per workgroup, splitting H (E <= 64)
 #endif
+#ifndef MOE_ROUTE_NW128
+#define MOE_ROUTE_NW128 4    // ... for 64 < E <= 128
+#endif
 #ifndef MOE_ROUTE_MT64
 #define MOE_ROUTE_MT64 4     // 16-token M-tiles per workgroup for E <= 64
 #endif
@@ -50,56 +53,112 @@ constexpr int kSentinel = 0x7fffffff;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// K rounds of arg-max over one token's logits held by a 16-lane group, then
-// w_k = exp(l_k - l_0) / sum_j exp(l_j - l_0) for the K picks.  Lane r keeps
-// round r's pick and writes ids[t*K + r], w[t*K + r].
-// v[q] is the logit of expert 16*q + r (already biased); experts >= E are
-// never candidates.
-template <int NT>
-__device__ __forceinline__ void select_topk_store(const float (&v)[NT], int r, int E, int K,
-                                                  int64_t t, bool valid, int32_t* __restrict__ ids,
+// Data movement inside a 16-lane row with DPP (a modifier on a VALU move, no
+// LDS round trip).  quad_perm(1,0,3,2) and quad_perm(2,3,0,1) exchange lanes
+// l^1 and l^2; row_half_mirror maps lane i to 7-i inside each half-row and
+// row_mirror maps i to 15-i.  Combining a value with its image under these
+// four, in that order, leaves every lane of the row with the combination of
+// all 16 lanes.
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(dpp_i<CTRL>(__float_as_int(v)));
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm(1,0,3,2)
+constexpr int kDppXor2 = 0x4E;        // quad_perm(2,3,0,1)
+constexpr int kDppHalfMirror = 0x141;  // row_half_mirror
+constexpr int kDppMirror = 0x140;      // row_mirror
+
+// (value, index) arg-max step: larger value wins, equal values go to the
+// lower index.  Symmetric, so the order of the partners does not matter.
+// Written with bitwise operators and selects: short-circuit conditions here
+// compile to divergent branches.
+template <int CTRL>
+__device__ __forceinline__ void argmax_step(float& bv, int& bi) {
+  const float ov = dpp_f<CTRL>(bv);
+  const int oi = dpp_i<CTRL>(bi);
+  const bool take = (ov > bv) | ((ov == bv) & (oi < bi));
+  bv = take ? ov : bv;
+  bi = take ? oi : bi;
+}
+
+__device__ __forceinline__ float sum16(float v) {
+  v += dpp_f<kDppXor1>(v);
+  v += dpp_f<kDppXor2>(v);
+  v += dpp_f<kDppHalfMirror>(v);
+  v += dpp_f<kDppMirror>(v);
+  return v;
+}
+
+// K rounds of arg-max over the logits of U tokens, each held by this 16-lane
+// group, then w_k = exp(l_k - l_0) / sum_j exp(l_j - l_0) for the K picks.
+// The U selections are independent and advance together, so their
+// dependency chains interleave.  Lane r keeps round r's pick of token u and
+// writes ids[t_u*K + r], w[t_u*K + r].
+// v[u][q] is the logit of expert 16*q + r for token t[u] (already biased);
+// experts >= E are never candidates.
+template <int NT, int U>
+__device__ __forceinline__ void select_topk_store(const float (&v)[U][NT], int r, int E, int K,
+                                                  const int64_t (&t)[U], int64_t N,
+                                                  int32_t* __restrict__ ids,
                                                   float* __restrict__ topw, int* hist) {
-  uint32_t taken = 0;
-  float my_val = 0.f, top = 0.f;
-  int my_id = 0;
-  for (int k = 0; k < K; ++k) {
-    float bv = -__builtin_inff();
-    int bi = kSentinel;
+  uint32_t taken[U];
+  float my_val[U], top[U];
+  int my_id[U];
 #pragma unroll
-    for (int q = 0; q < NT; ++q) {
-      const int e = 16 * q + r;
-      const bool cand = (e < E) && !((taken >> q) & 1u);
-      // experts are visited in ascending index: strict '>' keeps the lower
-      // index on ties; the first candidate always replaces the sentinel
-      if (cand && (bi == kSentinel || v[q] > bv)) {
-        bv = v[q];
-        bi = e;
-      }
-    }
-#pragma unroll
-    for (int off = 8; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off, 16);
-      const int oi = __shfl_xor(bi, off, 16);
-      if (ov > bv || (ov == bv && oi < bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
-    if (k == 0) top = bv;
-    if (r == k) {
-      my_val = bv;
-      my_id = bi;
-    }
-    if ((bi & 15) == r) taken |= 1u << (bi >> 4);
+  for (int u = 0; u < U; ++u) {
+    taken[u] = 0u;
+    my_val[u] = 0.f;
+    top[u] = 0.f;
+    my_id[u] = 0;
   }
-  float ex = (r < K) ? expf(my_val - top) : 0.f;
-  float sum = ex;
+  for (int k = 0; k < K; ++k) {
+    float bv[U];
+    int bi[U];
 #pragma unroll
-  for (int off = 8; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 16);
-  if (valid && r < K) {
-    ids[t * K + r] = my_id;
-    topw[t * K + r] = ex / sum;
-    if (hist) atomicAdd(&hist[my_id], 1);
+    for (int u = 0; u < U; ++u) {
+      bv[u] = -__builtin_inff();
+      bi[u] = kSentinel;
+#pragma unroll
+      for (int q = 0; q < NT; ++q) {
+        const int e = 16 * q + r;
+        const bool cand = (e < E) & (((taken[u] >> q) & 1u) == 0u);
+        // experts are visited in ascending index: strict '>' keeps the lower
+        // index on ties; the first candidate always replaces the sentinel
+        const bool better = cand & ((bi[u] == kSentinel) | (v[u][q] > bv[u]));
+        bv[u] = better ? v[u][q] : bv[u];
+        bi[u] = better ? e : bi[u];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) argmax_step<kDppXor1>(bv[u], bi[u]);
+#pragma unroll
+    for (int u = 0; u < U; ++u) argmax_step<kDppXor2>(bv[u], bi[u]);
+#pragma unroll
+    for (int u = 0; u < U; ++u) argmax_step<kDppHalfMirror>(bv[u], bi[u]);
+#pragma unroll
+    for (int u = 0; u < U; ++u) argmax_step<kDppMirror>(bv[u], bi[u]);
+    const bool mine = (r == k);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      top[u] = (k == 0) ? bv[u] : top[u];
+      my_val[u] = mine ? bv[u] : my_val[u];
+      my_id[u] = mine ? bi[u] : my_id[u];
+      taken[u] |= ((bi[u] & 15) == r) ? (1u << ((bi[u] >> 4) & 31)) : 0u;
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const float ex = (r < K) ? expf(my_val[u] - top[u]) : 0.f;
+    const float sum = sum16(ex);
+    if ((t[u] < N) & (r < K)) {
+      ids[t[u] * K + r] = my_id[u];
+      topw[t[u] * K + r] = ex / sum;
+      if (hist) atomicAdd(&hist[my_id[u]], 1);
+    }
   }
 }
 
@@ -322,20 +381,25 @@ __global__ __launch_bounds__(NW * 64) void route_bf16_kernel(
       for (int i = 0; i < 4; ++i) part[wid][16 * m + 4 * g + i][16 * q + r] = acc[m][q][i];
   __syncthreads();
 
-  for (int tl = wid * 4 + g; tl < BM; tl += NW * 4) {
-    const int64_t t = t0 + tl;
-    float v[NT];
+  // each 16-lane group selects for the U tokens tl = wid*4 + g + u*NW*4
+  constexpr int U = BM / (4 * NW);
+  float v[U][NT];
+  int64_t tt[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int tl = wid * 4 + g + u * NW * 4;
+    tt[u] = t0 + tl;
 #pragma unroll
     for (int q = 0; q < NT; ++q) {
       const int e = 16 * q + r;
       float sum = part[0][tl][e];
 #pragma unroll
       for (int w = 1; w < NW; ++w) sum += part[w][tl][e];
-      if (bias && e < E) sum += bias[e];
-      v[q] = sum;
+      if (bias) sum += bias[e < E ? e : 0];  // e >= E is never a candidate
+      v[u][q] = sum;
     }
-    select_topk_store<NT>(v, r, E, K, t, t < N, ids, topw, counts ? hist : nullptr);
   }
+  select_topk_store<NT, U>(v, r, E, K, tt, N, ids, topw, counts ? hist : nullptr);
 
   if (counts) {
     __syncthreads();
@@ -386,12 +450,18 @@ __global__ __launch_bounds__(256) void route_f32_kernel(const float* __restrict_
       }
     }
   }
+  if (bias) {
 #pragma unroll
-  for (int q = 0; q < NT; ++q) {
-    const int e = 16 * q + r;
-    if (bias && e < E) acc[q] += bias[e];
+    for (int q = 0; q < NT; ++q) {
+      const int e = 16 * q + r;
+      acc[q] += bias[e < E ? e : 0];  // e >= E is never a candidate
+    }
   }
-  select_topk_store<NT>(acc, r, E, K, t, t < N, ids, topw, counts ? hist : nullptr);
+  float v1[1][NT];
+#pragma unroll
+  for (int q = 0; q < NT; ++q) v1[0][q] = acc[q];
+  const int64_t t1[1] = {t};
+  select_topk_store<NT, 1>(v1, r, E, K, t1, N, ids, topw, counts ? hist : nullptr);
   if (counts) {
     __syncthreads();
     for (int e = tid; e < E; e += 256)
@@ -464,7 +534,7 @@ __global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
   if (i < n) p[i] = v;
 }
 
-template <int NT, int MT, int NW = (NT <= 4 ? MOE_ROUTE_NW : 4),
+template <int NT, int MT, int NW = (NT <= 4 ? MOE_ROUTE_NW : NT == 8 ? MOE_ROUTE_NW128 : 4),
           int D = (NT <= 4 ? MOE_ROUTE_DEPTH : 1)>
 hipError_t launch_bf16_nt(const uint16_t* x, const uint16_t* wgt, const float* bias, int64_t N,
                           int H, int E, int K, int32_t* ids, float* w, int32_t* counts,
