@@ -125,6 +125,33 @@ moe_status_t moe_dispatch(const int32_t *topk_ids, const void *x, int64_t N,
                           size_t workspace_bytes, void *stream);
 
 /*
+ * Bytes of device workspace moe_route_dispatch needs for (N, H, E, K, dtype).
+ */
+size_t moe_route_dispatch_workspace_size(int64_t N, int32_t H, int32_t E, int32_t K,
+                                         moe_dtype_t dtype);
+
+/*
+ * moe_route_dispatch -- moe_route followed by moe_dispatch of its ids, in
+ * fewer launches: the router's own epilogue produces the per-block counts
+ * and the stable in-block ranks the dispatch needs ([R]'s fused router feeds
+ * [D]'s counting sort directly; the per-expert dispatch counts of [R]'s token
+ * conservation check are `counts`).  Outputs are exactly those of the two
+ * calls made in sequence (moe_route without its counts, then moe_dispatch):
+ * topk_ids, topk_w [N,K]; counts [E]; offsets [E+1]; perm, inv [N*K];
+ * x_perm [N*K,H] (or NULL for the index arrays only).  Limits and
+ * preconditions are the union of the two calls' (notably K <= 16).
+ *   workspace >= moe_route_dispatch_workspace_size(N, H, E, K, dtype) bytes;
+ *              scratch
+ * N == 0 is a valid call: counts and offsets are zero-filled.
+ */
+moe_status_t moe_route_dispatch(const void *x, const void *gate_w, const float *bias,
+                                int64_t N, int32_t H, int32_t E, int32_t K,
+                                moe_dtype_t dtype, int32_t *topk_ids, float *topk_w,
+                                int32_t *counts, int32_t *offsets, int32_t *perm,
+                                int32_t *inv, void *x_perm, void *workspace,
+                                size_t workspace_bytes, void *stream);
+
+/*
  * moe_combine -- the weighted combine of [A] (forward_aggregate without the
  * residual): un-permutes the expert outputs and sums them per token
  *   out[n,:] = sum_{k=0..K-1} topk_w[n,k] * y[inv[n*K+k], :]

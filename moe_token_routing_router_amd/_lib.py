@@ -26,7 +26,8 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARGUMENT", 2: "MOE_ERR_UNSUPPORTED",
           3: "MOE_ERR_MISALIGNED", 4: "MOE_ERR_WORKSPACE_TOO_SMALL", 5: "MOE_ERR_HIP"}
 
 EXPORTS = ("moe_status_string", "moe_route_workspace_size", "moe_route",
-           "moe_dispatch_workspace_size", "moe_dispatch", "moe_combine")
+           "moe_dispatch_workspace_size", "moe_dispatch", "moe_route_dispatch_workspace_size",
+           "moe_route_dispatch", "moe_combine")
 
 
 class MoeError(RuntimeError):
@@ -59,6 +60,11 @@ def library() -> ctypes.CDLL:
         lib.moe_dispatch.argtypes = [P, P, i64, i32, i32, i32, ctypes.c_int, P, P, P, P, P, P,
                                      sz, P]
         lib.moe_dispatch.restype = ctypes.c_int
+        lib.moe_route_dispatch_workspace_size.argtypes = [i64, i32, i32, i32, ctypes.c_int]
+        lib.moe_route_dispatch_workspace_size.restype = sz
+        lib.moe_route_dispatch.argtypes = [P, P, P, i64, i32, i32, i32, ctypes.c_int, P, P, P, P,
+                                           P, P, P, P, sz, P]
+        lib.moe_route_dispatch.restype = ctypes.c_int
         lib.moe_combine.argtypes = [P, P, P, i64, i32, i32, ctypes.c_int, P, P]
         lib.moe_combine.restype = ctypes.c_int
         _lib = lib
@@ -111,6 +117,10 @@ def moe_route_workspace_size(H: int, E: int, dtype: torch.dtype) -> int:
 
 def moe_dispatch_workspace_size(N: int, E: int, K: int) -> int:
     return int(library().moe_dispatch_workspace_size(N, E, K))
+
+
+def moe_route_dispatch_workspace_size(N: int, H: int, E: int, K: int, dtype: torch.dtype) -> int:
+    return int(library().moe_route_dispatch_workspace_size(N, H, E, K, _dtype_code(dtype)))
 
 
 # ------------------------------------------------------------------ calls
@@ -168,6 +178,30 @@ def moe_dispatch(topk_ids: torch.Tensor, x: Optional[torch.Tensor], E: int,
         _stream(dev)))
 
 
+def moe_route_dispatch(x: torch.Tensor, gate_w: torch.Tensor, bias: Optional[torch.Tensor],
+                       K: int, topk_ids: torch.Tensor, topk_w: torch.Tensor,
+                       counts: torch.Tensor, offsets: torch.Tensor, perm: torch.Tensor,
+                       inv: torch.Tensor, x_perm: Optional[torch.Tensor],
+                       workspace: torch.Tensor) -> None:
+    """moe_route then moe_dispatch of its ids, fused (see include/moe.h)."""
+    N, H = x.shape
+    E = gate_w.shape[1]
+    if gate_w.shape[0] != H:
+        raise ValueError("gate_w must be [H, E]")
+    dev = x.device
+    _check("moe_route_dispatch", library().moe_route_dispatch(
+        _dev(x, "x", x.dtype, N * H, dev), _dev(gate_w, "gate_w", x.dtype, H * E, dev),
+        _dev(bias, "bias", torch.float32, E, dev), N, H, E, K, _dtype_code(x.dtype),
+        _dev(topk_ids, "topk_ids", torch.int32, N * K, dev),
+        _dev(topk_w, "topk_w", torch.float32, N * K, dev),
+        _dev(counts, "counts", torch.int32, E, dev),
+        _dev(offsets, "offsets", torch.int32, E + 1, dev),
+        _dev(perm, "perm", torch.int32, N * K, dev), _dev(inv, "inv", torch.int32, N * K, dev),
+        _dev(x_perm, "x_perm", x.dtype, N * K * H, dev),
+        _dev(workspace, "workspace", torch.uint8, workspace.numel(), dev), workspace.numel(),
+        _stream(dev)))
+
+
 def moe_combine(y: torch.Tensor, inv: torch.Tensor, topk_w: torch.Tensor,
                 out: torch.Tensor) -> None:
     """Weighted combine: out [N,H] = sum_k topk_w[n,k] * y[inv[n*K+k]], with
@@ -213,6 +247,26 @@ def dispatch(topk_ids: torch.Tensor, x: Optional[torch.Tensor], E: int, with_row
     moe_dispatch(topk_ids, x, E, counts, offsets, perm, inv, x_perm, ws,
                  H=None if x is not None else 8, dtype=None if x is not None else torch.bfloat16)
     return counts, offsets, perm, inv, x_perm
+
+
+def route_dispatch(x: torch.Tensor, gate_w: torch.Tensor, K: int,
+                   bias: Optional[torch.Tensor] = None, with_rows: bool = True):
+    """Allocate outputs and run moe_route_dispatch; returns
+    (ids, w, counts, offsets, perm, inv, x_perm-or-None)."""
+    N, H = x.shape
+    E = gate_w.shape[1]
+    dev = x.device
+    ids = torch.empty((N, K), dtype=torch.int32, device=dev)
+    w = torch.empty((N, K), dtype=torch.float32, device=dev)
+    counts = torch.empty((E,), dtype=torch.int32, device=dev)
+    offsets = torch.empty((E + 1,), dtype=torch.int32, device=dev)
+    perm = torch.empty((N * K,), dtype=torch.int32, device=dev)
+    inv = torch.empty((N * K,), dtype=torch.int32, device=dev)
+    x_perm = torch.empty((N * K, H), dtype=x.dtype, device=dev) if with_rows else None
+    ws = torch.empty((max(1, moe_route_dispatch_workspace_size(N, H, E, K, x.dtype)),),
+                     dtype=torch.uint8, device=dev)
+    moe_route_dispatch(x, gate_w, bias, K, ids, w, counts, offsets, perm, inv, x_perm, ws)
+    return ids, w, counts, offsets, perm, inv, x_perm
 
 
 def combine(y: torch.Tensor, inv: torch.Tensor, topk_w: torch.Tensor) -> torch.Tensor:

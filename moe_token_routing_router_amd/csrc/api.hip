@@ -67,7 +67,7 @@ moe_status_t moe_route(const void* x, const void* gate_w, const float* bias, int
                                               counts, s);
     if (e != hipSuccess) return MOE_ERR_HIP;
     return from_hip(moe::launch_route_bf16(reinterpret_cast<const uint16_t*>(x), wgt, bias, N, H,
-                                           E, K, topk_ids, topk_w, counts, s));
+                                           E, K, topk_ids, topk_w, counts, nullptr, nullptr, s));
   }
   if (counts) {
     hipError_t e = moe::launch_fill_i32(counts, E, 0, s);
@@ -78,10 +78,41 @@ moe_status_t moe_route(const void* x, const void* gate_w, const float* bias, int
                                         topk_ids, topk_w, counts, s));
 }
 
+namespace {
+
+// dispatch scratch: bhist [E][blocks of bt tokens] then lrank [N*K]
+size_t dispatch_scratch_bytes(int64_t N, int32_t E, int32_t K, int bt) {
+  const int64_t nb = moe::dispatch_num_blocks(N, bt);
+  return round_up((size_t)nb * (size_t)E * sizeof(int32_t), 256) +
+         round_up((size_t)N * (size_t)K * sizeof(int32_t), 256);
+}
+
+moe_status_t check_dispatch_outputs(int64_t N, int32_t H, int32_t E, int32_t K,
+                                    moe_dtype_t dtype, const void* x, const int32_t* counts,
+                                    const int32_t* offsets, const int32_t* perm,
+                                    const int32_t* inv, const void* x_perm) {
+  if (!counts || !offsets) return MOE_ERR_INVALID_ARGUMENT;
+  if (N > 0 && (!perm || !inv)) return MOE_ERR_INVALID_ARGUMENT;
+  if (N > 0 && x_perm && !x) return MOE_ERR_INVALID_ARGUMENT;
+  if (E > moe::kMaxExperts || N * (int64_t)K >= kMaxSlots || !row_ok(H, dtype))
+    return MOE_ERR_UNSUPPORTED;
+  if (!aligned(counts, 4) || !aligned(offsets, 4) || !aligned(perm, 4) || !aligned(inv, 4) ||
+      !aligned(x, 16) || !aligned(x_perm, 16))
+    return MOE_ERR_MISALIGNED;
+  return MOE_OK;
+}
+
+moe_status_t zero_counts_offsets(int32_t* counts, int32_t* offsets, int32_t E, hipStream_t s) {
+  hipError_t e = moe::launch_fill_i32(counts, E, 0, s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  return from_hip(moe::launch_fill_i32(offsets, (int64_t)E + 1, 0, s));
+}
+
+}  // namespace
+
 size_t moe_dispatch_workspace_size(int64_t N, int32_t E, int32_t K) {
   if (N < 0 || E <= 0 || E > moe::kMaxExperts || K < 1) return 0;
-  const int64_t num_sub = moe::dispatch_num_sub(N);
-  return round_up((size_t)num_sub * (size_t)E * sizeof(int32_t), 256) + 256;
+  return dispatch_scratch_bytes(N, E, K, moe::dispatch_count_tokens(K));
 }
 
 moe_status_t moe_dispatch(const int32_t* topk_ids, const void* x, int64_t N, int32_t H, int32_t E,
@@ -90,24 +121,78 @@ moe_status_t moe_dispatch(const int32_t* topk_ids, const void* x, int64_t N, int
                           size_t workspace_bytes, void* stream) {
   if (!valid_dtype(dtype) || N < 0 || H <= 0 || E <= 0 || K < 1 || K > E)
     return MOE_ERR_INVALID_ARGUMENT;
-  if (!counts || !offsets) return MOE_ERR_INVALID_ARGUMENT;
-  if (N > 0 && (!topk_ids || !perm || !inv || !workspace)) return MOE_ERR_INVALID_ARGUMENT;
-  if (N > 0 && x_perm && !x) return MOE_ERR_INVALID_ARGUMENT;
-  if (E > moe::kMaxExperts || N * (int64_t)K >= kMaxSlots || !row_ok(H, dtype))
-    return MOE_ERR_UNSUPPORTED;
-  if (!aligned(topk_ids, 4) || !aligned(counts, 4) || !aligned(offsets, 4) || !aligned(perm, 4) ||
-      !aligned(inv, 4) || !aligned(x, 16) || !aligned(x_perm, 16) || !aligned(workspace, 16))
+  if (N > 0 && (!topk_ids || !workspace)) return MOE_ERR_INVALID_ARGUMENT;
+  moe_status_t st = check_dispatch_outputs(N, H, E, K, dtype, x, counts, offsets, perm, inv, x_perm);
+  if (st != MOE_OK) return st;
+  if (!aligned(topk_ids, 4) || !aligned(workspace, 16)) return MOE_ERR_MISALIGNED;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (N == 0) return zero_counts_offsets(counts, offsets, E, s);
+  if (workspace_bytes < moe_dispatch_workspace_size(N, E, K)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  const int bt = moe::dispatch_count_tokens(K);
+  int32_t* bhist = reinterpret_cast<int32_t*>(workspace);
+  int32_t* lrank = reinterpret_cast<int32_t*>(
+      reinterpret_cast<char*>(workspace) +
+      round_up((size_t)moe::dispatch_num_blocks(N, bt) * E * sizeof(int32_t), 256));
+  hipError_t e = moe::launch_dispatch_count(topk_ids, N, E, K, lrank, bhist, s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  return from_hip(moe::launch_dispatch_finish(topk_ids, x, N, (int64_t)H * elem_bytes(dtype), E, K,
+                                              bt, counts, offsets, perm, inv, x_perm, lrank,
+                                              bhist, s));
+}
+
+size_t moe_route_dispatch_workspace_size(int64_t N, int32_t H, int32_t E, int32_t K,
+                                         moe_dtype_t dtype) {
+  if (N < 0 || H <= 0 || E <= 0 || E > moe::kMaxExperts || K < 1 || !valid_dtype(dtype)) return 0;
+  const int bt =
+      dtype == MOE_BF16 ? moe::route_tokens_per_block(E) : moe::dispatch_count_tokens(K);
+  return moe_route_workspace_size(H, E, dtype) + dispatch_scratch_bytes(N, E, K, bt);
+}
+
+moe_status_t moe_route_dispatch(const void* x, const void* gate_w, const float* bias, int64_t N,
+                                int32_t H, int32_t E, int32_t K, moe_dtype_t dtype,
+                                int32_t* topk_ids, float* topk_w, int32_t* counts,
+                                int32_t* offsets, int32_t* perm, int32_t* inv, void* x_perm,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  if (!valid_dtype(dtype) || N < 0 || H <= 0 || E <= 0 || K < 1 || K > E)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (N > 0 && (!x || !gate_w || !topk_ids || !topk_w || !workspace))
+    return MOE_ERR_INVALID_ARGUMENT;
+  moe_status_t st = check_dispatch_outputs(N, H, E, K, dtype, x, counts, offsets, perm, inv, x_perm);
+  if (st != MOE_OK) return st;
+  if (K > moe::kMaxRouteK) return MOE_ERR_UNSUPPORTED;
+  if (!aligned(gate_w, 16) || !aligned(bias, 4) || !aligned(topk_ids, 4) ||
+      !aligned(topk_w, 4) || !aligned(workspace, 16))
     return MOE_ERR_MISALIGNED;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (N == 0) {
-    hipError_t e = moe::launch_fill_i32(counts, E, 0, s);
+  if (N == 0) return zero_counts_offsets(counts, offsets, E, s);
+  if (workspace_bytes < moe_route_dispatch_workspace_size(N, H, E, K, dtype))
+    return MOE_ERR_WORKSPACE_TOO_SMALL;
+  const size_t rws = moe_route_workspace_size(H, E, dtype);
+  const int bt =
+      dtype == MOE_BF16 ? moe::route_tokens_per_block(E) : moe::dispatch_count_tokens(K);
+  char* base = reinterpret_cast<char*>(workspace);
+  int32_t* bhist = reinterpret_cast<int32_t*>(base + rws);
+  int32_t* lrank = reinterpret_cast<int32_t*>(
+      base + rws + round_up((size_t)moe::dispatch_num_blocks(N, bt) * E * sizeof(int32_t), 256));
+  hipError_t e;
+  if (dtype == MOE_BF16) {
+    uint16_t* wgt = reinterpret_cast<uint16_t*>(workspace);
+    e = moe::launch_gate_transpose(reinterpret_cast<const uint16_t*>(gate_w), H, E, wgt, nullptr,
+                                   s);
     if (e != hipSuccess) return MOE_ERR_HIP;
-    return from_hip(moe::launch_fill_i32(offsets, (int64_t)E + 1, 0, s));
+    e = moe::launch_route_bf16(reinterpret_cast<const uint16_t*>(x), wgt, bias, N, H, E, K,
+                               topk_ids, topk_w, nullptr, lrank, bhist, s);
+  } else {
+    e = moe::launch_route_f32(reinterpret_cast<const float*>(x),
+                              reinterpret_cast<const float*>(gate_w), bias, N, H, E, K, topk_ids,
+                              topk_w, nullptr, s);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    e = moe::launch_dispatch_count(topk_ids, N, E, K, lrank, bhist, s);
   }
-  if (workspace_bytes < moe_dispatch_workspace_size(N, E, K)) return MOE_ERR_WORKSPACE_TOO_SMALL;
-  return from_hip(moe::launch_dispatch(topk_ids, x, N, (int64_t)H * elem_bytes(dtype), E, K,
-                                       counts, offsets, perm, inv, x_perm,
-                                       reinterpret_cast<int32_t*>(workspace), s));
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  return from_hip(moe::launch_dispatch_finish(topk_ids, x, N, (int64_t)H * elem_bytes(dtype), E, K,
+                                              bt, counts, offsets, perm, inv, x_perm, lrank,
+                                              bhist, s));
 }
 
 moe_status_t moe_combine(const void* y, const int32_t* inv, const float* topk_w, int64_t N,

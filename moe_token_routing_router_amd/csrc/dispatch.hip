@@ -9,15 +9,20 @@
 // argsort / nonzero / searchsorted / repeat_interleave launches with fixed-size
 // outputs.  This build keeps that three-kernel shape, on CDNA4:
 //
-//  hist  (grid = #sub-chunks, 1 wave each)  LDS-atomic histogram of the ids of
-//        one sub-chunk of kDispatchTokens tokens -> blockcnt[e][sub]
-//  scan  (grid = E, 256 threads)            exclusive scan of blockcnt[e][:]
-//        across sub-chunks, in place; counts[e] = total
-//  scatter (grid = #sub-chunks, 256 thr.)   offsets = exclusive scan of counts
-//        (each block redoes this E-wide scan in LDS; block 0 stores it);
-//        stable rank of every slot inside its sub-chunk; inv/perm; then the
-//        block copies its tokens' rows, each row read once with 16-byte loads
-//        and written K times with 16-byte stores.
+//  count   (one workgroup per block of bt tokens)  stable rank of every slot
+//          among the equal ids of its block (wave ballots on the id bits, then
+//          per-wave counts in LDS), and the block's per-expert histogram
+//          -> lrank[slot], bhist[e][block]
+//  scan    (one workgroup per expert)  exclusive scan of bhist[e][:] across
+//          blocks, in place; counts[e] = total
+//  scatter (one workgroup per token)  offsets = exclusive scan of counts (each
+//          workgroup redoes this E-wide scan in LDS; workgroup 0 stores it);
+//          inv[slot] = offsets[e] + bhist[e][block] + lrank[slot]; perm; then
+//          the token's row is read once with 16-byte loads (issued before the
+//          index work) and written to its K rows with 16-byte stores.
+//
+// The fused router (route.hip) produces lrank and bhist in its own epilogue,
+// so moe_route_dispatch skips the count kernel.
 //
 // Atomics only ever produce counts; every position comes from a deterministic
 // rank, so the output is bitwise reproducible and equal to a stable argsort.
@@ -26,14 +31,14 @@
 #include "moe_internal.h"
 
 // Tuning knobs (compile-time; the defaults are the measured best on MI355X).
-#ifndef MOE_SCATTER_U
-#define MOE_SCATTER_U 4        // row vectors loaded per lane before their stores
-#endif
 #ifndef MOE_SCATTER_NT_LOAD
 #define MOE_SCATTER_NT_LOAD 1  // non-temporal loads of x
 #endif
 #ifndef MOE_SCATTER_NT_STORE
 #define MOE_SCATTER_NT_STORE 1 // non-temporal stores of x_perm (keeps them out of L2/MALL)
+#endif
+#ifndef MOE_SCATTER_TOKENS
+#define MOE_SCATTER_TOKENS 1   // tokens per scatter workgroup
 #endif
 
 namespace moe {
@@ -41,6 +46,8 @@ namespace moe {
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kScatterTokens = MOE_SCATTER_TOKENS;
 
 __device__ __forceinline__ u32x4 ld_row(const u32x4* p) {
 #if MOE_SCATTER_NT_LOAD
@@ -83,33 +90,31 @@ __device__ __forceinline__ int block_exclusive_scan_256(int v, int* lds, int* to
   return wbase + incl - v;
 }
 
-__global__ __launch_bounds__(64) void dispatch_hist_kernel(const int32_t* __restrict__ ids,
-                                                           int64_t T, int K, int E, int num_sub,
-                                                           int32_t* __restrict__ blockcnt) {
-  __shared__ int h[kMaxExperts];
+__global__ __launch_bounds__(256) void dispatch_count_kernel(const int32_t* __restrict__ ids,
+                                                             int64_t N, int K, int E, int bt,
+                                                             int nb, int32_t* __restrict__ lrank,
+                                                             int32_t* __restrict__ bhist) {
+  extern __shared__ int sids[];  // [bt*K]
+  __shared__ int hist[kMaxExperts];
+  __shared__ int wcnt[4 * kMaxExperts];
   const int tid = threadIdx.x;
-  const int sub = blockIdx.x;
-  for (int e = tid; e < E; e += 64) h[e] = 0;
-  __syncthreads();
-  const int64_t s0 = (int64_t)sub * kDispatchTokens * K;
-  int64_t s1 = s0 + (int64_t)kDispatchTokens * K;
-  if (s1 > T) s1 = T;
-  for (int64_t s = s0 + tid; s < s1; s += 64) {
-    const int e = ids[s];
-    if ((unsigned)e < (unsigned)E) atomicAdd(&h[e], 1);
-  }
-  __syncthreads();
-  for (int e = tid; e < E; e += 64) blockcnt[(int64_t)e * num_sub + sub] = h[e];
+  const int64_t n0 = (int64_t)blockIdx.x * bt;
+  const int ntok = (int)min((int64_t)bt, N - n0);
+  const int S = ntok * K;
+  const int64_t s0 = n0 * K;
+  for (int j = tid; j < S; j += 256) sids[j] = ids[s0 + j];
+  block_stable_rank<4>(sids, S, E, lrank + s0, hist, wcnt);
+  for (int e = tid; e < E; e += 256) bhist[(int64_t)e * nb + blockIdx.x] = hist[e];
 }
 
-__global__ __launch_bounds__(256) void dispatch_scan_kernel(int32_t* __restrict__ blockcnt,
-                                                            int num_sub,
+__global__ __launch_bounds__(256) void dispatch_scan_kernel(int32_t* __restrict__ bhist,
+                                                            int nb,
                                                             int32_t* __restrict__ counts) {
   __shared__ int lds[4];
-  int32_t* row = blockcnt + (int64_t)blockIdx.x * num_sub;
-  const int per = (num_sub + 255) / 256;
+  int32_t* row = bhist + (int64_t)blockIdx.x * nb;
+  const int per = (nb + 255) / 256;
   const int b0 = threadIdx.x * per;
-  const int b1 = min(num_sub, b0 + per);
+  const int b1 = min(nb, b0 + per);
   int local = 0;
   for (int b = b0; b < b1; ++b) local += row[b];
   int total;
@@ -122,69 +127,79 @@ __global__ __launch_bounds__(256) void dispatch_scan_kernel(int32_t* __restrict_
   if (threadIdx.x == 0) counts[blockIdx.x] = total;
 }
 
+// One workgroup per kScatterTokens tokens.  The rows' first loads are issued
+// before the index work (they do not depend on it), so the E-wide offset
+// scan and the index arithmetic overlap them.
 __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
     const int32_t* __restrict__ ids, const int32_t* __restrict__ counts,
-    const int32_t* __restrict__ blockcnt, int64_t N, int K, int E, int num_sub,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv,
-    const u32x4* __restrict__ x, u32x4* __restrict__ x_perm, int row_vecs) {
-  extern __shared__ int dyn[];  // sid[S] then dst[S], S = kDispatchTokens*K
+    const int32_t* __restrict__ bhist, const int32_t* __restrict__ lrank, int64_t N, int K,
+    int E, int nb, int bt, int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
+    int32_t* __restrict__ inv, const u32x4* __restrict__ x, u32x4* __restrict__ x_perm,
+    int row_vecs) {
+  extern __shared__ int dst[];  // [kScatterTokens*K]
   __shared__ int off[kMaxExperts];
   __shared__ int scan_lds[4];
   const int tid = threadIdx.x;
-  const int sub = blockIdx.x;
+  const int64_t n0 = (int64_t)blockIdx.x * kScatterTokens;
+  const int ntok = (int)min((int64_t)kScatterTokens, N - n0);
+  const int64_t T = N * K;
+
+  constexpr int U = 4;
+  const int total = ntok * row_vecs;
+  const u32x4* xs = x + n0 * (int64_t)row_vecs;
+  u32x4 v[U];
+  if (x_perm != nullptr) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int idx = min(tid + u * 256, total - 1);
+      v[u] = ld_row(xs + idx);
+    }
+  }
 
   // offsets = exclusive scan of counts (E <= 256: one expert per thread)
   {
     const int c = tid < E ? counts[tid] : 0;
-    int total;
-    const int ex = block_exclusive_scan_256(c, scan_lds, &total);
+    int tot;
+    const int ex = block_exclusive_scan_256(c, scan_lds, &tot);
     if (tid < E) off[tid] = ex;
-    if (sub == 0) {
+    if (blockIdx.x == 0) {
       if (tid < E) offsets[tid] = ex;
-      if (tid == 0) offsets[E] = total;
+      if (tid == 0) offsets[E] = tot;
     }
   }
+  __syncthreads();
 
-  const int64_t n0 = (int64_t)sub * kDispatchTokens;
-  const int ntok = (int)min((int64_t)kDispatchTokens, N - n0);
   const int S = ntok * K;
   const int64_t s0 = n0 * K;
-  int* sid = dyn;
-  int* dst = dyn + kDispatchTokens * K;
-  for (int j = tid; j < S; j += 256) sid[j] = ids[s0 + j];
-  __syncthreads();  // also publishes off[]
-
-  // stable rank inside the sub-chunk: earlier slots with the same expert
   for (int j = tid; j < S; j += 256) {
-    const int e = sid[j];
+    const int64_t slot = s0 + j;
+    const int e = ids[slot];
     int d = -1;
     if ((unsigned)e < (unsigned)E) {
-      int rank = 0;
-      for (int q = 0; q < j; ++q) rank += (sid[q] == e);
-      d = off[e] + blockcnt[(int64_t)e * num_sub + sub] + rank;
-      perm[d] = (int32_t)(s0 + j);
+      const int64_t b = (slot / K) / bt;
+      const int64_t dd = (int64_t)off[e] + bhist[(int64_t)e * nb + b] + lrank[slot];
+      if (dd >= 0 && dd < T) {  // always true for consistent inputs
+        d = (int)dd;
+        perm[d] = (int32_t)slot;
+      }
     }
-    inv[s0 + j] = d;
+    inv[slot] = d;
     dst[j] = d;
   }
   if (x_perm == nullptr) return;
   __syncthreads();
 
-  // copy: flat index over (token, 16-byte column); each row is read once and
-  // stored to its K dispatched rows.  U loads are issued before their stores.
-  constexpr int U = MOE_SCATTER_U;
-  const int total = ntok * row_vecs;
-  const u32x4* xs = x + n0 * (int64_t)row_vecs;
-  for (int base = tid; base < total; base += 256 * U) {
-    u32x4 v[U];
+  for (int base = 0; base < total; base += 256 * U) {
+    if (base > 0) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int idx = min(base + u * 256, total - 1);
-      v[u] = ld_row(xs + idx);  // idx < ntok * row_vecs: token idx / row_vecs of this block
+      for (int u = 0; u < U; ++u) {
+        const int idx = min(base + tid + u * 256, total - 1);
+        v[u] = ld_row(xs + idx);
+      }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int idx = base + u * 256;
+      const int idx = base + tid + u * 256;
       if (idx < total) {
         const int tt = idx / row_vecs;
         const int c = idx - tt * row_vecs;
@@ -200,23 +215,30 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
 
 }  // namespace
 
-int64_t dispatch_num_sub(int64_t N) { return (N + kDispatchTokens - 1) / kDispatchTokens; }
+int64_t dispatch_num_blocks(int64_t N, int bt) { return (N + bt - 1) / bt; }
 
-hipError_t launch_dispatch(const int32_t* ids, const void* x, int64_t N, int64_t row_bytes, int E,
-                           int K, int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
-                           void* x_perm, int32_t* blockcnt, hipStream_t s) {
-  const int64_t T = N * K;
-  const int num_sub = (int)dispatch_num_sub(N);
-  hipLaunchKernelGGL(dispatch_hist_kernel, dim3(num_sub), dim3(64), 0, s, ids, T, K, E, num_sub,
-                     blockcnt);
+hipError_t launch_dispatch_count(const int32_t* ids, int64_t N, int E, int K, int32_t* lrank,
+                                 int32_t* bhist, hipStream_t s) {
+  const int bt = dispatch_count_tokens(K);
+  const int nb = (int)dispatch_num_blocks(N, bt);
+  const size_t dyn = sizeof(int) * (size_t)bt * K;
+  hipLaunchKernelGGL(dispatch_count_kernel, dim3(nb), dim3(256), dyn, s, ids, N, K, E, bt, nb,
+                     lrank, bhist);
+  return hipGetLastError();
+}
+
+hipError_t launch_dispatch_finish(const int32_t* ids, const void* x, int64_t N, int64_t row_bytes,
+                                  int E, int K, int bt, int32_t* counts, int32_t* offsets,
+                                  int32_t* perm, int32_t* inv, void* x_perm,
+                                  const int32_t* lrank, int32_t* bhist, hipStream_t s) {
+  const int nb = (int)dispatch_num_blocks(N, bt);
+  hipLaunchKernelGGL(dispatch_scan_kernel, dim3(E), dim3(256), 0, s, bhist, nb, counts);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(dispatch_scan_kernel, dim3(E), dim3(256), 0, s, blockcnt, num_sub, counts);
-  err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  const size_t dyn = sizeof(int) * 2 * (size_t)kDispatchTokens * K;
-  hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(num_sub), dim3(256), dyn, s, ids, counts,
-                     blockcnt, N, K, E, num_sub, offsets, perm, inv,
+  const int64_t blocks = (N + kScatterTokens - 1) / kScatterTokens;
+  const size_t dyn = sizeof(int) * (size_t)kScatterTokens * K;
+  hipLaunchKernelGGL(dispatch_scatter_kernel, dim3((unsigned)blocks), dim3(256), dyn, s, ids,
+                     counts, bhist, lrank, N, K, E, nb, bt, offsets, perm, inv,
                      reinterpret_cast<const u32x4*>(x), reinterpret_cast<u32x4*>(x_perm),
                      (int)(row_bytes / 16));
   return hipGetLastError();

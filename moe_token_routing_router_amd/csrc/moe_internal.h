@@ -10,10 +10,9 @@ namespace moe {
 // ---- limits -------------------------------------------------------------
 constexpr int kMaxExperts = 256;     // selection range of the fused router
 constexpr int kMaxRouteK = 16;       // one 16-lane group keeps one pick per lane
-#ifndef MOE_DISPATCH_TOKENS
-#define MOE_DISPATCH_TOKENS 16
-#endif
-constexpr int kDispatchTokens = MOE_DISPATCH_TOKENS;  // tokens per dispatch sub-chunk
+// tokens per block of the standalone count kernel (at most 4096 slots, so
+// its LDS copy of the ids stays at 16 KiB)
+inline int dispatch_count_tokens(int K) { return K <= 64 ? 64 : 4096 / K; }
 
 // ---- vector types -------------------------------------------------------
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -35,25 +34,91 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
 }
 
+// ---- block-level stable ranking ------------------------------------------
+// For the S slot ids sids[0..S) of one block (in LDS, published by the
+// caller's writes before the call), computes with NWAVES*64 threads:
+//   out[j]  = #{ j' < j : sids[j'] == sids[j] }  for valid ids (0 <= id < E),
+//             -1 for invalid ones (global memory);
+//   hist[e] = #{ j : sids[j] == e }              (LDS, kMaxExperts ints).
+// Slots are taken NWAVES*64 at a time.  Inside a wave, lanes holding the same
+// id are found with one ballot per id bit (E <= 256: at most 8) and ranked by
+// the count of matching lanes below them; per-wave counts in LDS (wcnt,
+// NWAVES*kMaxExperts ints) give the offset of each wave, and hist carries the
+// running count from round to round.  Every thread of the block must call it.
+template <int NWAVES>
+__device__ void block_stable_rank(const int* sids, int S, int E, int32_t* out, int* hist,
+                                  int* wcnt) {
+  constexpr int NTH = NWAVES * 64;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wid = tid >> 6;
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  for (int e = tid; e < E; e += NTH) hist[e] = 0;
+  for (int i = tid; i < NWAVES * kMaxExperts; i += NTH) wcnt[i] = 0;
+  __syncthreads();
+  const unsigned long long below = (1ull << lane) - 1ull;
+  for (int base = 0; base < S; base += NTH) {
+    const int j = base + tid;
+    const int e = (j < S) ? sids[j] : -1;
+    const bool valid = (unsigned)e < (unsigned)E;
+    unsigned long long m = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = valid && ((e >> b) & 1);
+      const unsigned long long bb = __ballot(bit);
+      m &= bit ? bb : ~bb;
+    }
+    const int rw = __popcll(m & below);
+    if (valid && rw == 0) wcnt[wid * kMaxExperts + e] = __popcll(m);
+    __syncthreads();
+    if (valid) {
+      int rank = hist[e] + rw;
+      for (int w = 0; w < wid; ++w) rank += wcnt[w * kMaxExperts + e];
+      out[j] = rank;
+    } else if (j < S) {
+      out[j] = -1;
+    }
+    __syncthreads();
+    for (int e2 = tid; e2 < E; e2 += NTH) {
+      int sum = 0;
+      for (int w = 0; w < NWAVES; ++w) {
+        sum += wcnt[w * kMaxExperts + e2];
+        wcnt[w * kMaxExperts + e2] = 0;
+      }
+      hist[e2] += sum;
+    }
+    __syncthreads();
+  }
+}
+
 // ---- launchers (each validates nothing: the C ABI layer has done it) -----
-// Router.  wgt is the fragment-major packed gate (bf16 path only).
+// Router.  wgt is the fragment-major packed gate (bf16 path only).  When
+// lrank is not null the router also ranks its own selections for the dispatch
+// (blocks of route_tokens_per_block(E) tokens; see launch_dispatch_finish).
 int route_padded_experts(int E);
 int route_gate_rows(int H);  // H rounded up to whole 64-wide steps (packed gate)
+int route_tokens_per_block(int E);
 hipError_t launch_gate_transpose(const uint16_t* gate_w, int H, int E, uint16_t* wgt,
                                  int32_t* counts, hipStream_t s);
 hipError_t launch_route_bf16(const uint16_t* x, const uint16_t* wgt, const float* bias,
                              int64_t N, int H, int E, int K, int32_t* ids, float* w,
-                             int32_t* counts, hipStream_t s);
+                             int32_t* counts, int32_t* lrank, int32_t* bhist, hipStream_t s);
 hipError_t launch_route_f32(const float* x, const float* gate_w, const float* bias, int64_t N,
                             int H, int E, int K, int32_t* ids, float* w, int32_t* counts,
                             hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
 
-// Dispatch.
-int64_t dispatch_num_sub(int64_t N);
-hipError_t launch_dispatch(const int32_t* ids, const void* x, int64_t N, int64_t row_bytes,
-                           int E, int K, int32_t* counts, int32_t* offsets, int32_t* perm,
-                           int32_t* inv, void* x_perm, int32_t* blockcnt, hipStream_t s);
+// Dispatch.  lrank [N*K] and bhist [E][dispatch_num_blocks(N, bt)] live in
+// the workspace.  count: ranks + block histograms for bt = dispatch_count_tokens(K).
+// finish: scan of bhist (in place) + counts, then scatter (offsets, inv,
+// perm, rows).
+int64_t dispatch_num_blocks(int64_t N, int bt);
+hipError_t launch_dispatch_count(const int32_t* ids, int64_t N, int E, int K, int32_t* lrank,
+                                 int32_t* bhist, hipStream_t s);
+hipError_t launch_dispatch_finish(const int32_t* ids, const void* x, int64_t N, int64_t row_bytes,
+                                  int E, int K, int bt, int32_t* counts, int32_t* offsets,
+                                  int32_t* perm, int32_t* inv, void* x_perm,
+                                  const int32_t* lrank, int32_t* bhist, hipStream_t s);
 
 // Combine.
 hipError_t launch_combine(const void* y, const int32_t* inv, const float* w, int64_t N, int H,

@@ -104,7 +104,8 @@ template <int NT, int U>
 __device__ __forceinline__ void select_topk_store(const float (&v)[U][NT], int r, int E, int K,
                                                   const int64_t (&t)[U], int64_t N,
                                                   int32_t* __restrict__ ids,
-                                                  float* __restrict__ topw, int* hist) {
+                                                  float* __restrict__ topw, int* hist,
+                                                  int (&pick)[U]) {
   uint32_t taken[U];
   float my_val[U], top[U];
   int my_id[U];
@@ -152,6 +153,7 @@ __device__ __forceinline__ void select_topk_store(const float (&v)[U][NT], int r
   }
 #pragma unroll
   for (int u = 0; u < U; ++u) {
+    pick[u] = my_id[u];
     const float ex = (r < K) ? expf(my_val[u] - top[u]) : 0.f;
     const float sum = sum16(ex);
     if ((t[u] < N) & (r < K)) {
@@ -190,7 +192,8 @@ template <int NT, int MT, int NW, int D>
 __global__ __launch_bounds__(NW * 64) void route_bf16_kernel(
     const uint16_t* __restrict__ x, const u32x4* __restrict__ gfrag,
     const float* __restrict__ bias, int64_t N, int H, int E, int K, int32_t* __restrict__ ids,
-    float* __restrict__ topw, int32_t* __restrict__ counts) {
+    float* __restrict__ topw, int32_t* __restrict__ counts, int32_t* __restrict__ lrank,
+    int32_t* __restrict__ bhist, int nb) {
   constexpr int BM = 16 * MT;
   constexpr int EP = 16 * NT;
   constexpr int ROWP = EP + 4;
@@ -199,6 +202,8 @@ __global__ __launch_bounds__(NW * 64) void route_bf16_kernel(
   constexpr int SMEM_A = NW * TILE;
   constexpr int SMEM_P = NW * BM * ROWP * 4;
   static_assert(BM % (4 * NW) == 0, "epilogue maps 4 tokens per wave per pass");
+  static_assert((BM * kMaxRouteK + (NW + 1) * kMaxExperts) * 4 <= (SMEM_A > SMEM_P ? SMEM_A : SMEM_P),
+                "dispatch ranking reuses the tile / partial-sum area");
   __shared__ __align__(16) char smem[SMEM_A > SMEM_P ? SMEM_A : SMEM_P];
   __shared__ int hist[EP];
 
@@ -399,7 +404,28 @@ __global__ __launch_bounds__(NW * 64) void route_bf16_kernel(
       v[u][q] = sum;
     }
   }
-  select_topk_store<NT, U>(v, r, E, K, tt, N, ids, topw, counts ? hist : nullptr);
+  int pick[U];
+  select_topk_store<NT, U>(v, r, E, K, tt, N, ids, topw, counts ? hist : nullptr, pick);
+
+  // For the fused dispatch: stable rank of every selected slot among the
+  // equal ids of this workgroup's BM tokens, and the workgroup's per-expert
+  // histogram (the dispatch count kernel's outputs for blocks of BM tokens).
+  if (lrank) {
+    __syncthreads();  // every wave is done reading the partial sums
+    int* sids = reinterpret_cast<int*>(smem);
+    int* rhist = sids + BM * kMaxRouteK;
+    int* wcnt = rhist + kMaxExperts;
+    if (r < K) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int tl = wid * 4 + g + u * NW * 4;
+        sids[tl * K + r] = pick[u];
+      }
+    }
+    const int ntok = (int)min((int64_t)BM, N - t0);
+    block_stable_rank<NW>(sids, ntok * K, E, lrank + t0 * K, rhist, wcnt);
+    for (int e = tid; e < E; e += NW * 64) bhist[(int64_t)e * nb + blockIdx.x] = rhist[e];
+  }
 
   if (counts) {
     __syncthreads();
@@ -461,7 +487,8 @@ __global__ __launch_bounds__(256) void route_f32_kernel(const float* __restrict_
 #pragma unroll
   for (int q = 0; q < NT; ++q) v1[0][q] = acc[q];
   const int64_t t1[1] = {t};
-  select_topk_store<NT, 1>(v1, r, E, K, t1, N, ids, topw, counts ? hist : nullptr);
+  int pick[1];
+  select_topk_store<NT, 1>(v1, r, E, K, t1, N, ids, topw, counts ? hist : nullptr, pick);
   if (counts) {
     __syncthreads();
     for (int e = tid; e < E; e += 256)
@@ -538,11 +565,18 @@ template <int NT, int MT, int NW = (NT <= 4 ? MOE_ROUTE_NW : NT == 8 ? MOE_ROUTE
           int D = (NT <= 4 ? MOE_ROUTE_DEPTH : 1)>
 hipError_t launch_bf16_nt(const uint16_t* x, const uint16_t* wgt, const float* bias, int64_t N,
                           int H, int E, int K, int32_t* ids, float* w, int32_t* counts,
-                          hipStream_t s) {
+                          int32_t* lrank, int32_t* bhist, hipStream_t s) {
   const int64_t blocks = (N + 16 * MT - 1) / (16 * MT);
   hipLaunchKernelGGL((route_bf16_kernel<NT, MT, NW, D>), dim3((unsigned)blocks), dim3(NW * 64), 0,
-                     s, x, reinterpret_cast<const u32x4*>(wgt), bias, N, H, E, K, ids, w, counts);
+                     s, x, reinterpret_cast<const u32x4*>(wgt), bias, N, H, E, K, ids, w, counts,
+                     lrank, bhist, (int)blocks);
   return hipGetLastError();
+}
+
+// tokens per workgroup of route_bf16_kernel for E experts (must match the
+// MT chosen in launch_route_bf16)
+constexpr int route_mt(int EP) {
+  return EP <= 64 ? (EP <= 32 ? 4 : MOE_ROUTE_MT64) : EP == 128 ? MOE_ROUTE_MT128 : 1;
 }
 
 template <int NT>
@@ -582,15 +616,27 @@ hipError_t launch_gate_transpose(const uint16_t* gate_w, int H, int E, uint16_t*
   return hipGetLastError();
 }
 
+int route_tokens_per_block(int E) { return 16 * route_mt(route_padded_experts(E)); }
+
 hipError_t launch_route_bf16(const uint16_t* x, const uint16_t* wgt, const float* bias, int64_t N,
                              int H, int E, int K, int32_t* ids, float* w, int32_t* counts,
-                             hipStream_t s) {
+                             int32_t* lrank, int32_t* bhist, hipStream_t s) {
   switch (route_padded_experts(E)) {
-    case 16: return launch_bf16_nt<1, 4>(x, wgt, bias, N, H, E, K, ids, w, counts, s);
-    case 32: return launch_bf16_nt<2, 4>(x, wgt, bias, N, H, E, K, ids, w, counts, s);
-    case 64: return launch_bf16_nt<4, MOE_ROUTE_MT64>(x, wgt, bias, N, H, E, K, ids, w, counts, s);
-    case 128: return launch_bf16_nt<8, MOE_ROUTE_MT128>(x, wgt, bias, N, H, E, K, ids, w, counts, s);
-    case 256: return launch_bf16_nt<16, 1, 4>(x, wgt, bias, N, H, E, K, ids, w, counts, s);
+    case 16:
+      return launch_bf16_nt<1, route_mt(16)>(x, wgt, bias, N, H, E, K, ids, w, counts, lrank,
+                                             bhist, s);
+    case 32:
+      return launch_bf16_nt<2, route_mt(32)>(x, wgt, bias, N, H, E, K, ids, w, counts, lrank,
+                                             bhist, s);
+    case 64:
+      return launch_bf16_nt<4, route_mt(64)>(x, wgt, bias, N, H, E, K, ids, w, counts, lrank,
+                                             bhist, s);
+    case 128:
+      return launch_bf16_nt<8, route_mt(128)>(x, wgt, bias, N, H, E, K, ids, w, counts, lrank,
+                                              bhist, s);
+    case 256:
+      return launch_bf16_nt<16, route_mt(256), 4>(x, wgt, bias, N, H, E, K, ids, w, counts,
+                                                  lrank, bhist, s);
   }
   return hipErrorInvalidValue;
 }

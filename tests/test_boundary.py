@@ -62,10 +62,18 @@ def test_workspace_sizes(lib):
         assert n >= EP * H * 2 and n % 256 == 0 and n <= EP * (H + 256) * 2 + 256
     assert lib.moe_route_workspace_size(256, 16, F32) == 0
     assert lib.moe_route_workspace_size(256, 300, BF16) == 0
-    # dispatch: one int per (expert, sub-chunk of 16 tokens), rounded, + 256
-    assert lib.moe_dispatch_workspace_size(16384, 64, 2) == 1024 * 64 * 4 + 256
-    assert lib.moe_dispatch_workspace_size(17, 3, 2) >= 2 * 3 * 4
+    # dispatch: per-block expert histograms (blocks of <= 64 tokens) plus one
+    # rank per slot, each rounded to 256 bytes
+    for N, E, K in ((16384, 64, 2), (17, 3, 2), (32768, 128, 8), (5, 256, 256)):
+        n = lib.moe_dispatch_workspace_size(N, E, K)
+        bt = 64 if K <= 64 else 4096 // K
+        assert n >= N * K * 4 + -(-N // bt) * E * 4 and n % 256 == 0
     assert lib.moe_dispatch_workspace_size(-1, 3, 2) == 0
+    # fused route+dispatch: the router's packed gate plus the dispatch scratch
+    n = lib.moe_route_dispatch_workspace_size(16384, 4096, 64, 2, BF16)
+    assert n >= lib.moe_route_workspace_size(4096, 64, BF16) + 16384 * 2 * 4
+    assert lib.moe_route_dispatch_workspace_size(512, 256, 16, 2, F32) == \
+        lib.moe_dispatch_workspace_size(512, 16, 2)
 
 
 def route(lib, x=A, gw=A, bias=None, N=4, H=16, E=8, K=2, dt=BF16, ids=A2, w=A2, counts=None,
@@ -112,6 +120,27 @@ def test_dispatch_validation(lib):
     assert dispatch(lib, xp=MIS8) == MISALIGNED
     assert dispatch(lib, inv=MIS) == MISALIGNED
     assert dispatch(lib, wsb=8) == WS_SMALL
+
+
+def route_dispatch(lib, x=A, gw=A, bias=None, N=4, H=16, E=8, K=2, dt=BF16, ids=A2, w=A2,
+                   counts=A2, offsets=A2, perm=A2, inv=A2, xp=A, ws=A, wsb=1 << 20):
+    return lib.moe_route_dispatch(x, gw, bias, N, H, E, K, dt, ids, w, counts, offsets, perm, inv,
+                                  xp, ws, wsb, None)
+
+
+def test_route_dispatch_validation(lib):
+    assert route_dispatch(lib, K=9) == INVALID
+    assert route_dispatch(lib, gw=None) == INVALID
+    assert route_dispatch(lib, counts=None) == INVALID
+    assert route_dispatch(lib, perm=None) == INVALID
+    assert route_dispatch(lib, ws=None) == INVALID
+    assert route_dispatch(lib, E=300, K=2) == UNSUPPORTED
+    assert route_dispatch(lib, E=64, K=17) == UNSUPPORTED
+    assert route_dispatch(lib, H=12) == UNSUPPORTED
+    assert route_dispatch(lib, x=MIS8) == MISALIGNED
+    assert route_dispatch(lib, xp=MIS8) == MISALIGNED
+    assert route_dispatch(lib, inv=MIS) == MISALIGNED
+    assert route_dispatch(lib, wsb=64) == WS_SMALL
 
 
 def combine(lib, y=A, inv=A2, w=A2, N=4, H=16, K=2, dt=BF16, out=A):

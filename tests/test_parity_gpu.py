@@ -230,3 +230,63 @@ def test_bitwise_deterministic():
     r2 = gpu_dispatch(a[0], d["x"], d["E"], d["dtype"])
     for u, v in zip(r1, r2):
         np.testing.assert_array_equal(u, v)
+
+
+# ------------------------------------------------------------ fused route+dispatch
+
+def _fused_and_check(d, K, E, dtype, with_rows=True):
+    x = to_dev(d["x"], dtype)
+    gw = to_dev(d["gate_w"], dtype)
+    b = None if d["bias"] is None else torch.from_numpy(d["bias"]).cuda()
+    ids, w, counts, offsets, perm, inv, xp = L.route_dispatch(x, gw, K, bias=b,
+                                                              with_rows=with_rows)
+    # the same two calls made in sequence
+    ids2, w2, _ = L.route(x, gw, K, bias=b)
+    c2, o2, p2, i2, xp2 = L.dispatch(ids2, x if with_rows else None, E, with_rows=with_rows)
+    torch.cuda.synchronize()
+    gids = from_dev(ids)
+    for a, b2 in ((ids, ids2), (w, w2), (counts, c2), (offsets, o2), (perm, p2), (inv, i2)):
+        np.testing.assert_array_equal(from_dev(a), from_dev(b2))
+    # the oracle's dispatch of the fused router's ids, bit for bit
+    oc, oo, op, oi = O.dispatch(gids, E)
+    np.testing.assert_array_equal(from_dev(counts), oc)
+    np.testing.assert_array_equal(from_dev(offsets), oo)
+    np.testing.assert_array_equal(from_dev(perm), op)
+    np.testing.assert_array_equal(from_dev(inv), oi)
+    if with_rows:
+        np.testing.assert_array_equal(from_dev(xp).view(np.uint8),
+                                      O.permute_rows(d["x"], op, K).view(np.uint8))
+        np.testing.assert_array_equal(from_dev(xp).view(np.uint8), from_dev(xp2).view(np.uint8))
+    return gids, from_dev(w)
+
+
+@pytest.mark.parametrize("name", WORKLOADS)
+def test_route_dispatch_full_size(name):
+    d = workload(name)
+    o = d["o"]
+    print(f"[route_dispatch] {name}", flush=True)
+    gids, gw_ = _fused_and_check(d, d["K"], d["E"], d["dtype"])
+    check_route(gids, gw_, o["ids"], o["w"], o["logits"], d["K"], d["dtype"])
+
+
+@pytest.mark.parametrize("N,H,E,K,dtype,bias", EDGE)
+def test_route_dispatch_edge_cases(N, H, E, K, dtype, bias):
+    print(f"[route_dispatch edge] N={N} H={H} E={E} K={K} {dtype}", flush=True)
+    d = I.random_case(N * 7 + H, N, H, E, K, dtype, bias=bias)
+    ids_o, w_o, logits_o, _ = O.route(d["x"], d["gate_w"], d["bias"], K, dtype)
+    gids, gw_ = _fused_and_check(d, K, E, dtype)
+    check_route(gids, gw_, ids_o, w_o, logits_o, K, dtype)
+
+
+def test_route_dispatch_metadata_only():
+    d = I.random_case(11, 777, 256, 64, 4, "bf16", bias=True)
+    _fused_and_check(d, 4, 64, "bf16", with_rows=False)
+
+
+def test_route_dispatch_empty():
+    dev = torch.device("cuda")
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device=dev)
+    gw = torch.zeros((64, 16), dtype=torch.bfloat16, device=dev)
+    ids, w, counts, offsets, perm, inv, xp = L.route_dispatch(x, gw, 2)
+    torch.cuda.synchronize()
+    assert (counts == 0).all() and (offsets == 0).all() and xp.shape == (0, 64)
