@@ -4,9 +4,11 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 One step is one pass of the whole path over one batch of synthetic input:
-moe_route (x @ gate_w -> top-K -> renormalised weights), moe_dispatch
-(counting sort + row scatter into expert-contiguous order) and moe_combine
-(weighted un-permute of the expert outputs y).  The default workload is
+routing (x @ gate_w -> top-K -> renormalised weights), dispatch (counting
+sort + row scatter into expert-contiguous order) and combine (weighted
+un-permute of the expert outputs y), made as moe_route_dispatch +
+moe_combine; the same path as three calls (moe_route, moe_dispatch,
+moe_combine) is timed beside it.  The default workload is
 N=16384 tokens (8 sequences x 2048), H=4096, E=64, K=2, bf16.  Inputs are
 resident in HBM before the timed region; three input sets are rotated so the
 256 MiB Infinity Cache never serves a step the data of the previous step.
@@ -146,7 +148,6 @@ def main():
         st = dict(x=x, y=y,
                   ids=torch.empty((N, K), dtype=torch.int32, device=dev),
                   w=torch.empty((N, K), dtype=torch.float32, device=dev),
-                  counts_r=torch.empty((E,), dtype=torch.int32, device=dev),
                   counts=torch.empty((E,), dtype=torch.int32, device=dev),
                   offsets=torch.empty((E + 1,), dtype=torch.int32, device=dev),
                   perm=torch.empty((T,), dtype=torch.int32, device=dev),
@@ -157,12 +158,16 @@ def main():
     rws = torch.empty((max(1, L.moe_route_workspace_size(H, E, tdt)),), dtype=torch.uint8,
                       device=dev)
     dws = torch.empty((L.moe_dispatch_workspace_size(N, E, K),), dtype=torch.uint8, device=dev)
+    fws = torch.empty((L.moe_route_dispatch_workspace_size(N, H, E, K, tdt),), dtype=torch.uint8,
+                      device=dev)
 
     # validate every buffer once through the checked binding
     for st in sets:
-        L.moe_route(st["x"], gw, bias, K, st["ids"], st["w"], st["counts_r"], rws)
+        L.moe_route(st["x"], gw, bias, K, st["ids"], st["w"], None, rws)
         L.moe_dispatch(st["ids"], st["x"], E, st["counts"], st["offsets"], st["perm"],
                        st["inv"], st["x_perm"], dws)
+        L.moe_route_dispatch(st["x"], gw, bias, K, st["ids"], st["w"], st["counts"],
+                             st["offsets"], st["perm"], st["inv"], st["x_perm"], fws)
         L.moe_combine(st["y"], st["inv"], st["w"], st["out"])
     torch.cuda.synchronize()
 
@@ -173,69 +178,76 @@ def main():
     dt = L.MOE_BF16 if wl.dtype == "bf16" else L.MOE_F32
     calls = []
     for st in sets:
-        calls.append((
-            (P(st["x"]), P(gw), P(bias), N, H, E, K, dt, P(st["ids"]), P(st["w"]),
-             P(st["counts_r"]), P(rws), rws.numel(), sp),
-            (P(st["ids"]), P(st["x"]), N, H, E, K, dt, P(st["counts"]), P(st["offsets"]),
-             P(st["perm"]), P(st["inv"]), P(st["x_perm"]), P(dws), dws.numel(), sp),
-            (P(st["y"]), P(st["inv"]), P(st["w"]), N, H, K, dt, P(st["out"]), sp)))
+        calls.append(dict(
+            route=(P(st["x"]), P(gw), P(bias), N, H, E, K, dt, P(st["ids"]), P(st["w"]), None,
+                   P(rws), rws.numel(), sp),
+            dispatch=(P(st["ids"]), P(st["x"]), N, H, E, K, dt, P(st["counts"]),
+                      P(st["offsets"]), P(st["perm"]), P(st["inv"]), P(st["x_perm"]), P(dws),
+                      dws.numel(), sp),
+            route_dispatch=(P(st["x"]), P(gw), P(bias), N, H, E, K, dt, P(st["ids"]),
+                            P(st["w"]), P(st["counts"]), P(st["offsets"]), P(st["perm"]),
+                            P(st["inv"]), P(st["x_perm"]), P(fws), fws.numel(), sp),
+            combine=(P(st["y"]), P(st["inv"]), P(st["w"]), N, H, K, dt, P(st["out"]), sp)))
+    fn = {"route": lib.moe_route, "dispatch": lib.moe_dispatch,
+          "route_dispatch": lib.moe_route_dispatch, "combine": lib.moe_combine}
 
-    def step(i):
-        r, dsp, c = calls[i % N_SETS]
-        s1 = lib.moe_route(*r)
-        s2 = lib.moe_dispatch(*dsp)
-        s3 = lib.moe_combine(*c)
-        if s1 or s2 or s3:
-            raise RuntimeError(f"status route={s1} dispatch={s2} combine={s3}")
+    def call(name, i):
+        status = fn[name](*calls[i % N_SETS][name])
+        if status:
+            raise RuntimeError(f"{name} returned status {status}")
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
+    def step(i):  # the whole path: fused route+dispatch, then combine
+        call("route_dispatch", i)
+        call("combine", i)
 
-    # timed region 1: the whole path, K steps, nothing between the launches
-    e_start = torch.cuda.Event(enable_timing=True)
-    e_stop = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    e_start.record(stream)
-    for i in range(args.steps):
-        step(i)
-    e_stop.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    gpu_ms = e_start.elapsed_time(e_stop)
+    def step_unfused(i):  # the same path as three separate calls
+        call("route", i)
+        call("dispatch", i)
+        call("combine", i)
 
-    # timed region 2: each stage on its own, K back-to-back calls (rotating
-    # the input sets) between one pair of HIP events on the launch stream:
-    # the average duration of one call of that stage
-    stage_fn = {"route": lambda i: lib.moe_route(*calls[i % N_SETS][0]),
-                "dispatch": lambda i: lib.moe_dispatch(*calls[i % N_SETS][1]),
-                "combine": lambda i: lib.moe_combine(*calls[i % N_SETS][2])}
-    stage_ms = {}
-    for name, fn in stage_fn.items():
-        for i in range(3):
-            fn(i)
+    def timed(fn_step, n):
         a = torch.cuda.Event(enable_timing=True)
         z = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
+        t0 = time.perf_counter()
         a.record(stream)
-        for i in range(args.steps):
-            fn(i)
+        for i in range(n):
+            fn_step(i)
         z.record(stream)
         torch.cuda.synchronize()
-        stage_ms[name] = a.elapsed_time(z) / args.steps
+        return time.perf_counter() - t0, a.elapsed_time(z)
+
+    for i in range(args.warmup):
+        step(i)
+        step_unfused(i)
+    torch.cuda.synchronize()
+
+    # timed region 1: the whole path, K steps, nothing between the launches
+    wall, gpu_ms = timed(step, args.steps)
+    # timed region 2: the same path as three separate calls
+    wall_u, gpu_ms_u = timed(step_unfused, args.steps)
+    # timed region 3: each call on its own, K back-to-back calls (rotating the
+    # input sets) between one pair of HIP events on the launch stream: the
+    # average duration of one call
+    stage_ms = {}
+    for name in ("route_dispatch", "combine", "route", "dispatch"):
+        for i in range(3):
+            call(name, i)
+        _, ms = timed(lambda i, n=name: call(n, i), args.steps)
+        stage_ms[name] = ms / args.steps
     # leave every set's outputs consistent for the check below
     for i in range(N_SETS):
         step(i)
     torch.cuda.synchronize()
 
-    # correctness guard on the last step's outputs (cheap invariants only)
-    last = sets[(args.steps - 1) % N_SETS]
+    # correctness guard on the outputs (cheap invariants only)
+    last = sets[0]
     cnt = last["counts"].cpu().numpy()
     assert cnt.sum() == T, "token conservation violated"
     load = cnt.astype(np.float64)
 
     alg = algorithmic_bytes(N, H, E, K, b)
+    alg["route_dispatch"] = alg["route"] + alg["dispatch"]
     stages = {}
     for k, ms in stage_ms.items():
         stages[k] = {"ms_per_call": round(ms, 5), "alg_MB": round(alg[k] / 1e6, 3),
@@ -245,8 +257,8 @@ def main():
     stages["route"]["mfma_util"] = round(
         r_flops / (stage_ms["route"] * 1e-3) / (BF16_MFMA_PEAK_TFLOPS * 1e12), 4)
 
-    # dominant kernel: combine (one launch per call, the largest per-kernel
-    # time of the path)
+    # dominant kernel: combine (one launch per call, the largest kernel of
+    # the path)
     kern = "combine"
     avg_ms = stage_ms[kern]
     achieved = alg[kern] / (avg_ms * 1e-3) / 1e9
@@ -265,6 +277,7 @@ def main():
         torch.cuda.synchronize()
 
     ms_per_step = wall * 1e3 / args.steps
+    alg_step = alg["route"] + alg["dispatch"] + alg["combine"]
     res = {
         "metric": "routed tokens/s (route+dispatch+combine)",
         "value": round(N * args.steps / wall, 1),
@@ -275,11 +288,15 @@ def main():
         "dtype": wl.dtype, "data": "synthetic (seeded, resident in HBM, 3 rotating sets)",
         "config": {"workload": wl.describe(), "N": N, "H": H, "E": E, "K": K,
                    "bias": wl.bias, "name": wl.name},
-        "pipeline": {"gpu_ms_per_step": round(gpu_ms / args.steps, 5),
-                     "stage_sum_ms": round(sum(stage_ms.values()), 5),
-                     "alg_MB_per_step": round(sum(alg.values()) / 1e6, 3),
-                     "hbm_frac": round(sum(alg.values()) / (gpu_ms / args.steps * 1e-3) / 1e9
+        "pipeline": {"calls": "moe_route_dispatch + moe_combine",
+                     "gpu_ms_per_step": round(gpu_ms / args.steps, 5),
+                     "alg_MB_per_step": round(alg_step / 1e6, 3),
+                     "hbm_frac": round(alg_step / (gpu_ms / args.steps * 1e-3) / 1e9
                                        / HBM_PEAK_GBS, 4)},
+        "pipeline_unfused": {"calls": "moe_route + moe_dispatch + moe_combine",
+                             "ms_per_step": round(wall_u * 1e3 / args.steps, 5),
+                             "gpu_ms_per_step": round(gpu_ms_u / args.steps, 5),
+                             "tokens_per_s": round(N * args.steps / wall_u, 1)},
         "stages": stages,
         "load_max_over_mean": round(float(load.max() / load.mean()), 3),
         "roofline": roofline,
