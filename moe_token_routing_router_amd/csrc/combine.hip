@@ -18,6 +18,9 @@
 #ifndef MOE_COMBINE_TOKENS
 #define MOE_COMBINE_TOKENS 1   // tokens per workgroup
 #endif
+#ifndef MOE_COMBINE_U2
+#define MOE_COMBINE_U2 4        // output vectors per lane in flight for K = 2
+#endif
 #ifndef MOE_COMBINE_NT_LOAD
 #define MOE_COMBINE_NT_LOAD 1   // non-temporal loads of y (each row is read once)
 #endif
@@ -173,7 +176,7 @@ hipError_t launch_dtype(const void* y, const int32_t* inv, const float* w, int64
                         int K, void* out, hipStream_t s) {
   switch (K) {
     case 1: return launch_k<BF16, 1, 8>(y, inv, w, N, H, K, out, s);
-    case 2: return launch_k<BF16, 2, 4>(y, inv, w, N, H, K, out, s);
+    case 2: return launch_k<BF16, 2, MOE_COMBINE_U2>(y, inv, w, N, H, K, out, s);
     case 4: return launch_k<BF16, 4, 2>(y, inv, w, N, H, K, out, s);
     case 8: return launch_k<BF16, 8, 2>(y, inv, w, N, H, K, out, s);
     default: return launch_k<BF16, 0, 1>(y, inv, w, N, H, K, out, s);

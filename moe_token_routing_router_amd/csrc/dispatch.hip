@@ -40,6 +40,9 @@
 #ifndef MOE_SCATTER_TOKENS
 #define MOE_SCATTER_TOKENS 1   // tokens per scatter workgroup
 #endif
+#ifndef MOE_SCATTER_U
+#define MOE_SCATTER_U 4        // row vectors per lane loaded before their stores
+#endif
 
 namespace moe {
 
@@ -144,7 +147,7 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
   const int ntok = (int)min((int64_t)kScatterTokens, N - n0);
   const int64_t T = N * K;
 
-  constexpr int U = 4;
+  constexpr int U = MOE_SCATTER_U;
   const int total = ntok * row_vecs;
   const u32x4* xs = x + n0 * (int64_t)row_vecs;
   u32x4 v[U];
