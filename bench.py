@@ -253,6 +253,14 @@ def main():
         stages[k] = {"ms_per_call": round(ms, 5), "alg_MB": round(alg[k] / 1e6, 3),
                      "alg_GBs": round(alg[k] / ms / 1e6, 1),
                      "hbm_frac": round(alg[k] / ms / 1e6 / HBM_PEAK_GBS, 4)}
+    # what dispatch adds to the fused call: moe_route_dispatch minus moe_route
+    # (the router's epilogue does the ranking, so the count launch disappears)
+    if "route_dispatch" in stage_ms and "route" in stage_ms:
+        marg = stage_ms["route_dispatch"] - stage_ms["route"]
+        stages["dispatch_marginal_in_fused_call"] = {
+            "ms_per_call": round(marg, 5), "alg_MB": round(alg["dispatch"] / 1e6, 3),
+            "alg_GBs": round(alg["dispatch"] / marg / 1e6, 1),
+            "hbm_frac": round(alg["dispatch"] / marg / 1e6 / HBM_PEAK_GBS, 4)}
     r_flops = 2.0 * N * H * E
     stages["route"]["mfma_util"] = round(
         r_flops / (stage_ms["route"] * 1e-3) / (BF16_MFMA_PEAK_TFLOPS * 1e12), 4)

@@ -73,12 +73,7 @@ __device__ __forceinline__ void st_row(u32x4* p, u32x4 v) {
 __device__ __forceinline__ int block_exclusive_scan_256(int v, int* lds, int* total) {
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
-  int incl = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int o = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += o;
-  }
+  const int incl = wave_inclusive_sum(v);
   if (lane == 63) lds[wid] = incl;
   __syncthreads();
   int wbase = 0, tot = 0;

@@ -34,6 +34,26 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
 }
 
+// ---- wave-wide inclusive prefix sum with DPP ------------------------------
+// Hillis-Steele inside each 16-lane row (row_shr 1, 2, 4, 8: a lane without
+// a source adds 0), then row_bcast:15 adds row 0's total to row 1 and row 2's
+// to row 3, and row_bcast:31 adds lane 31's (rows 0-1) to rows 2 and 3.
+// Register-to-register moves, no LDS round trips.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ int dpp_add_src(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xF, false);
+}
+
+__device__ __forceinline__ int wave_inclusive_sum(int v) {
+  v += dpp_add_src<0x111>(v);         // row_shr:1
+  v += dpp_add_src<0x112>(v);         // row_shr:2
+  v += dpp_add_src<0x114>(v);         // row_shr:4
+  v += dpp_add_src<0x118>(v);         // row_shr:8
+  v += dpp_add_src<0x142, 0xA>(v);    // row_bcast:15 into rows 1, 3
+  v += dpp_add_src<0x143, 0xC>(v);    // row_bcast:31 into rows 2, 3
+  return v;
+}
+
 // ---- block-level stable ranking ------------------------------------------
 // For the S slot ids sids[0..S) of one block (in LDS, published by the
 // caller's writes before the call), computes with NWAVES*64 threads:
@@ -46,7 +66,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // NWAVES*kMaxExperts ints) give the offset of each wave, and hist carries the
 // running count from round to round.  Every thread of the block must call it.
 template <int NWAVES>
-__device__ void block_stable_rank(const int* sids, int S, int E, int32_t* out, int* hist,
+__device__ __forceinline__ void block_stable_rank(const int* sids, int S, int E, int32_t* out, int* hist,
                                   int* wcnt) {
   constexpr int NTH = NWAVES * 64;
   const int tid = threadIdx.x;

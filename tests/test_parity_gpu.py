@@ -137,6 +137,7 @@ EDGE = [
     (250, 64, 64, 1, "bf16", False),
     (1000, 264, 32, 2, "f32", False),
     (5000, 128, 64, 6, "bf16", True),     # many dispatch sub-chunks
+    (2000, 64, 256, 4, "bf16", True),     # fused path: histograms too many for the in-router scan
 ]
 
 
@@ -167,6 +168,20 @@ def test_dispatch_skewed_and_empty_experts(skew):
     oc, oo, op, oi = O.dispatch(ids, E)
     if skew >= 4.0:
         assert (oc == 0).any()
+    gc, go, gp, gi, gx = gpu_dispatch(ids, x, E, "bf16")
+    for a, b in ((gc, oc), (go, oo), (gp, op), (gi, oi)):
+        np.testing.assert_array_equal(a, b)
+    np.testing.assert_array_equal(gx, O.permute_rows(x, op, K))
+
+
+def test_dispatch_many_blocks():
+    # 1025 histogram blocks with a ragged last one: the scan's per-thread runs
+    # span several blocks
+    N, E, K, H = 65537, 24, 2, 8
+    print(f"[dispatch-many-blocks] N={N} slots={N * K}", flush=True)
+    ids = I.random_ids(N, N, E, K, skew=1.0)
+    x = I.random_case(N, N, H, 4, 1, "bf16", with_y=False)["x"]
+    oc, oo, op, oi = O.dispatch(ids, E)
     gc, go, gp, gi, gx = gpu_dispatch(ids, x, E, "bf16")
     for a, b in ((gc, oc), (go, oo), (gp, op), (gi, oi)):
         np.testing.assert_array_equal(a, b)
