@@ -211,6 +211,106 @@ int oracle_permute_rows(const void *x, int64_t N, int32_t K, int64_t row_bytes,
   return 0;
 }
 
+/* ---- [D] expert-parallel dispatch metadata, deduplicated ---------------- */
+
+/*
+ * oracle_ep_dispatch: the metadata of [D] 8.2's fused_dedup_prepare_dispatch
+ * for ep_size = R ranks holding E/R consecutive experts each (expert e lives
+ * on rank e / (E/R)), with the ranks simulated as segments of one buffer.
+ * Readings (the pages name the steps, not their outputs):
+ *  - a token is sent once to each distinct rank among its K experts
+ *    (deduplication); slot i = n*K+k "owns" the pair (n, rank of ids[i]) when
+ *    no k' < k of the same token has an expert on that rank;
+ *  - the send buffer is rank-major, tokens in ascending order inside a rank
+ *    (a stable counting sort of the owner slots by rank);
+ *  - expand_idx lists, for every dispatched row p of the expert-contiguous
+ *    order of oracle_dispatch, the row of the receiving rank's segment that
+ *    holds its token, counted from the start of that segment.
+ * Outputs:
+ *   send_counts[r]  = number of owner slots on rank r      (R entries)
+ *   send_offsets[0] = 0, send_offsets[r+1] = send_offsets[r] + send_counts[r]
+ *   send_tok[j]     = token of send row j, j < send_offsets[R]
+ *   send_row[i]     = send row of token i/K for the rank of ids[i] (slots
+ *                     sharing a rank share the row)
+ *   expand_idx[p]   = send_row[perm[p]] - send_offsets[rank of ids[perm[p]]]
+ * with perm from the counting-sort dispatch (computed here the same literal
+ * way).  Returns -1 on a bad argument, E % R != 0, an id outside [0,E) or a
+ * token with a repeated expert.
+ */
+int oracle_ep_dispatch(const int32_t *ids, int64_t N, int32_t K, int32_t E,
+                       int32_t R, int32_t *send_counts, int32_t *send_offsets,
+                       int32_t *send_tok, int32_t *send_row,
+                       int32_t *expand_idx) {
+  if (N < 0 || K < 1 || E <= 0 || R <= 0 || E % R != 0) return -1;
+  const int32_t per_rank = E / R;
+  const int64_t T = N * (int64_t)K;
+  int32_t *counts = (int32_t *)malloc(sizeof(int32_t) * (size_t)E);
+  int32_t *offsets = (int32_t *)malloc(sizeof(int32_t) * ((size_t)E + 1));
+  int32_t *perm = (int32_t *)malloc(sizeof(int32_t) * (size_t)(T > 0 ? T : 1));
+  int32_t *inv = (int32_t *)malloc(sizeof(int32_t) * (size_t)(T > 0 ? T : 1));
+  unsigned char *owner = (unsigned char *)malloc((size_t)(T > 0 ? T : 1));
+  int32_t *cursor = (int32_t *)malloc(sizeof(int32_t) * (size_t)R);
+  int rc = -1;
+  if (!counts || !offsets || !perm || !inv || !owner || !cursor) goto done;
+
+  /* expert-level counting sort (the same definition as oracle_dispatch) */
+  if (oracle_dispatch(ids, N, K, E, counts, offsets, perm, inv) != 0) goto done;
+
+  /* which slots own a (token, rank) pair; per-rank counts of the owners */
+  for (int32_t r = 0; r < R; ++r) send_counts[r] = 0;
+  for (int64_t n = 0; n < N; ++n) {
+    for (int32_t k = 0; k < K; ++k) {
+      const int32_t e = ids[n * K + k];
+      const int32_t r = e / per_rank;
+      int first = 1;
+      for (int32_t k2 = 0; k2 < k; ++k2) {
+        if (ids[n * K + k2] == e) goto done; /* repeated expert */
+        if (ids[n * K + k2] / per_rank == r) first = 0;
+      }
+      owner[n * K + k] = (unsigned char)first;
+      if (first) send_counts[r] += 1;
+    }
+  }
+  send_offsets[0] = 0;
+  for (int32_t r = 0; r < R; ++r) send_offsets[r + 1] = send_offsets[r] + send_counts[r];
+
+  /* stable counting sort of the owner slots by rank */
+  for (int32_t r = 0; r < R; ++r) cursor[r] = send_offsets[r];
+  for (int64_t i = 0; i < T; ++i) {
+    if (!owner[i]) continue;
+    const int32_t row = cursor[ids[i] / per_rank]++;
+    send_tok[row] = (int32_t)(i / K);
+    send_row[i] = row;
+  }
+  /* slots that share a rank with an earlier slot of their token */
+  for (int64_t n = 0; n < N; ++n) {
+    for (int32_t k = 0; k < K; ++k) {
+      if (owner[n * K + k]) continue;
+      const int32_t r = ids[n * K + k] / per_rank;
+      for (int32_t k2 = 0; k2 < k; ++k2) {
+        if (owner[n * K + k2] && ids[n * K + k2] / per_rank == r) {
+          send_row[n * K + k] = send_row[n * K + k2];
+          break;
+        }
+      }
+    }
+  }
+  /* receiver side: dispatched row p takes its token from its rank's segment */
+  for (int64_t p = 0; p < T; ++p) {
+    const int32_t i = perm[p];
+    expand_idx[p] = send_row[i] - send_offsets[ids[i] / per_rank];
+  }
+  rc = 0;
+done:
+  free(counts);
+  free(offsets);
+  free(perm);
+  free(inv);
+  free(owner);
+  free(cursor);
+  return rc;
+}
+
 /* ---- [A] weighted combine --------------------------------------------- */
 
 /*

@@ -5,6 +5,7 @@ IEEE double.  bf16 tensors travel as their raw uint16 bit patterns, fp32 as
 float32.  See oracle.c for the definitions and the pages they follow:
   route    - moe-engine page, "Fused Triton routing kernel" section
   dispatch - PithTrain page, section 8.2 (counting sort instead of argsort)
+  ep_dispatch - the same section: per-rank counts, send metadata, dedup
   combine  - PithTrain page, section 6.1 (forward_aggregate)
 """
 import ctypes
@@ -34,6 +35,8 @@ def _load():
         lib.oracle_route.restype = ctypes.c_int
         lib.oracle_dispatch.argtypes = [P, i64, i32, i32, P, P, P, P]
         lib.oracle_dispatch.restype = ctypes.c_int
+        lib.oracle_ep_dispatch.argtypes = [P, i64, i32, i32, i32, P, P, P, P, P]
+        lib.oracle_ep_dispatch.restype = ctypes.c_int
         lib.oracle_permute_rows.argtypes = [P, i64, i32, i64, P, P]
         lib.oracle_permute_rows.restype = ctypes.c_int
         lib.oracle_combine.argtypes = [P, P, P, i64, i32, i32, i32, P]
@@ -105,6 +108,29 @@ def dispatch(ids, E):
     if rc != 0:
         raise ValueError("oracle_dispatch rejected its arguments")
     return counts, offsets, perm, inv
+
+
+def ep_dispatch(ids, E, R):
+    """Expert-parallel send metadata with per-(token, rank) deduplication.
+
+    ids int32 [N,K]; R ranks of E/R experts each.  Returns (send_counts [R],
+    send_offsets [R+1], send_tok [S], send_row [N*K], expand_idx [N*K]), all
+    int32, S = send_offsets[R] (see oracle_ep_dispatch for the definitions).
+    """
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    N, K = ids.shape
+    T = N * K
+    send_counts = np.empty((R,), np.int32)
+    send_offsets = np.empty((R + 1,), np.int32)
+    send_tok = np.empty((max(T, 1),), np.int32)
+    send_row = np.empty((T,), np.int32)
+    expand_idx = np.empty((T,), np.int32)
+    rc = _load().oracle_ep_dispatch(_ptr(ids), N, K, E, R, _ptr(send_counts),
+                                    _ptr(send_offsets), _ptr(send_tok), _ptr(send_row),
+                                    _ptr(expand_idx))
+    if rc != 0:
+        raise ValueError("oracle_ep_dispatch rejected its arguments")
+    return send_counts, send_offsets, send_tok[:send_offsets[R]].copy(), send_row, expand_idx
 
 
 def permute_rows(x, perm, K):

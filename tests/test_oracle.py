@@ -257,6 +257,89 @@ def test_dispatch_rejects_out_of_range_ids():
         O.dispatch(np.array([[-1, 0]], np.int32), 4)
 
 
+# ---------------------------------------------------------------- EP metadata
+
+def test_ep_dispatch_hand_example():
+    c = _golden()["ep_dispatch_small"]
+    got = O.ep_dispatch(np.array(c["ids"], np.int32), c["E"], c["R"])
+    for a, key in zip(got, ("send_counts", "send_offsets", "send_tok", "send_row", "expand_idx")):
+        np.testing.assert_array_equal(a, c[key])
+
+
+def test_ep_dispatch_single_rank_closed_form():
+    # one rank holds every expert: each token is sent exactly once, in order
+    ids = I.random_ids(3, 57, 12, 3)
+    sc, so, st, sr, ex = O.ep_dispatch(ids, 12, 1)
+    _, _, perm, _ = O.dispatch(ids, 12)
+    np.testing.assert_array_equal(sc, [57])
+    np.testing.assert_array_equal(so, [0, 57])
+    np.testing.assert_array_equal(st, np.arange(57))
+    np.testing.assert_array_equal(sr, np.repeat(np.arange(57), 3))
+    np.testing.assert_array_equal(ex, perm // 3)
+
+
+def test_ep_dispatch_one_expert_per_rank_is_plain_dispatch():
+    # E ranks of one expert: nothing to deduplicate (a token's experts are
+    # distinct), so the send metadata is the dispatch metadata
+    ids = I.random_ids(4, 91, 10, 4, skew=1.0)
+    counts, offsets, perm, inv = O.dispatch(ids, 10)
+    sc, so, st, sr, ex = O.ep_dispatch(ids, 10, 10)
+    np.testing.assert_array_equal(sc, counts)
+    np.testing.assert_array_equal(so, offsets)
+    np.testing.assert_array_equal(sr, inv)
+    np.testing.assert_array_equal(st, perm // 4)
+    seg = np.repeat(np.arange(10), counts)
+    np.testing.assert_array_equal(ex, np.arange(91 * 4) - offsets[seg])
+
+
+def test_ep_dispatch_bruteforce_sets():
+    # built another way on tiny inputs: the set of tokens each rank needs,
+    # sorted, and numpy's stable argsort for the expert order
+    for seed in range(300):
+        rng = np.random.default_rng(20_000 + seed)
+        R = int(rng.integers(1, 5))
+        E = R * int(rng.integers(1, 4))
+        K = int(rng.integers(1, min(E, 4) + 1))
+        N = int(rng.integers(0, 40))
+        ids = I.random_ids(seed, N, E, K, skew=float(rng.uniform(0, 2)))
+        sc, so, st, sr, ex = O.ep_dispatch(ids, E, R)
+        per = E // R
+        toks = [sorted({n for n in range(N) for k in range(K) if ids[n, k] // per == r})
+                for r in range(R)]
+        np.testing.assert_array_equal(sc, [len(t) for t in toks])
+        base = np.concatenate([[0], np.cumsum([len(t) for t in toks])])
+        np.testing.assert_array_equal(so, base)
+        np.testing.assert_array_equal(st, np.array([n for t in toks for n in t], np.int64))
+        want_row = [base[ids[n, k] // per] + toks[ids[n, k] // per].index(n)
+                    for n in range(N) for k in range(K)]
+        np.testing.assert_array_equal(sr, np.array(want_row, np.int64).reshape(-1))
+        perm = np.argsort(ids.ravel(), kind="stable")
+        np.testing.assert_array_equal(ex, np.array(want_row, np.int64).reshape(-1)[perm]
+                                      - base[ids.ravel()[perm] // per])
+
+
+def test_ep_dispatch_receivers_rebuild_the_dispatched_rows():
+    # the deduplicated send rows, expanded with expand_idx on each rank,
+    # are exactly the rows of the plain dispatch
+    d = I.random_case(8, 300, 16, 4, 1, "bf16", with_y=False)
+    ids = I.random_ids(8, 300, 32, 6)
+    sc, so, st, sr, ex = O.ep_dispatch(ids, 32, 4)
+    _, _, perm, _ = O.dispatch(ids, 32)
+    x_send = d["x"][st]
+    ranks = ids.ravel()[perm] // 8
+    np.testing.assert_array_equal(x_send[so[ranks] + ex], O.permute_rows(d["x"], perm, 6))
+    assert sc.sum() < 300 * 6  # six experts over four ranks always share one
+
+
+def test_ep_dispatch_rejects_bad_arguments():
+    with pytest.raises(ValueError):
+        O.ep_dispatch(np.array([[0, 1]], np.int32), 6, 4)  # E % R != 0
+    with pytest.raises(ValueError):
+        O.ep_dispatch(np.array([[1, 1]], np.int32), 4, 2)  # repeated expert
+    with pytest.raises(ValueError):
+        O.ep_dispatch(np.array([[0, 4]], np.int32), 4, 2)  # id out of range
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_permute_rows_is_row_gather(dtype):
     # P10: x_perm[r] is bitwise x[perm[r] // K] (numpy fancy indexing)

@@ -55,6 +55,18 @@ MUTANTS = [
     ("combine rounds twice",
      "double_to_bf16(acc);",
      "double_to_bf16((double)(float)acc);"),
+    ("ep no deduplication",
+     "if (ids[n * K + k2] / per_rank == r) first = 0;",
+     "if (0) first = 0;"),
+    ("ep tokens in descending order",
+     "for (int64_t i = 0; i < T; ++i) {\n    if (!owner[i]) continue;",
+     "for (int64_t i = T - 1; i >= 0; --i) {\n    if (!owner[i]) continue;"),
+    ("ep shared slot off by one",
+     "send_row[n * K + k] = send_row[n * K + k2];",
+     "send_row[n * K + k] = send_row[n * K + k2] + 1;"),
+    ("ep expand index not segment-relative",
+     "expand_idx[p] = send_row[i] - send_offsets[ids[i] / per_rank];",
+     "expand_idx[p] = send_row[i];"),
     ("bf16 decode shifted",
      "uint32_t u = (uint32_t)b << 16;",
      "uint32_t u = (uint32_t)b << 15;"),
