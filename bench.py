@@ -36,6 +36,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA, TFLOP/s
 N_SETS = 3
+EP_RANKS = 8                  # expert-parallel ranks simulated by moe_ep_dispatch
 
 
 def algorithmic_bytes(N, H, E, K, b):
@@ -155,6 +156,18 @@ def main():
                   x_perm=torch.empty((T, H), dtype=tdt, device=dev),
                   out=torch.empty((N, H), dtype=tdt, device=dev))
         sets.append(st)
+    # expert-parallel send metadata (measured on its own, not part of the step)
+    R = EP_RANKS if E % EP_RANKS == 0 else 1
+    cap = N * min(K, R)
+    for st in sets:
+        st.update(send_counts=torch.empty((R,), dtype=torch.int32, device=dev),
+                  send_offsets=torch.empty((R + 1,), dtype=torch.int32, device=dev),
+                  send_tok=torch.empty((cap,), dtype=torch.int32, device=dev),
+                  send_row=torch.empty((T,), dtype=torch.int32, device=dev),
+                  expand_idx=torch.empty((T,), dtype=torch.int32, device=dev),
+                  x_send=torch.empty((cap, H), dtype=tdt, device=dev))
+    ews = torch.empty((L.moe_ep_dispatch_workspace_size(N, E, K, R),), dtype=torch.uint8,
+                      device=dev)
     rws = torch.empty((max(1, L.moe_route_workspace_size(H, E, tdt)),), dtype=torch.uint8,
                       device=dev)
     dws = torch.empty((L.moe_dispatch_workspace_size(N, E, K),), dtype=torch.uint8, device=dev)
@@ -169,6 +182,9 @@ def main():
         L.moe_route_dispatch(st["x"], gw, bias, K, st["ids"], st["w"], st["counts"],
                              st["offsets"], st["perm"], st["inv"], st["x_perm"], fws)
         L.moe_combine(st["y"], st["inv"], st["w"], st["out"])
+        L.moe_ep_dispatch(st["ids"], st["x"], E, R, st["counts"], st["offsets"], st["perm"],
+                          st["inv"], st["send_counts"], st["send_offsets"], st["send_tok"],
+                          st["send_row"], st["expand_idx"], st["x_send"], ews)
     torch.cuda.synchronize()
 
     # then call the C ABI directly with the pointers (no per-call Python checks)
@@ -187,9 +203,14 @@ def main():
             route_dispatch=(P(st["x"]), P(gw), P(bias), N, H, E, K, dt, P(st["ids"]),
                             P(st["w"]), P(st["counts"]), P(st["offsets"]), P(st["perm"]),
                             P(st["inv"]), P(st["x_perm"]), P(fws), fws.numel(), sp),
-            combine=(P(st["y"]), P(st["inv"]), P(st["w"]), N, H, K, dt, P(st["out"]), sp)))
+            combine=(P(st["y"]), P(st["inv"]), P(st["w"]), N, H, K, dt, P(st["out"]), sp),
+            ep_dispatch=(P(st["ids"]), P(st["x"]), N, H, E, K, R, dt, P(st["counts"]),
+                         P(st["offsets"]), P(st["perm"]), P(st["inv"]), P(st["send_counts"]),
+                         P(st["send_offsets"]), P(st["send_tok"]), P(st["send_row"]),
+                         P(st["expand_idx"]), P(st["x_send"]), P(ews), ews.numel(), sp)))
     fn = {"route": lib.moe_route, "dispatch": lib.moe_dispatch,
-          "route_dispatch": lib.moe_route_dispatch, "combine": lib.moe_combine}
+          "route_dispatch": lib.moe_route_dispatch, "combine": lib.moe_combine,
+          "ep_dispatch": lib.moe_ep_dispatch}
 
     def call(name, i):
         status = fn[name](*calls[i % N_SETS][name])
@@ -230,7 +251,7 @@ def main():
     # input sets) between one pair of HIP events on the launch stream: the
     # average duration of one call
     stage_ms = {}
-    for name in ("route_dispatch", "combine", "route", "dispatch"):
+    for name in ("route_dispatch", "combine", "route", "dispatch", "ep_dispatch"):
         for i in range(3):
             call(name, i)
         _, ms = timed(lambda i, n=name: call(n, i), args.steps)
@@ -248,6 +269,12 @@ def main():
 
     alg = algorithmic_bytes(N, H, E, K, b)
     alg["route_dispatch"] = alg["route"] + alg["dispatch"]
+    # ep_dispatch: ids in, x read once, S deduplicated rows out, the expert
+    # metadata (counts, offsets, perm, inv) and the send metadata (send
+    # counts/offsets, send_tok [S], send_row and expand_idx [N*K])
+    S = int(sets[0]["send_offsets"][R].item())
+    alg["ep_dispatch"] = (T * 4 + N * H * b + S * H * b + (2 * E + 1) * 4 + 2 * T * 4
+                          + (2 * R + 1) * 4 + S * 4 + 2 * T * 4)
     stages = {}
     for k, ms in stage_ms.items():
         stages[k] = {"ms_per_call": round(ms, 5), "alg_MB": round(alg[k] / 1e6, 3),
@@ -261,6 +288,7 @@ def main():
             "ms_per_call": round(marg, 5), "alg_MB": round(alg["dispatch"] / 1e6, 3),
             "alg_GBs": round(alg["dispatch"] / marg / 1e6, 1),
             "hbm_frac": round(alg["dispatch"] / marg / 1e6 / HBM_PEAK_GBS, 4)}
+    stages["ep_dispatch"].update(ep_size=R, send_rows=S, slots=T)
     r_flops = 2.0 * N * H * E
     stages["route"]["mfma_util"] = round(
         r_flops / (stage_ms["route"] * 1e-3) / (BF16_MFMA_PEAK_TFLOPS * 1e12), 4)

@@ -29,6 +29,9 @@
  *      sort 替代 O(n log n) argsort).
  *  [A] same page, section 6.1 "Model protocol first" (6.1 模型协议先行),
  *      forward_aggregate.
+ *  [P] same page, section 8.2, fused_dedup_prepare_dispatch: per-expert and
+ *      per-rank counts, prefix sums and send metadata, deduplicated scatter
+ *      with a counting sort and the receivers' expand index.
  */
 #ifndef MOE_H_
 #define MOE_H_
@@ -150,6 +153,43 @@ moe_status_t moe_route_dispatch(const void *x, const void *gate_w, const float *
                                 int32_t *counts, int32_t *offsets, int32_t *perm,
                                 int32_t *inv, void *x_perm, void *workspace,
                                 size_t workspace_bytes, void *stream);
+
+/*
+ * Bytes of device workspace moe_ep_dispatch needs (0 for invalid sizes).
+ */
+size_t moe_ep_dispatch_workspace_size(int64_t N, int32_t E, int32_t K, int32_t ep_size);
+
+/*
+ * moe_ep_dispatch -- the expert-parallel send metadata of [P] on one GPU,
+ * with ep_size = R ranks of E/R consecutive experts (expert e lives on rank
+ * e / (E/R)) simulated as segments of one send buffer.  A token is sent once
+ * to each distinct rank among its K experts; the send buffer is rank-major,
+ * tokens ascending inside a rank.
+ *   counts, offsets, perm, inv     exactly as moe_dispatch (expert level)
+ *   send_counts [R]     int32 out  tokens sent to rank r (deduplicated)
+ *   send_offsets [R+1]  int32 out  exclusive prefix sums; S = send_offsets[R]
+ *   send_tok [N*min(K,R)] int32 out  token of send row j (j < S; the rest is
+ *                                  not written)
+ *   send_row [N*K]      int32 out  send row of token i/K for the rank of
+ *                                  ids[i] (slots sharing a rank share it)
+ *   expand_idx [N*K]    int32 out  for dispatched row p (expert-contiguous
+ *                                  order): the row of the receiving rank's
+ *                                  segment holding its token, counted from
+ *                                  send_offsets[rank];  so
+ *                                  x_perm[p] = x_send[send_offsets[r] + expand_idx[p]]
+ *   x_send [N*min(K,R), H] dtype out, or NULL: x_send[j] = x[send_tok[j]]
+ *   workspace >= moe_ep_dispatch_workspace_size(N, E, K, ep_size); scratch
+ * INVALID_ARGUMENT also when ep_size < 1 or E % ep_size != 0.  Preconditions
+ * and the treatment of ids outside [0,E) are those of moe_dispatch (such a
+ * slot gets send_row = -1; expand_idx rows past offsets[E] are -1).
+ * N == 0 is a valid call: the counts and offsets are zero-filled.
+ */
+moe_status_t moe_ep_dispatch(const int32_t *topk_ids, const void *x, int64_t N, int32_t H,
+                             int32_t E, int32_t K, int32_t ep_size, moe_dtype_t dtype,
+                             int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv,
+                             int32_t *send_counts, int32_t *send_offsets, int32_t *send_tok,
+                             int32_t *send_row, int32_t *expand_idx, void *x_send,
+                             void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * moe_combine -- the weighted combine of [A] (forward_aggregate without the

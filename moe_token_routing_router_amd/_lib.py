@@ -27,7 +27,8 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARGUMENT", 2: "MOE_ERR_UNSUPPORTED",
 
 EXPORTS = ("moe_status_string", "moe_route_workspace_size", "moe_route",
            "moe_dispatch_workspace_size", "moe_dispatch", "moe_route_dispatch_workspace_size",
-           "moe_route_dispatch", "moe_combine")
+           "moe_route_dispatch", "moe_ep_dispatch_workspace_size", "moe_ep_dispatch",
+           "moe_combine")
 
 
 class MoeError(RuntimeError):
@@ -65,6 +66,11 @@ def library() -> ctypes.CDLL:
         lib.moe_route_dispatch.argtypes = [P, P, P, i64, i32, i32, i32, ctypes.c_int, P, P, P, P,
                                            P, P, P, P, sz, P]
         lib.moe_route_dispatch.restype = ctypes.c_int
+        lib.moe_ep_dispatch_workspace_size.argtypes = [i64, i32, i32, i32]
+        lib.moe_ep_dispatch_workspace_size.restype = sz
+        lib.moe_ep_dispatch.argtypes = [P, P, i64, i32, i32, i32, i32, ctypes.c_int, P, P, P, P,
+                                        P, P, P, P, P, P, P, sz, P]
+        lib.moe_ep_dispatch.restype = ctypes.c_int
         lib.moe_combine.argtypes = [P, P, P, i64, i32, i32, ctypes.c_int, P, P]
         lib.moe_combine.restype = ctypes.c_int
         _lib = lib
@@ -121,6 +127,10 @@ def moe_dispatch_workspace_size(N: int, E: int, K: int) -> int:
 
 def moe_route_dispatch_workspace_size(N: int, H: int, E: int, K: int, dtype: torch.dtype) -> int:
     return int(library().moe_route_dispatch_workspace_size(N, H, E, K, _dtype_code(dtype)))
+
+
+def moe_ep_dispatch_workspace_size(N: int, E: int, K: int, ep_size: int) -> int:
+    return int(library().moe_ep_dispatch_workspace_size(N, E, K, ep_size))
 
 
 # ------------------------------------------------------------------ calls
@@ -202,6 +212,38 @@ def moe_route_dispatch(x: torch.Tensor, gate_w: torch.Tensor, bias: Optional[tor
         _stream(dev)))
 
 
+def moe_ep_dispatch(topk_ids: torch.Tensor, x: Optional[torch.Tensor], E: int, ep_size: int,
+                    counts: torch.Tensor, offsets: torch.Tensor, perm: torch.Tensor,
+                    inv: torch.Tensor, send_counts: torch.Tensor, send_offsets: torch.Tensor,
+                    send_tok: torch.Tensor, send_row: torch.Tensor, expand_idx: torch.Tensor,
+                    x_send: Optional[torch.Tensor], workspace: torch.Tensor,
+                    H: Optional[int] = None, dtype: Optional[torch.dtype] = None) -> None:
+    """Expert-parallel send metadata of topk_ids [N,K] for ep_size ranks
+    (see include/moe.h); x_send [N*min(K,ep_size), H] rows of x if given."""
+    N, K = topk_ids.shape
+    dev = topk_ids.device
+    if x is not None:
+        H = x.shape[1]
+        dtype = x.dtype
+    if H is None or dtype is None:
+        raise ValueError("H and dtype are needed when x is None")
+    cap = N * min(K, ep_size)
+    _check("moe_ep_dispatch", library().moe_ep_dispatch(
+        _dev(topk_ids, "topk_ids", torch.int32, N * K, dev),
+        _dev(x, "x", dtype, N * H, dev), N, H, E, K, ep_size, _dtype_code(dtype),
+        _dev(counts, "counts", torch.int32, E, dev),
+        _dev(offsets, "offsets", torch.int32, E + 1, dev),
+        _dev(perm, "perm", torch.int32, N * K, dev), _dev(inv, "inv", torch.int32, N * K, dev),
+        _dev(send_counts, "send_counts", torch.int32, ep_size, dev),
+        _dev(send_offsets, "send_offsets", torch.int32, ep_size + 1, dev),
+        _dev(send_tok, "send_tok", torch.int32, cap, dev),
+        _dev(send_row, "send_row", torch.int32, N * K, dev),
+        _dev(expand_idx, "expand_idx", torch.int32, N * K, dev),
+        _dev(x_send, "x_send", dtype, cap * H, dev),
+        _dev(workspace, "workspace", torch.uint8, workspace.numel(), dev), workspace.numel(),
+        _stream(dev)))
+
+
 def moe_combine(y: torch.Tensor, inv: torch.Tensor, topk_w: torch.Tensor,
                 out: torch.Tensor) -> None:
     """Weighted combine: out [N,H] = sum_k topk_w[n,k] * y[inv[n*K+k]], with
@@ -267,6 +309,31 @@ def route_dispatch(x: torch.Tensor, gate_w: torch.Tensor, K: int,
                      dtype=torch.uint8, device=dev)
     moe_route_dispatch(x, gate_w, bias, K, ids, w, counts, offsets, perm, inv, x_perm, ws)
     return ids, w, counts, offsets, perm, inv, x_perm
+
+
+def ep_dispatch(topk_ids: torch.Tensor, x: Optional[torch.Tensor], E: int, ep_size: int,
+                with_rows: bool = True):
+    """Allocate outputs and run moe_ep_dispatch; returns (counts, offsets,
+    perm, inv, send_counts, send_offsets, send_tok, send_row, expand_idx,
+    x_send-or-None); send_tok and x_send have N*min(K, ep_size) rows, of
+    which the first send_offsets[ep_size] are written."""
+    N, K = topk_ids.shape
+    dev = topk_ids.device
+    cap = N * min(K, ep_size)
+    i32 = dict(dtype=torch.int32, device=dev)
+    counts, offsets = torch.empty((E,), **i32), torch.empty((E + 1,), **i32)
+    perm, inv = torch.empty((N * K,), **i32), torch.empty((N * K,), **i32)
+    send_counts, send_offsets = torch.empty((ep_size,), **i32), torch.empty((ep_size + 1,), **i32)
+    send_tok = torch.empty((cap,), **i32)
+    send_row, expand_idx = torch.empty((N * K,), **i32), torch.empty((N * K,), **i32)
+    x_send = torch.empty((cap, x.shape[1]), dtype=x.dtype, device=dev) if with_rows else None
+    ws = torch.empty((max(1, moe_ep_dispatch_workspace_size(N, E, K, ep_size)),),
+                     dtype=torch.uint8, device=dev)
+    moe_ep_dispatch(topk_ids, x if with_rows else None, E, ep_size, counts, offsets, perm, inv,
+                    send_counts, send_offsets, send_tok, send_row, expand_idx, x_send, ws,
+                    H=None if with_rows else 8, dtype=None if with_rows else torch.bfloat16)
+    return (counts, offsets, perm, inv, send_counts, send_offsets, send_tok, send_row,
+            expand_idx, x_send)
 
 
 def combine(y: torch.Tensor, inv: torch.Tensor, topk_w: torch.Tensor) -> torch.Tensor:

@@ -81,10 +81,12 @@ moe_status_t moe_route(const void* x, const void* gate_w, const float* bias, int
 namespace {
 
 // dispatch scratch: bhist [E][blocks of bt tokens] then lrank [N*K]
+size_t bhist_bytes(int64_t N, int32_t E, int bt) {
+  return round_up((size_t)moe::dispatch_num_blocks(N, bt) * (size_t)E * sizeof(int32_t), 256);
+}
+
 size_t dispatch_scratch_bytes(int64_t N, int32_t E, int32_t K, int bt) {
-  const int64_t nb = moe::dispatch_num_blocks(N, bt);
-  return round_up((size_t)nb * (size_t)E * sizeof(int32_t), 256) +
-         round_up((size_t)N * (size_t)K * sizeof(int32_t), 256);
+  return bhist_bytes(N, E, bt) + round_up((size_t)N * (size_t)K * sizeof(int32_t), 256);
 }
 
 moe_status_t check_dispatch_outputs(int64_t N, int32_t H, int32_t E, int32_t K,
@@ -193,6 +195,72 @@ moe_status_t moe_route_dispatch(const void* x, const void* gate_w, const float* 
   return from_hip(moe::launch_dispatch_finish(topk_ids, x, N, (int64_t)H * elem_bytes(dtype), E, K,
                                               bt, counts, offsets, perm, inv, x_perm, lrank,
                                               bhist, s));
+}
+
+size_t moe_ep_dispatch_workspace_size(int64_t N, int32_t E, int32_t K, int32_t ep_size) {
+  if (N < 0 || E <= 0 || E > moe::kMaxExperts || K < 1 || ep_size < 1 || E % ep_size != 0)
+    return 0;
+  // dispatch scratch (shared by the expert- and the rank-level passes), then
+  // the rank keys and the owner slots' send rows
+  return dispatch_scratch_bytes(N, E, K, moe::dispatch_count_tokens(K)) +
+         2 * round_up((size_t)N * (size_t)K * sizeof(int32_t), 256);
+}
+
+moe_status_t moe_ep_dispatch(const int32_t* topk_ids, const void* x, int64_t N, int32_t H,
+                             int32_t E, int32_t K, int32_t ep_size, moe_dtype_t dtype,
+                             int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
+                             int32_t* send_counts, int32_t* send_offsets, int32_t* send_tok,
+                             int32_t* send_row, int32_t* expand_idx, void* x_send,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  if (!valid_dtype(dtype) || N < 0 || H <= 0 || E <= 0 || K < 1 || K > E || ep_size < 1 ||
+      E % ep_size != 0)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (N > 0 && (!topk_ids || !workspace)) return MOE_ERR_INVALID_ARGUMENT;
+  if (!send_counts || !send_offsets) return MOE_ERR_INVALID_ARGUMENT;
+  if (N > 0 && (!send_tok || !send_row || !expand_idx)) return MOE_ERR_INVALID_ARGUMENT;
+  if (N > 0 && x_send && !x) return MOE_ERR_INVALID_ARGUMENT;
+  moe_status_t st = check_dispatch_outputs(N, H, E, K, dtype, x, counts, offsets, perm, inv,
+                                           nullptr);
+  if (st != MOE_OK) return st;
+  if (!aligned(topk_ids, 4) || !aligned(send_counts, 4) || !aligned(send_offsets, 4) ||
+      !aligned(send_tok, 4) || !aligned(send_row, 4) || !aligned(expand_idx, 4) ||
+      !aligned(x_send, 16) || !aligned(workspace, 16))
+    return MOE_ERR_MISALIGNED;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (N == 0) {
+    st = zero_counts_offsets(counts, offsets, E, s);
+    if (st != MOE_OK) return st;
+    return zero_counts_offsets(send_counts, send_offsets, ep_size, s);
+  }
+  if (workspace_bytes < moe_ep_dispatch_workspace_size(N, E, K, ep_size))
+    return MOE_ERR_WORKSPACE_TOO_SMALL;
+  const int64_t T = N * K;
+  const int bt = moe::dispatch_count_tokens(K);
+  char* base = reinterpret_cast<char*>(workspace);
+  int32_t* bhist = reinterpret_cast<int32_t*>(base);
+  int32_t* lrank = reinterpret_cast<int32_t*>(base + bhist_bytes(N, E, bt));
+  int32_t* keys = reinterpret_cast<int32_t*>(base + dispatch_scratch_bytes(N, E, K, bt));
+  int32_t* owner_row = reinterpret_cast<int32_t*>(
+      base + dispatch_scratch_bytes(N, E, K, bt) + round_up((size_t)T * sizeof(int32_t), 256));
+  const int64_t row_bytes = (int64_t)H * elem_bytes(dtype);
+  // expert level: counts, offsets, perm, inv (no rows)
+  hipError_t e = moe::launch_dispatch_count(topk_ids, N, E, K, lrank, bhist, s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  e = moe::launch_dispatch_finish(topk_ids, nullptr, N, row_bytes, E, K, bt, counts, offsets,
+                                  perm, inv, nullptr, lrank, bhist, s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  // rank level on the deduplicated keys: send counts/offsets, send slots (in
+  // send_tok), owner rows, and the rows themselves
+  e = moe::launch_ep_keys(topk_ids, N, K, E, E / ep_size, keys, s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  e = moe::launch_dispatch_count(keys, N, ep_size, K, lrank, bhist, s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  e = moe::launch_dispatch_finish(keys, x, N, row_bytes, ep_size, K, bt, send_counts,
+                                  send_offsets, send_tok, owner_row, x_send, lrank, bhist,
+                                  N * (int64_t)(K < ep_size ? K : ep_size), s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  return from_hip(moe::launch_ep_finish(topk_ids, perm, offsets, owner_row, send_offsets, N, K, E,
+                                        ep_size, send_tok, send_row, expand_idx, s));
 }
 
 moe_status_t moe_combine(const void* y, const int32_t* inv, const float* topk_w, int64_t N,

@@ -133,14 +133,13 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
     const int32_t* __restrict__ bhist, const int32_t* __restrict__ lrank, int64_t N, int K,
     int E, int nb, int bt, int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
     int32_t* __restrict__ inv, const u32x4* __restrict__ x, u32x4* __restrict__ x_perm,
-    int row_vecs) {
+    int row_vecs, int64_t dlim) {
   extern __shared__ int dst[];  // [kScatterTokens*K]
   __shared__ int off[kMaxExperts];
   __shared__ int scan_lds[4];
   const int tid = threadIdx.x;
   const int64_t n0 = (int64_t)blockIdx.x * kScatterTokens;
   const int ntok = (int)min((int64_t)kScatterTokens, N - n0);
-  const int64_t T = N * K;
 
   constexpr int U = MOE_SCATTER_U;
   const int total = ntok * row_vecs;
@@ -176,7 +175,7 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
     if ((unsigned)e < (unsigned)E) {
       const int64_t b = (slot / K) / bt;
       const int64_t dd = (int64_t)off[e] + bhist[(int64_t)e * nb + b] + lrank[slot];
-      if (dd >= 0 && dd < T) {  // always true for consistent inputs
+      if (dd >= 0 && dd < dlim) {  // always true for consistent inputs
         d = (int)dd;
         perm[d] = (int32_t)slot;
       }
@@ -229,6 +228,15 @@ hipError_t launch_dispatch_finish(const int32_t* ids, const void* x, int64_t N, 
                                   int E, int K, int bt, int32_t* counts, int32_t* offsets,
                                   int32_t* perm, int32_t* inv, void* x_perm,
                                   const int32_t* lrank, int32_t* bhist, hipStream_t s) {
+  return launch_dispatch_finish(ids, x, N, row_bytes, E, K, bt, counts, offsets, perm, inv, x_perm,
+                                lrank, bhist, N * K, s);
+}
+
+hipError_t launch_dispatch_finish(const int32_t* ids, const void* x, int64_t N, int64_t row_bytes,
+                                  int E, int K, int bt, int32_t* counts, int32_t* offsets,
+                                  int32_t* perm, int32_t* inv, void* x_perm,
+                                  const int32_t* lrank, int32_t* bhist, int64_t dlim,
+                                  hipStream_t s) {
   const int nb = (int)dispatch_num_blocks(N, bt);
   hipLaunchKernelGGL(dispatch_scan_kernel, dim3(E), dim3(256), 0, s, bhist, nb, counts);
   hipError_t err = hipGetLastError();
@@ -238,7 +246,7 @@ hipError_t launch_dispatch_finish(const int32_t* ids, const void* x, int64_t N, 
   hipLaunchKernelGGL(dispatch_scatter_kernel, dim3((unsigned)blocks), dim3(256), dyn, s, ids,
                      counts, bhist, lrank, N, K, E, nb, bt, offsets, perm, inv,
                      reinterpret_cast<const u32x4*>(x), reinterpret_cast<u32x4*>(x_perm),
-                     (int)(row_bytes / 16));
+                     (int)(row_bytes / 16), dlim);
   return hipGetLastError();
 }
 

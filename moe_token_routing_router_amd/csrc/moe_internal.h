@@ -139,6 +139,23 @@ hipError_t launch_dispatch_finish(const int32_t* ids, const void* x, int64_t N, 
                                   int E, int K, int bt, int32_t* counts, int32_t* offsets,
                                   int32_t* perm, int32_t* inv, void* x_perm,
                                   const int32_t* lrank, int32_t* bhist, hipStream_t s);
+// ... with destinations limited to [0, dlim) (perm, x_perm capacity; N*K above)
+hipError_t launch_dispatch_finish(const int32_t* ids, const void* x, int64_t N, int64_t row_bytes,
+                                  int E, int K, int bt, int32_t* counts, int32_t* offsets,
+                                  int32_t* perm, int32_t* inv, void* x_perm,
+                                  const int32_t* lrank, int32_t* bhist, int64_t dlim,
+                                  hipStream_t s);
+
+// Expert-parallel metadata (ep.hip).  keys[i] = rank of ids[i] if slot i is
+// the first of its token on that rank, else -1 (invalid ids: -1).
+hipError_t launch_ep_keys(const int32_t* ids, int64_t N, int K, int E, int per_rank,
+                          int32_t* keys, hipStream_t s);
+// send_tok holds send slots on entry (from the rank-keyed scatter) and
+// tokens on exit; owner_row[i] is the send row of owner slot i (-1 otherwise).
+hipError_t launch_ep_finish(const int32_t* ids, const int32_t* perm, const int32_t* offsets,
+                            const int32_t* owner_row, const int32_t* send_offsets, int64_t N,
+                            int K, int E, int R, int32_t* send_tok, int32_t* send_row,
+                            int32_t* expand_idx, hipStream_t s);
 
 // Combine.
 hipError_t launch_combine(const void* y, const int32_t* inv, const float* w, int64_t N, int H,

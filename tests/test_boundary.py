@@ -143,6 +143,34 @@ def test_route_dispatch_validation(lib):
     assert route_dispatch(lib, wsb=64) == WS_SMALL
 
 
+def ep(lib, ids=A, x=A, N=4, H=16, E=8, K=2, R=2, dt=BF16, counts=A2, offsets=A2, perm=A2,
+       inv=A2, sc=A2, so=A2, st=A2, sr=A2, ex=A2, xs=A, ws=A, wsb=1 << 20):
+    return lib.moe_ep_dispatch(ids, x, N, H, E, K, R, dt, counts, offsets, perm, inv, sc, so, st,
+                               sr, ex, xs, ws, wsb, None)
+
+
+def test_ep_dispatch_validation(lib):
+    assert ep(lib, R=3) == INVALID             # E % ep_size != 0
+    assert ep(lib, R=0) == INVALID
+    assert ep(lib, K=9) == INVALID
+    assert ep(lib, sc=None) == INVALID
+    assert ep(lib, so=None) == INVALID
+    assert ep(lib, ex=None) == INVALID
+    assert ep(lib, st=None) == INVALID
+    assert ep(lib, x=None) == INVALID          # rows asked for without x
+    assert ep(lib, ws=None) == INVALID
+    assert ep(lib, E=300, R=2) == UNSUPPORTED
+    assert ep(lib, H=4) == UNSUPPORTED
+    assert ep(lib, xs=MIS8) == MISALIGNED
+    assert ep(lib, st=MIS) == MISALIGNED
+    assert ep(lib, wsb=8) == WS_SMALL
+    # sizes: the dispatch scratch plus the rank keys and owner rows
+    for N, E, K, R in ((16384, 64, 2, 8), (17, 6, 2, 3), (32768, 128, 8, 8)):
+        n = lib.moe_ep_dispatch_workspace_size(N, E, K, R)
+        assert n >= lib.moe_dispatch_workspace_size(N, E, K) + 2 * N * K * 4 and n % 256 == 0
+    assert lib.moe_ep_dispatch_workspace_size(16, 6, 2, 4) == 0
+
+
 def combine(lib, y=A, inv=A2, w=A2, N=4, H=16, K=2, dt=BF16, out=A):
     return lib.moe_combine(y, inv, w, N, H, K, dt, out, None)
 

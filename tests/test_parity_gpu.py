@@ -305,3 +305,70 @@ def test_route_dispatch_empty():
     ids, w, counts, offsets, perm, inv, xp = L.route_dispatch(x, gw, 2)
     torch.cuda.synchronize()
     assert (counts == 0).all() and (offsets == 0).all() and xp.shape == (0, 64)
+
+
+# ------------------------------------------------------------ expert-parallel metadata
+
+EP_CASES = [
+    # (N, H, E, K, ep_size, dtype, skew)
+    (16384, 4096, 64, 2, 8, "bf16", 0.0),    # headline shape over 8 ranks
+    (32768, 2048, 128, 8, 8, "bf16", 1.1),   # 8 experts per token over 8 ranks: heavy sharing
+    (4096, 2048, 64, 4, 4, "bf16", 0.5),
+    (1000, 264, 32, 2, 32, "f32", 0.0),      # one expert per rank: nothing to deduplicate
+    (777, 64, 48, 6, 1, "bf16", 0.0),        # one rank: every token once
+    (1, 8, 4, 4, 2, "bf16", 0.0),
+    (129, 520, 256, 16, 16, "bf16", 0.0),    # E and K at their limits
+    (3001, 64, 48, 4, 12, "bf16", 4.0),      # skewed: empty experts and ranks
+]
+
+
+def _ep_check(ids, x, E, R, dtype):
+    N, K = ids.shape
+    res = L.ep_dispatch(torch.from_numpy(np.ascontiguousarray(ids)).cuda(), to_dev(x, dtype), E, R)
+    torch.cuda.synchronize()
+    gc, go, gp, gi, gsc, gso, gst, gsr, gex, gxs = [from_dev(t) for t in res]
+    oc, oo, op, oi = O.dispatch(ids, E)
+    sc, so, st, sr, ex = O.ep_dispatch(ids, E, R)
+    for a, b in ((gc, oc), (go, oo), (gp, op), (gi, oi), (gsc, sc), (gso, so), (gsr, sr), (gex, ex)):
+        np.testing.assert_array_equal(a, b)
+    S = int(so[R])
+    np.testing.assert_array_equal(gst[:S], st)
+    np.testing.assert_array_equal(gxs[:S].view(np.uint8), x[st].view(np.uint8))
+    # receivers rebuild exactly the dispatched rows
+    ranks = ids.ravel()[op] // (E // R)
+    np.testing.assert_array_equal(gxs[so[ranks] + gex].view(np.uint8),
+                                  O.permute_rows(x, op, K).view(np.uint8))
+
+
+@pytest.mark.parametrize("N,H,E,K,R,dtype,skew", EP_CASES)
+def test_ep_dispatch_bit_exact(N, H, E, K, R, dtype, skew):
+    print(f"[ep] N={N} H={H} E={E} K={K} R={R} {dtype} skew={skew}", flush=True)
+    ids = I.random_ids(N + R, N, E, K, skew=skew)
+    x = I.random_case(N + R, N, H, 4, 1, dtype, with_y=False)["x"]
+    _ep_check(ids, x, E, R, dtype)
+
+
+def test_ep_dispatch_of_routed_ids():
+    # the ids the fused router picks on the biased workload, over 16 ranks
+    d = workload("biased-bf16")
+    print("[ep] routed ids of biased-bf16, 16 ranks", flush=True)
+    _ep_check(d["o"]["ids"], d["x"], d["E"], 16, d["dtype"])
+
+
+def test_ep_dispatch_out_of_range_ids():
+    N, H, E, K, R = 50, 64, 8, 3, 4
+    ids = I.random_ids(9, N, E, K)
+    ids[4, 1] = -1
+    ids[7, 2] = E
+    x = I.random_case(9, N, H, 4, 1, "bf16", with_y=False)["x"]
+    res = L.ep_dispatch(torch.from_numpy(ids).cuda(), to_dev(x, "bf16"), E, R)
+    torch.cuda.synchronize()
+    gc, go, gp, gi, gsc, gso, gst, gsr, gex, gxs = [from_dev(t) for t in res]
+    valid = ((ids >= 0) & (ids < E)).ravel()
+    np.testing.assert_array_equal(gc, np.bincount(ids.ravel()[valid], minlength=E))
+    assert gsr[4 * K + 1] == -1 and gsr[7 * K + 2] == -1
+    assert (gex[go[E]:] == -1).all()
+    pairs = {(i // K, int(e) // (E // R)) for i, e in enumerate(ids.ravel()) if valid[i]}
+    np.testing.assert_array_equal(gsc, np.bincount([r for _, r in pairs], minlength=R))
+    slots = np.nonzero(valid)[0]
+    np.testing.assert_array_equal(gxs[gsr[slots]], x[slots // K])
