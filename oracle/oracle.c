@@ -343,6 +343,168 @@ int oracle_combine(const void *y, const int32_t *inv, const float *w, int64_t N,
   return 0;
 }
 
+/* ---- backward of the path ([A] 6.2: the stages run backward in training) */
+
+static void store_elem(void *base, int64_t idx, int dtype, double v) {
+  if (dtype == ORACLE_BF16)
+    ((uint16_t *)base)[idx] = double_to_bf16(v);
+  else
+    ((float *)base)[idx] = (float)v;
+}
+
+/*
+ * oracle_combine_backward: the gradient of out[n,:] = sum_k w[n,k] *
+ * y[inv[n*K+k],:] for an upstream gradient dout [N,H]:
+ *   dy[inv[n*K+k], h] = round( w[n,k] * dout[n,h] )        (rows of y)
+ *   dw[n,k]           = sum_h dout[n,h] * y[inv[n*K+k], h]  (h ascending, fp32)
+ * Every row of dy is written once (inv is a permutation of [0, N*K)).
+ */
+int oracle_combine_backward(const void *dout, const void *y, const int32_t *inv,
+                            const float *w, int64_t N, int32_t H, int32_t K,
+                            int32_t dtype, void *dy, float *dw) {
+  if (N < 0 || H <= 0 || K < 1) return -1;
+  if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return -1;
+  const int64_t T = N * (int64_t)K;
+  for (int64_t n = 0; n < N; ++n) {
+    for (int32_t k = 0; k < K; ++k) {
+      const int64_t row = inv[n * K + k];
+      if (row < 0 || row >= T) return -1;
+      double acc = 0.0;
+      for (int32_t h = 0; h < H; ++h) {
+        const double g = load_elem(dout, n * (int64_t)H + h, dtype);
+        acc += g * load_elem(y, row * H + h, dtype);
+        store_elem(dy, row * H + h, dtype, (double)w[n * K + k] * g);
+      }
+      dw[n * K + k] = (float)acc;
+    }
+  }
+  return 0;
+}
+
+/*
+ * oracle_dispatch_backward: the gradient of x_perm[inv[n*K+k],:] = x[n,:]:
+ *   dx[n,h] = round( sum_k dx_perm[inv[n*K+k], h] )   (k ascending)
+ */
+int oracle_dispatch_backward(const void *dx_perm, const int32_t *inv, int64_t N,
+                             int32_t H, int32_t K, int32_t dtype, void *dx) {
+  if (N < 0 || H <= 0 || K < 1) return -1;
+  if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return -1;
+  const int64_t T = N * (int64_t)K;
+  for (int64_t n = 0; n < N; ++n) {
+    for (int32_t h = 0; h < H; ++h) {
+      double acc = 0.0;
+      for (int32_t k = 0; k < K; ++k) {
+        const int64_t row = inv[n * K + k];
+        if (row < 0 || row >= T) return -1;
+        acc += load_elem(dx_perm, row * H + h, dtype);
+      }
+      store_elem(dx, n * (int64_t)H + h, dtype, acc);
+    }
+  }
+  return 0;
+}
+
+/*
+ * oracle_route_backward: the gradient of the router's weights w [N,K] (for
+ * the given selection ids) with respect to its inputs, for an upstream
+ * gradient dw [N,K], by the chain rule through the two steps of [R]'s gate:
+ *   p = softmax over all E experts of l = x @ gate_w (+ bias):
+ *       dl[e] = p[e] * (dp[e] - sum_a dp[a] p[a])
+ *   w[k] = p[ids[k]] / s, s = sum_j p[ids[j]]  (renormalisation):
+ *       dp[a] = [a kept] dw[k(a)] / s - sum_k dw[k] p[ids[k]] / s^2
+ * with l, p, s recomputed in double from x, gate_w and bias.  Then
+ *   dgate_w[h,e] = sum_n x[n,h] dl[n,e]         (fp32 out)
+ *   dbias[e]     = sum_n dl[n,e]                (fp32 out, may be NULL)
+ *   dx[n,h]      = round( sum_k dx_perm[inv[n*K+k],h] + sum_e dl[n,e] gate_w[h,e] )
+ * where the first term (the dispatch backward) is left out when dx_perm is
+ * NULL.  dlogits [N,E] (double) may be NULL.
+ */
+int oracle_route_backward(const void *x, const void *gate_w, const float *bias,
+                          const int32_t *ids, const float *dw, const void *dx_perm,
+                          const int32_t *inv, int64_t N, int32_t H, int32_t E,
+                          int32_t K, int32_t dtype, double *dlogits, float *dgate_w,
+                          float *dbias, void *dx) {
+  if (N < 0 || H <= 0 || E <= 0 || K < 1 || K > E) return -1;
+  if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return -1;
+  const int64_t T = N * (int64_t)K;
+  double *l = (double *)malloc(sizeof(double) * (size_t)E);
+  double *p = (double *)malloc(sizeof(double) * (size_t)E);
+  double *dp = (double *)malloc(sizeof(double) * (size_t)E);
+  double *dl = (double *)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1) * (size_t)E);
+  double *gacc = (double *)calloc((size_t)H * (size_t)E, sizeof(double));
+  double *bacc = (double *)calloc((size_t)E, sizeof(double));
+  int rc = -1;
+  if (!l || !p || !dp || !dl || !gacc || !bacc) goto done;
+  for (int64_t n = 0; n < N; ++n) {
+    for (int32_t e = 0; e < E; ++e) l[e] = 0.0;
+    for (int32_t h = 0; h < H; ++h) {
+      const double xv = load_elem(x, n * (int64_t)H + h, dtype);
+      for (int32_t e = 0; e < E; ++e) l[e] += xv * load_elem(gate_w, (int64_t)h * E + e, dtype);
+    }
+    if (bias)
+      for (int32_t e = 0; e < E; ++e) l[e] += (double)bias[e];
+    double mx = l[0];
+    for (int32_t e = 1; e < E; ++e)
+      if (l[e] > mx) mx = l[e];
+    double z = 0.0;
+    for (int32_t e = 0; e < E; ++e) {
+      p[e] = exp(l[e] - mx);
+      z += p[e];
+    }
+    for (int32_t e = 0; e < E; ++e) p[e] /= z;
+    double s = 0.0, t = 0.0;
+    for (int32_t k = 0; k < K; ++k) {
+      const int32_t e = ids[n * K + k];
+      if (e < 0 || e >= E) goto done;
+      s += p[e];
+    }
+    for (int32_t k = 0; k < K; ++k) t += (double)dw[n * K + k] * p[ids[n * K + k]];
+    /* back through the renormalisation */
+    for (int32_t e = 0; e < E; ++e) dp[e] = 0.0;
+    for (int32_t k = 0; k < K; ++k) dp[ids[n * K + k]] = (double)dw[n * K + k] / s - t / (s * s);
+    /* back through the softmax */
+    double u = 0.0;
+    for (int32_t a = 0; a < E; ++a) u += dp[a] * p[a];
+    for (int32_t e = 0; e < E; ++e) dl[n * E + e] = p[e] * (dp[e] - u);
+  }
+  for (int64_t n = 0; n < N; ++n) {
+    for (int32_t h = 0; h < H; ++h) {
+      const double xv = load_elem(x, n * (int64_t)H + h, dtype);
+      for (int32_t e = 0; e < E; ++e) gacc[(int64_t)h * E + e] += xv * dl[n * E + e];
+    }
+    for (int32_t e = 0; e < E; ++e) bacc[e] += dl[n * E + e];
+  }
+  for (int64_t i = 0; i < (int64_t)H * E; ++i) dgate_w[i] = (float)gacc[i];
+  if (dbias)
+    for (int32_t e = 0; e < E; ++e) dbias[e] = (float)bacc[e];
+  for (int64_t n = 0; n < N; ++n) {
+    for (int32_t h = 0; h < H; ++h) {
+      double acc = 0.0;
+      if (dx_perm) {
+        for (int32_t k = 0; k < K; ++k) {
+          const int64_t row = inv[n * K + k];
+          if (row < 0 || row >= T) goto done;
+          acc += load_elem(dx_perm, row * (int64_t)H + h, dtype);
+        }
+      }
+      for (int32_t e = 0; e < E; ++e)
+        acc += dl[n * E + e] * load_elem(gate_w, (int64_t)h * E + e, dtype);
+      store_elem(dx, n * (int64_t)H + h, dtype, acc);
+    }
+  }
+  if (dlogits)
+    for (int64_t i = 0; i < N * (int64_t)E; ++i) dlogits[i] = dl[i];
+  rc = 0;
+done:
+  free(l);
+  free(p);
+  free(dp);
+  free(dl);
+  free(gacc);
+  free(bacc);
+  return rc;
+}
+
 /* Exposed for the encode/decode pins only. */
 uint16_t oracle_round_bf16(double v) { return double_to_bf16(v); }
 double oracle_decode_bf16(uint16_t b) { return bf16_to_double(b); }

@@ -6,6 +6,8 @@ float32.  See oracle.c for the definitions and the pages they follow:
   route    - moe-engine page, "Fused Triton routing kernel" section
   dispatch - PithTrain page, section 8.2 (counting sort instead of argsort)
   ep_dispatch - the same section: per-rank counts, send metadata, dedup
+  *_backward - the gradients of route, dispatch and combine (training runs
+               the stages backward; PithTrain page, section 6.2)
   combine  - PithTrain page, section 6.1 (forward_aggregate)
 """
 import ctypes
@@ -41,6 +43,13 @@ def _load():
         lib.oracle_permute_rows.restype = ctypes.c_int
         lib.oracle_combine.argtypes = [P, P, P, i64, i32, i32, i32, P]
         lib.oracle_combine.restype = ctypes.c_int
+        lib.oracle_combine_backward.argtypes = [P, P, P, P, i64, i32, i32, i32, P, P]
+        lib.oracle_combine_backward.restype = ctypes.c_int
+        lib.oracle_dispatch_backward.argtypes = [P, P, i64, i32, i32, i32, P]
+        lib.oracle_dispatch_backward.restype = ctypes.c_int
+        lib.oracle_route_backward.argtypes = [P, P, P, P, P, P, P, i64, i32, i32, i32, i32,
+                                              P, P, P, P]
+        lib.oracle_route_backward.restype = ctypes.c_int
         lib.oracle_round_bf16.argtypes = [dbl]
         lib.oracle_round_bf16.restype = ctypes.c_uint16
         lib.oracle_decode_bf16.argtypes = [ctypes.c_uint16]
@@ -175,3 +184,65 @@ def round_bf16(v):
 def decode_bf16(bits):
     """bf16 bit pattern -> float (exact)."""
     return float(_load().oracle_decode_bf16(int(bits)))
+
+
+def combine_backward(dout, y, inv, w, dtype):
+    """Gradient of the combine: (dy [N*K,H] in `dtype` storage, rows in
+    dispatched order; dw [N,K] float32)."""
+    dout = _storage(dout, dtype)
+    y = _storage(y, dtype)
+    inv = np.ascontiguousarray(inv, dtype=np.int32)
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    N, K = w.shape
+    H = dout.shape[1]
+    dy = np.empty((N * K, H), dout.dtype)
+    dw = np.empty((N, K), np.float32)
+    rc = _load().oracle_combine_backward(_ptr(dout), _ptr(y), _ptr(inv), _ptr(w), N, H, K,
+                                         DTYPES[dtype], _ptr(dy), _ptr(dw))
+    if rc != 0:
+        raise ValueError("oracle_combine_backward rejected its arguments")
+    return dy, dw
+
+
+def dispatch_backward(dx_perm, inv, K, dtype):
+    """Gradient of the row dispatch: dx [N,H] = sum_k dx_perm[inv[n*K+k]]."""
+    dx_perm = _storage(dx_perm, dtype)
+    inv = np.ascontiguousarray(inv, dtype=np.int32)
+    N = inv.shape[0] // K
+    H = dx_perm.shape[1]
+    dx = np.empty((N, H), dx_perm.dtype)
+    rc = _load().oracle_dispatch_backward(_ptr(dx_perm), _ptr(inv), N, H, K, DTYPES[dtype],
+                                          _ptr(dx))
+    if rc != 0:
+        raise ValueError("oracle_dispatch_backward rejected its arguments")
+    return dx
+
+
+def route_backward(x, gate_w, bias, ids, dw, dx_perm, inv, dtype):
+    """Gradient of the router weights (fixed selection ids) with respect to
+    gate_w, bias and x, plus the dispatch backward of dx_perm (or None).
+    Returns (dlogits [N,E] float64, dgate_w [H,E] float32, dbias [E]
+    float32, dx [N,H] in `dtype` storage)."""
+    x = _storage(x, dtype)
+    gate_w = _storage(gate_w, dtype)
+    N, H = x.shape
+    E = gate_w.shape[1]
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    K = ids.shape[1]
+    dw = np.ascontiguousarray(dw, dtype=np.float32)
+    if bias is not None:
+        bias = np.ascontiguousarray(bias, dtype=np.float32)
+    if dx_perm is not None:
+        dx_perm = _storage(dx_perm, dtype)
+        inv = np.ascontiguousarray(inv, dtype=np.int32)
+    dlogits = np.empty((N, E), np.float64)
+    dgate_w = np.empty((H, E), np.float32)
+    dbias = np.empty((E,), np.float32)
+    dx = np.empty((N, H), x.dtype)
+    rc = _load().oracle_route_backward(_ptr(x), _ptr(gate_w), _ptr(bias), _ptr(ids), _ptr(dw),
+                                       _ptr(dx_perm), _ptr(inv if dx_perm is not None else None),
+                                       N, H, E, K, DTYPES[dtype], _ptr(dlogits),
+                                       _ptr(dgate_w), _ptr(dbias), _ptr(dx))
+    if rc != 0:
+        raise ValueError("oracle_route_backward rejected its arguments")
+    return dlogits, dgate_w, dbias, dx

@@ -454,3 +454,149 @@ def test_combine_negative_zero_row_sums_to_positive_zero():
     y = np.array([[0x8000, 0x3F80], [0x8000, 0x3F80]], np.uint16)
     out = O.combine(y, np.array([0, 1], np.int32), np.array([[0.5, 0.5]], np.float32), "bf16")
     assert out[0, 0] == 0x0000 and out[0, 1] == 0x3F80
+
+
+# ---------------------------------------------------------------- backward
+
+def _dyadic(rng, shape, lo=-4, hi=5):
+    """Small integers: every product and sum below is exact in float32."""
+    return rng.integers(lo, hi, size=shape).astype(np.float32)
+
+
+def test_combine_backward_is_the_adjoint_exactly():
+    # <dout, combine(y, w)> == <dy, y> for every y: the defining property of
+    # the gradient with respect to y; exact on dyadic data
+    rng = np.random.default_rng(31)
+    N, H, E, K = 23, 12, 7, 3
+    ids = I.random_ids(31, N, E, K)
+    _, _, _, inv = O.dispatch(ids, E)
+    w = rng.choice([0.25, 0.5, 1.0, -0.75], size=(N, K)).astype(np.float32)
+    y = _dyadic(rng, (N * K, H))
+    dout = _dyadic(rng, (N, H))
+    dy, dw = O.combine_backward(dout, y, inv, w, "f32")
+    out = O.combine(y, inv, w, "f32")
+    assert float((dout.astype(np.float64) * out).sum()) == float((dy.astype(np.float64) * y).sum())
+    # the same identity for another y (linearity): dy does not depend on y
+    y2 = _dyadic(rng, (N * K, H))
+    dy2, _ = O.combine_backward(dout, y2, inv, w, "f32")
+    np.testing.assert_array_equal(dy, dy2)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_combine_backward_weight_gradient_is_a_dot_product(dtype):
+    d = I.random_case(32, 40, 96, 8, 2, dtype, bias=False)
+    ids = I.random_ids(32, 40, 8, 2)
+    _, _, _, inv = O.dispatch(ids, 8)
+    w = np.random.default_rng(32).random((40, 2)).astype(np.float32)
+    dout = d["y"][:40]
+    dy, dw = O.combine_backward(dout, d["y"], inv, w, dtype)
+    want = np.einsum("nh,nkh->nk", _decode(dout, dtype),
+                     _decode(d["y"], dtype)[inv.reshape(40, 2)])
+    np.testing.assert_allclose(dw, want, rtol=1e-6, atol=1e-6)
+    # dy rows: w * dout rounded once (within the unit roundoff of the storage
+    # type: 2^-8 for bf16's 8 significant bits, 2^-24 for fp32)
+    exact = w.astype(np.float64)[:, :, None] * _decode(dout, dtype)[:, None, :]
+    got = _decode(dy, dtype)[inv.reshape(40, 2)]
+    u = 2.0 ** -8 if dtype == "bf16" else 2.0 ** -24
+    assert (np.abs(got - exact) <= u * np.abs(exact)).all()
+
+
+def test_dispatch_backward_is_the_adjoint_exactly():
+    rng = np.random.default_rng(33)
+    N, H, E, K = 31, 9, 5, 2
+    ids = I.random_ids(33, N, E, K)
+    _, _, perm, inv = O.dispatch(ids, E)
+    x = _dyadic(rng, (N, H))
+    g = _dyadic(rng, (N * K, H))
+    dx = O.dispatch_backward(g, inv, K, "f32")
+    lhs = float((g.astype(np.float64) * O.permute_rows(x, perm, K)).sum())
+    assert lhs == float((dx.astype(np.float64) * x).sum())
+
+
+def _fd_case(seed):
+    """A tiny fp32 router case whose selection no small perturbation changes."""
+    for s in range(seed, seed + 200):
+        d = I.random_case(s, 3, 5, 6, 2, "f32", bias=True)
+        ids, w, lg, margin = O.route(d["x"], d["gate_w"], d["bias"], 2, "f32")
+        if margin.min() > 0.05:
+            return d, ids
+    raise AssertionError("no well-separated case found")
+
+
+def test_route_backward_matches_finite_differences():
+    # f = sum dw * w(x, gate_w, bias) through the oracle's own forward; central
+    # differences over every entry of gate_w, bias and x
+    d, ids = _fd_case(40)
+    dw = np.random.default_rng(41).standard_normal((3, 2)).astype(np.float32)
+    _, dg, db, dx = O.route_backward(d["x"], d["gate_w"], d["bias"], ids, dw, None, None, "f32")
+
+    def f(x, g, b):
+        ids2, w, _, _ = O.route(x, g, b, 2, "f32")
+        assert (ids2 == ids).all()
+        return float((dw.astype(np.float64) * w).sum())
+
+    def fd(arr, idx, which):
+        out = []
+        for sgn in (1, -1):
+            a = arr.copy()
+            a[idx] = np.float32(arr[idx] + sgn * 1e-3)
+            args = dict(x=d["x"], g=d["gate_w"], b=d["bias"])
+            args[which] = a
+            out.append((f(args["x"], args["g"], args["b"]), float(a[idx])))
+        (fp, ap), (fm, am) = out
+        return (fp - fm) / (ap - am)
+
+    for idx in np.ndindex(d["gate_w"].shape):
+        assert abs(fd(d["gate_w"], idx, "g") - dg[idx]) < 2e-4, idx
+    for e in range(6):
+        assert abs(fd(d["bias"], (e,), "b") - db[e]) < 2e-4, e
+    for idx in np.ndindex(d["x"].shape):
+        assert abs(fd(d["x"], idx, "x") - dx[idx]) < 2e-4, idx
+
+
+def test_route_backward_invariants_and_closed_forms():
+    d = I.random_case(42, 50, 32, 10, 3, "f32", bias=True)
+    ids, w, lg, _ = O.route(d["x"], d["gate_w"], d["bias"], 3, "f32")
+    dw = np.random.default_rng(42).standard_normal((50, 3)).astype(np.float32)
+    dl, dg, db, dx = O.route_backward(d["x"], d["gate_w"], d["bias"], ids, dw, None, None, "f32")
+    # the weights depend on logit differences only: each row sums to zero
+    assert np.abs(dl.sum(axis=1)).max() < 1e-12
+    # experts outside the selection get no gradient (the full softmax
+    # denominator cancels in the renormalisation)
+    mask = np.ones_like(dl, bool)
+    mask[np.arange(50)[:, None], ids] = False
+    assert np.abs(dl[mask]).max() < 1e-15
+    # dgate_w = x^T dl and dbias = column sums (library matmul in float64)
+    np.testing.assert_allclose(dg, d["x"].astype(np.float64).T @ dl, rtol=1e-6, atol=1e-9)
+    np.testing.assert_allclose(db, dl.sum(axis=0), rtol=1e-6, atol=1e-9)
+    # K = 1: the single weight is 1 whatever the logits, so nothing flows back
+    ids1, _, _, _ = O.route(d["x"], d["gate_w"], d["bias"], 1, "f32")
+    dl1, dg1, db1, dx1 = O.route_backward(d["x"], d["gate_w"], d["bias"], ids1,
+                                          dw[:, :1].copy(), None, None, "f32")
+    assert np.abs(dl1).max() < 1e-15 and np.abs(dg1).max() < 1e-12 and np.abs(dx1).max() < 1e-12
+
+
+def test_route_backward_full_selection_is_the_softmax_jacobian():
+    # K = E: the weights are the full softmax, whose Jacobian is
+    # diag(p) - p p^T (scipy's softmax of the oracle's logits)
+    d = I.random_case(43, 20, 16, 5, 5, "f32", bias=False)
+    ids, w, lg, _ = O.route(d["x"], d["gate_w"], None, 5, "f32")
+    dw = np.random.default_rng(43).standard_normal((20, 5)).astype(np.float32)
+    dl, _, _, _ = O.route_backward(d["x"], d["gate_w"], None, ids, dw, None, None, "f32")
+    p = scipy.special.softmax(lg, axis=1)
+    g = np.zeros((20, 5))
+    g[np.arange(20)[:, None], ids] = dw
+    want = p * (g - (p * g).sum(axis=1, keepdims=True))
+    np.testing.assert_allclose(dl, want, rtol=1e-12, atol=1e-15)
+
+
+def test_route_backward_adds_the_dispatch_backward():
+    d = I.random_case(44, 30, 24, 8, 2, "f32", bias=False)
+    ids, w, _, _ = O.route(d["x"], d["gate_w"], None, 2, "f32")
+    _, _, _, inv = O.dispatch(ids, 8)
+    dw = np.random.default_rng(44).standard_normal((30, 2)).astype(np.float32)
+    g = np.random.default_rng(45).standard_normal((60, 24)).astype(np.float32)
+    _, _, _, dx0 = O.route_backward(d["x"], d["gate_w"], None, ids, dw, None, None, "f32")
+    _, _, _, dx1 = O.route_backward(d["x"], d["gate_w"], None, ids, dw, g, inv, "f32")
+    np.testing.assert_allclose(dx1.astype(np.float64) - dx0,
+                               O.dispatch_backward(g, inv, 2, "f32"), rtol=1e-5, atol=1e-6)

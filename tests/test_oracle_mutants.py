@@ -67,6 +67,27 @@ MUTANTS = [
     ("ep expand index not segment-relative",
      "expand_idx[p] = send_row[i] - send_offsets[ids[i] / per_rank];",
      "expand_idx[p] = send_row[i];"),
+    ("backward: softmax Jacobian without the probability factor",
+     "dl[n * E + e] = p[e] * (dp[e] - u);",
+     "dl[n * E + e] = (dp[e] - u);"),
+    ("backward: renormalisation term with the wrong sign",
+     "(double)dw[n * K + k] / s - t / (s * s);",
+     "(double)dw[n * K + k] / s + t / (s * s);"),
+    ("backward: renormalisation term dropped",
+     "(double)dw[n * K + k] / s - t / (s * s);",
+     "(double)dw[n * K + k] / s;"),
+    ("backward: gate gradient expert index reversed",
+     "gacc[(int64_t)h * E + e] += xv * dl[n * E + e];",
+     "gacc[(int64_t)h * E + e] += xv * dl[n * E + (E - 1 - e)];"),
+    ("backward: combine gradient ignores the weight",
+     "store_elem(dy, row * H + h, dtype, (double)w[n * K + k] * g);",
+     "store_elem(dy, row * H + h, dtype, g);"),
+    ("backward: weight gradient dots dout with itself",
+     "acc += g * load_elem(y, row * H + h, dtype);",
+     "acc += g * g;"),
+    ("backward: dispatch gradient takes one slot",
+     "acc += load_elem(dx_perm, row * H + h, dtype);",
+     "acc = load_elem(dx_perm, row * H + h, dtype);"),
     ("bf16 decode shifted",
      "uint32_t u = (uint32_t)b << 16;",
      "uint32_t u = (uint32_t)b << 15;"),
