@@ -367,13 +367,13 @@ int oracle_combine_backward(const void *dout, const void *y, const int32_t *inv,
   const int64_t T = N * (int64_t)K;
   for (int64_t n = 0; n < N; ++n) {
     for (int32_t k = 0; k < K; ++k) {
-      const int64_t row = inv[n * K + k];
-      if (row < 0 || row >= T) return -1;
+      const int64_t rw = inv[n * K + k];
+      if (rw < 0 || rw >= T) return -1;
       double acc = 0.0;
       for (int32_t h = 0; h < H; ++h) {
         const double g = load_elem(dout, n * (int64_t)H + h, dtype);
-        acc += g * load_elem(y, row * H + h, dtype);
-        store_elem(dy, row * H + h, dtype, (double)w[n * K + k] * g);
+        acc += g * load_elem(y, rw * H + h, dtype);
+        store_elem(dy, rw * H + h, dtype, (double)w[n * K + k] * g);
       }
       dw[n * K + k] = (float)acc;
     }
@@ -394,9 +394,9 @@ int oracle_dispatch_backward(const void *dx_perm, const int32_t *inv, int64_t N,
     for (int32_t h = 0; h < H; ++h) {
       double acc = 0.0;
       for (int32_t k = 0; k < K; ++k) {
-        const int64_t row = inv[n * K + k];
-        if (row < 0 || row >= T) return -1;
-        acc += load_elem(dx_perm, row * H + h, dtype);
+        const int64_t rw = inv[n * K + k];
+        if (rw < 0 || rw >= T) return -1;
+        acc += load_elem(dx_perm, rw * H + h, dtype);
       }
       store_elem(dx, n * (int64_t)H + h, dtype, acc);
     }
@@ -439,7 +439,7 @@ int oracle_route_backward(const void *x, const void *gate_w, const float *bias,
     for (int32_t e = 0; e < E; ++e) l[e] = 0.0;
     for (int32_t h = 0; h < H; ++h) {
       const double xv = load_elem(x, n * (int64_t)H + h, dtype);
-      for (int32_t e = 0; e < E; ++e) l[e] += xv * load_elem(gate_w, (int64_t)h * E + e, dtype);
+      for (int32_t e = 0; e < E; ++e) l[e] += xv * load_elem(gate_w, h * (int64_t)E + e, dtype);
     }
     if (bias)
       for (int32_t e = 0; e < E; ++e) l[e] += (double)bias[e];
@@ -482,13 +482,13 @@ int oracle_route_backward(const void *x, const void *gate_w, const float *bias,
       double acc = 0.0;
       if (dx_perm) {
         for (int32_t k = 0; k < K; ++k) {
-          const int64_t row = inv[n * K + k];
-          if (row < 0 || row >= T) goto done;
-          acc += load_elem(dx_perm, row * (int64_t)H + h, dtype);
+          const int64_t rw = inv[n * K + k];
+          if (rw < 0 || rw >= T) goto done;
+          acc += load_elem(dx_perm, rw * (int64_t)H + h, dtype);
         }
       }
       for (int32_t e = 0; e < E; ++e)
-        acc += dl[n * E + e] * load_elem(gate_w, (int64_t)h * E + e, dtype);
+        acc += dl[n * E + e] * load_elem(gate_w, h * (int64_t)E + e, dtype);
       store_elem(dx, n * (int64_t)H + h, dtype, acc);
     }
   }

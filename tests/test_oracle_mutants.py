@@ -80,14 +80,14 @@ MUTANTS = [
      "gacc[(int64_t)h * E + e] += xv * dl[n * E + e];",
      "gacc[(int64_t)h * E + e] += xv * dl[n * E + (E - 1 - e)];"),
     ("backward: combine gradient ignores the weight",
-     "store_elem(dy, row * H + h, dtype, (double)w[n * K + k] * g);",
-     "store_elem(dy, row * H + h, dtype, g);"),
+     "store_elem(dy, rw * H + h, dtype, (double)w[n * K + k] * g);",
+     "store_elem(dy, rw * H + h, dtype, g);"),
     ("backward: weight gradient dots dout with itself",
-     "acc += g * load_elem(y, row * H + h, dtype);",
+     "acc += g * load_elem(y, rw * H + h, dtype);",
      "acc += g * g;"),
     ("backward: dispatch gradient takes one slot",
-     "acc += load_elem(dx_perm, row * H + h, dtype);",
-     "acc = load_elem(dx_perm, row * H + h, dtype);"),
+     "acc += load_elem(dx_perm, rw * H + h, dtype);",
+     "acc = load_elem(dx_perm, rw * H + h, dtype);"),
     ("bf16 decode shifted",
      "uint32_t u = (uint32_t)b << 16;",
      "uint32_t u = (uint32_t)b << 15;"),
