@@ -209,6 +209,71 @@ moe_status_t moe_combine(const void *y, const int32_t *inv, const float *topk_w,
                          int64_t N, int32_t H, int32_t K, moe_dtype_t dtype,
                          void *out, void *stream);
 
+/* ---------------------------------------------------------------- backward
+ * Training runs the path's stages backward ([A], section 6.2 "The five
+ * stages").  Each call below is the exact gradient of the forward call named
+ * in it, with the same layouts; floating-point sums run in fp32 in a fixed
+ * order (bitwise reproducible), results are rounded once to their type.
+ */
+
+/*
+ * moe_combine_backward -- gradient of moe_combine for an upstream gradient
+ * dout [N,H] (dtype):
+ *   dy[inv[n*K+k], :] = w[n,k] * dout[n, :]   rounded once, exactly (bf16:
+ *                                             nearest, ties to even)
+ *   dtopk_w[n,k]      = sum_h dout[n,h] * y[inv[n*K+k], h]    (fp32)
+ *   y [N*K,H], dy [N*K,H] dtype, dispatched (expert-contiguous) row order;
+ *   inv [N*K] int32 as from moe_dispatch; topk_w, dtopk_w [N,K] fp32.
+ * Every row of dy is written once when inv is a permutation; a slot whose
+ * inv is outside [0, N*K) writes no row and gets dtopk_w = 0.
+ */
+moe_status_t moe_combine_backward(const void *dout, const void *y, const int32_t *inv,
+                                  const float *topk_w, int64_t N, int32_t H, int32_t K,
+                                  moe_dtype_t dtype, void *dy, float *dtopk_w, void *stream);
+
+/*
+ * moe_dispatch_backward -- gradient of moe_dispatch's row copy:
+ *   dx[n, :] = sum_k dx_perm[inv[n*K+k], :]   (fp32, k ascending, one rounding)
+ *   dx_perm [N*K,H], dx [N,H] dtype; inv [N*K] int32.
+ */
+moe_status_t moe_dispatch_backward(const void *dx_perm, const int32_t *inv, int64_t N, int32_t H,
+                                   int32_t K, moe_dtype_t dtype, void *dx, void *stream);
+
+/*
+ * Bytes of device workspace moe_route_backward needs (0 for invalid sizes).
+ */
+size_t moe_route_backward_workspace_size(int64_t N, int32_t H, int32_t E, int32_t K,
+                                         moe_dtype_t dtype);
+
+/*
+ * moe_route_backward -- gradient of moe_route's weights (the selection ids
+ * held fixed) for an upstream gradient dtopk_w [N,K], with respect to the
+ * gate, the bias and the tokens, plus (optionally) the dispatch backward:
+ *   dl[n,e] = w[n,k] * (dtopk_w[n,k] - sum_j w[n,j] dtopk_w[n,j]) if
+ *             e = ids[n,k], else 0     (the gradient of the logits of [R]'s
+ *             softmax -> top-K -> renorm chain: the full-softmax
+ *             denominator cancels)
+ *   dgate_w[h,e] = sum_n x[n,h] dl[n,e]           [H,E] fp32 out
+ *   dbias[e]     = sum_n dl[n,e]                  [E] fp32 out, or NULL
+ *   dx[n,:]      = sum_k dx_perm[inv[n*K+k],:]  +  sum_e dl[n,e] gate_w[:,e]
+ *                  [N,H] dtype out, one rounding; the first sum is left out
+ *                  when dx_perm is NULL
+ * Inputs: x_perm [N*K,H] dtype, the forward's dispatched rows (x_perm[p] =
+ * x[perm[p]/K]); gate_w [H,E] dtype; topk_ids [N,K] int32, topk_w [N,K]
+ * fp32 (moe_route's outputs); perm [N*K], offsets [E+1] and inv [N*K]
+ * int32 (moe_dispatch's outputs for those ids); dx_perm [N*K,H] dtype or
+ * NULL.  Sums of dgate_w and dbias run over each expert's dispatched rows in
+ * order, in chunks of 32 rows, then over the chunks in order.
+ *   workspace >= moe_route_backward_workspace_size(N, H, E, K, dtype); scratch
+ * N == 0 is a valid call: dgate_w (and dbias) are zero-filled.
+ */
+moe_status_t moe_route_backward(const void *x_perm, const void *gate_w, const int32_t *topk_ids,
+                                const float *topk_w, const float *dtopk_w, const int32_t *perm,
+                                const int32_t *offsets, const int32_t *inv, const void *dx_perm,
+                                int64_t N, int32_t H, int32_t E, int32_t K, moe_dtype_t dtype,
+                                float *dgate_w, float *dbias, void *dx, void *workspace,
+                                size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -28,7 +28,8 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARGUMENT", 2: "MOE_ERR_UNSUPPORTED",
 EXPORTS = ("moe_status_string", "moe_route_workspace_size", "moe_route",
            "moe_dispatch_workspace_size", "moe_dispatch", "moe_route_dispatch_workspace_size",
            "moe_route_dispatch", "moe_ep_dispatch_workspace_size", "moe_ep_dispatch",
-           "moe_combine")
+           "moe_combine", "moe_combine_backward", "moe_dispatch_backward",
+           "moe_route_backward_workspace_size", "moe_route_backward")
 
 
 class MoeError(RuntimeError):
@@ -73,6 +74,15 @@ def library() -> ctypes.CDLL:
         lib.moe_ep_dispatch.restype = ctypes.c_int
         lib.moe_combine.argtypes = [P, P, P, i64, i32, i32, ctypes.c_int, P, P]
         lib.moe_combine.restype = ctypes.c_int
+        lib.moe_combine_backward.argtypes = [P, P, P, P, i64, i32, i32, ctypes.c_int, P, P, P]
+        lib.moe_combine_backward.restype = ctypes.c_int
+        lib.moe_dispatch_backward.argtypes = [P, P, i64, i32, i32, ctypes.c_int, P, P]
+        lib.moe_dispatch_backward.restype = ctypes.c_int
+        lib.moe_route_backward_workspace_size.argtypes = [i64, i32, i32, i32, ctypes.c_int]
+        lib.moe_route_backward_workspace_size.restype = sz
+        lib.moe_route_backward.argtypes = [P, P, P, P, P, P, P, P, P, i64, i32, i32, i32,
+                                           ctypes.c_int, P, P, P, P, sz, P]
+        lib.moe_route_backward.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -131,6 +141,10 @@ def moe_route_dispatch_workspace_size(N: int, H: int, E: int, K: int, dtype: tor
 
 def moe_ep_dispatch_workspace_size(N: int, E: int, K: int, ep_size: int) -> int:
     return int(library().moe_ep_dispatch_workspace_size(N, E, K, ep_size))
+
+
+def moe_route_backward_workspace_size(N: int, H: int, E: int, K: int, dtype: torch.dtype) -> int:
+    return int(library().moe_route_backward_workspace_size(N, H, E, K, _dtype_code(dtype)))
 
 
 # ------------------------------------------------------------------ calls
@@ -257,6 +271,60 @@ def moe_combine(y: torch.Tensor, inv: torch.Tensor, topk_w: torch.Tensor,
         _dev(out, "out", y.dtype, N * H, dev), _stream(dev)))
 
 
+def moe_combine_backward(dout: torch.Tensor, y: torch.Tensor, inv: torch.Tensor,
+                         topk_w: torch.Tensor, dy: torch.Tensor, dtopk_w: torch.Tensor) -> None:
+    """Gradient of moe_combine: dy [N*K,H] (dispatched order), dtopk_w [N,K]."""
+    N, K = topk_w.shape
+    H = dout.shape[1]
+    dev = dout.device
+    _check("moe_combine_backward", library().moe_combine_backward(
+        _dev(dout, "dout", dout.dtype, N * H, dev), _dev(y, "y", dout.dtype, N * K * H, dev),
+        _dev(inv, "inv", torch.int32, N * K, dev),
+        _dev(topk_w, "topk_w", torch.float32, N * K, dev), N, H, K, _dtype_code(dout.dtype),
+        _dev(dy, "dy", dout.dtype, N * K * H, dev),
+        _dev(dtopk_w, "dtopk_w", torch.float32, N * K, dev), _stream(dev)))
+
+
+def moe_dispatch_backward(dx_perm: torch.Tensor, inv: torch.Tensor, dx: torch.Tensor) -> None:
+    """Gradient of the dispatch row copy: dx [N,H] = sum_k dx_perm[inv[n*K+k]]."""
+    N, H = dx.shape
+    T = inv.numel()
+    if N and T % N:
+        raise ValueError("inv must hold N*K entries")
+    K = T // N if N else 1
+    dev = dx.device
+    _check("moe_dispatch_backward", library().moe_dispatch_backward(
+        _dev(dx_perm, "dx_perm", dx.dtype, T * H, dev), _dev(inv, "inv", torch.int32, T, dev),
+        N, H, K, _dtype_code(dx.dtype), _dev(dx, "dx", dx.dtype, N * H, dev), _stream(dev)))
+
+
+def moe_route_backward(x_perm: torch.Tensor, gate_w: torch.Tensor, topk_ids: torch.Tensor,
+                       topk_w: torch.Tensor, dtopk_w: torch.Tensor, perm: torch.Tensor,
+                       offsets: torch.Tensor, inv: Optional[torch.Tensor],
+                       dx_perm: Optional[torch.Tensor], dgate_w: torch.Tensor,
+                       dbias: Optional[torch.Tensor], dx: torch.Tensor,
+                       workspace: torch.Tensor) -> None:
+    """Gradient of moe_route's weights (ids fixed) with respect to gate_w,
+    bias and x, plus the dispatch backward of dx_perm (see include/moe.h)."""
+    N, K = topk_ids.shape
+    H, E = gate_w.shape
+    dev = gate_w.device
+    dt = gate_w.dtype
+    _check("moe_route_backward", library().moe_route_backward(
+        _dev(x_perm, "x_perm", dt, N * K * H, dev), _dev(gate_w, "gate_w", dt, H * E, dev),
+        _dev(topk_ids, "topk_ids", torch.int32, N * K, dev),
+        _dev(topk_w, "topk_w", torch.float32, N * K, dev),
+        _dev(dtopk_w, "dtopk_w", torch.float32, N * K, dev),
+        _dev(perm, "perm", torch.int32, N * K, dev),
+        _dev(offsets, "offsets", torch.int32, E + 1, dev),
+        _dev(inv, "inv", torch.int32, N * K, dev),
+        _dev(dx_perm, "dx_perm", dt, N * K * H, dev), N, H, E, K, _dtype_code(dt),
+        _dev(dgate_w, "dgate_w", torch.float32, H * E, dev),
+        _dev(dbias, "dbias", torch.float32, E, dev), _dev(dx, "dx", dt, N * H, dev),
+        _dev(workspace, "workspace", torch.uint8, workspace.numel(), dev), workspace.numel(),
+        _stream(dev)))
+
+
 # ------------------------------------------------------- allocating forms
 
 def route(x: torch.Tensor, gate_w: torch.Tensor, K: int, bias: Optional[torch.Tensor] = None,
@@ -342,3 +410,37 @@ def combine(y: torch.Tensor, inv: torch.Tensor, topk_w: torch.Tensor) -> torch.T
     out = torch.empty((N, y.shape[1]), dtype=y.dtype, device=y.device)
     moe_combine(y, inv, topk_w, out)
     return out
+
+
+def combine_backward(dout: torch.Tensor, y: torch.Tensor, inv: torch.Tensor,
+                     topk_w: torch.Tensor):
+    """Allocate and run moe_combine_backward; returns (dy, dtopk_w)."""
+    dy = torch.empty_like(y)
+    dw = torch.empty_like(topk_w)
+    moe_combine_backward(dout, y, inv, topk_w, dy, dw)
+    return dy, dw
+
+
+def dispatch_backward(dx_perm: torch.Tensor, inv: torch.Tensor, N: int) -> torch.Tensor:
+    """Allocate and run moe_dispatch_backward; returns dx [N,H]."""
+    dx = torch.empty((N, dx_perm.shape[1]), dtype=dx_perm.dtype, device=dx_perm.device)
+    moe_dispatch_backward(dx_perm, inv, dx)
+    return dx
+
+
+def route_backward(x_perm: torch.Tensor, gate_w: torch.Tensor, topk_ids: torch.Tensor,
+                   topk_w: torch.Tensor, dtopk_w: torch.Tensor, perm: torch.Tensor,
+                   offsets: torch.Tensor, inv: Optional[torch.Tensor] = None,
+                   dx_perm: Optional[torch.Tensor] = None, with_bias: bool = True):
+    """Allocate and run moe_route_backward; returns (dgate_w, dbias-or-None, dx)."""
+    N, K = topk_ids.shape
+    H, E = gate_w.shape
+    dev = gate_w.device
+    dgate_w = torch.empty((H, E), dtype=torch.float32, device=dev)
+    dbias = torch.empty((E,), dtype=torch.float32, device=dev) if with_bias else None
+    dx = torch.empty((N, H), dtype=gate_w.dtype, device=dev)
+    ws = torch.empty((max(1, moe_route_backward_workspace_size(N, H, E, K, gate_w.dtype)),),
+                     dtype=torch.uint8, device=dev)
+    moe_route_backward(x_perm, gate_w, topk_ids, topk_w, dtopk_w, perm, offsets, inv, dx_perm,
+                       dgate_w, dbias, dx, ws)
+    return dgate_w, dbias, dx

@@ -276,4 +276,101 @@ moe_status_t moe_combine(const void* y, const int32_t* inv, const float* topk_w,
                                       reinterpret_cast<hipStream_t>(stream)));
 }
 
+// ---------------------------------------------------------------- backward
+
+moe_status_t moe_combine_backward(const void* dout, const void* y, const int32_t* inv,
+                                  const float* topk_w, int64_t N, int32_t H, int32_t K,
+                                  moe_dtype_t dtype, void* dy, float* dtopk_w, void* stream) {
+  if (!valid_dtype(dtype) || N < 0 || H <= 0 || K < 1) return MOE_ERR_INVALID_ARGUMENT;
+  if (N > 0 && (!dout || !y || !inv || !topk_w || !dy || !dtopk_w))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (K > moe::kMaxExperts || N * (int64_t)K >= kMaxSlots || !row_ok(H, dtype))
+    return MOE_ERR_UNSUPPORTED;
+  if (!aligned(dout, 16) || !aligned(y, 16) || !aligned(dy, 16) || !aligned(inv, 4) ||
+      !aligned(topk_w, 4) || !aligned(dtopk_w, 4))
+    return MOE_ERR_MISALIGNED;
+  if (N == 0) return MOE_OK;
+  return from_hip(moe::launch_combine_backward(dout, y, inv, topk_w, N, H, K, dtype == MOE_BF16,
+                                               dy, dtopk_w,
+                                               reinterpret_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_dispatch_backward(const void* dx_perm, const int32_t* inv, int64_t N, int32_t H,
+                                   int32_t K, moe_dtype_t dtype, void* dx, void* stream) {
+  if (!valid_dtype(dtype) || N < 0 || H <= 0 || K < 1) return MOE_ERR_INVALID_ARGUMENT;
+  if (N > 0 && (!dx_perm || !inv || !dx)) return MOE_ERR_INVALID_ARGUMENT;
+  if (K > moe::kMaxExperts || N * (int64_t)K >= kMaxSlots || !row_ok(H, dtype))
+    return MOE_ERR_UNSUPPORTED;
+  if (!aligned(dx_perm, 16) || !aligned(dx, 16) || !aligned(inv, 4)) return MOE_ERR_MISALIGNED;
+  if (N == 0) return MOE_OK;
+  return from_hip(moe::launch_combine(dx_perm, inv, nullptr, N, H, K, dtype == MOE_BF16, dx,
+                                      reinterpret_cast<hipStream_t>(stream)));
+}
+
+namespace {
+
+struct RouteBwdLayout {
+  size_t gate_t, dlsel, chunk_base, part, part_b, total;
+};
+
+RouteBwdLayout route_bwd_layout(int64_t N, int32_t H, int32_t E, int32_t K, moe_dtype_t dtype) {
+  const int64_t T = N * K;
+  const int64_t chunks = moe::route_bwd_max_chunks(T, E);
+  RouteBwdLayout l;
+  l.gate_t = 0;
+  l.dlsel = l.gate_t + round_up((size_t)E * (size_t)H * elem_bytes(dtype), 256);
+  l.chunk_base = l.dlsel + round_up((size_t)T * sizeof(float), 256);
+  l.part = l.chunk_base + round_up(((size_t)E + 1) * sizeof(int32_t), 256);
+  l.part_b = l.part + round_up((size_t)chunks * (size_t)H * sizeof(float), 256);
+  l.total = l.part_b + round_up((size_t)chunks * sizeof(float), 256);
+  return l;
+}
+
+}  // namespace
+
+size_t moe_route_backward_workspace_size(int64_t N, int32_t H, int32_t E, int32_t K,
+                                         moe_dtype_t dtype) {
+  if (N < 0 || H <= 0 || E <= 0 || E > moe::kMaxExperts || K < 1 || K > E || !valid_dtype(dtype) ||
+      N * (int64_t)K >= kMaxSlots)
+    return 0;
+  return route_bwd_layout(N, H, E, K, dtype).total;
+}
+
+moe_status_t moe_route_backward(const void* x_perm, const void* gate_w, const int32_t* topk_ids,
+                                const float* topk_w, const float* dtopk_w, const int32_t* perm,
+                                const int32_t* offsets, const int32_t* inv, const void* dx_perm,
+                                int64_t N, int32_t H, int32_t E, int32_t K, moe_dtype_t dtype,
+                                float* dgate_w, float* dbias, void* dx, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  if (!valid_dtype(dtype) || N < 0 || H <= 0 || E <= 0 || K < 1 || K > E)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (!gate_w || !dgate_w) return MOE_ERR_INVALID_ARGUMENT;
+  if (N > 0 && (!x_perm || !topk_ids || !topk_w || !dtopk_w || !perm || !offsets || !dx ||
+                !workspace))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (N > 0 && dx_perm && !inv) return MOE_ERR_INVALID_ARGUMENT;
+  if (E > moe::kMaxExperts || N * (int64_t)K >= kMaxSlots || !row_ok(H, dtype))
+    return MOE_ERR_UNSUPPORTED;
+  if (!aligned(x_perm, 16) || !aligned(gate_w, 16) || !aligned(dx_perm, 16) || !aligned(dx, 16) ||
+      !aligned(topk_ids, 4) || !aligned(topk_w, 4) || !aligned(dtopk_w, 4) || !aligned(perm, 4) ||
+      !aligned(offsets, 4) || !aligned(inv, 4) || !aligned(dgate_w, 4) || !aligned(dbias, 4) ||
+      !aligned(workspace, 16))
+    return MOE_ERR_MISALIGNED;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (N == 0) {
+    // no tokens: the gate and bias gradients are zero
+    hipError_t e = moe::launch_fill_i32(reinterpret_cast<int32_t*>(dgate_w), (int64_t)H * E, 0, s);
+    if (e != hipSuccess || !dbias) return from_hip(e);
+    return from_hip(moe::launch_fill_i32(reinterpret_cast<int32_t*>(dbias), E, 0, s));
+  }
+  const RouteBwdLayout l = route_bwd_layout(N, H, E, K, dtype);
+  if (workspace_bytes < l.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  char* base = reinterpret_cast<char*>(workspace);
+  return from_hip(moe::launch_route_backward(
+      x_perm, gate_w, topk_ids, topk_w, dtopk_w, perm, offsets, inv, dx_perm, N, H, E, K,
+      dtype == MOE_BF16, dgate_w, dbias, dx, base + l.gate_t,
+      reinterpret_cast<float*>(base + l.dlsel), reinterpret_cast<int32_t*>(base + l.chunk_base),
+      reinterpret_cast<float*>(base + l.part), reinterpret_cast<float*>(base + l.part_b), s));
+}
+
 }  // extern "C"

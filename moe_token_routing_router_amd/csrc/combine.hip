@@ -100,7 +100,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4* __restrict__ 
   for (int j = tid; j < ntok * K; j += 256) {
     const int rrow = inv[n0 * K + j];
     lrow[j] = ((unsigned)rrow < (unsigned long long)T) ? rrow : -1;
-    lw[j] = w[n0 * K + j];
+    lw[j] = w ? w[n0 * K + j] : 1.f;  // no weights: the dispatch backward (a plain sum)
   }
   __syncthreads();
 

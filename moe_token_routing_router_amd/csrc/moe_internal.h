@@ -54,6 +54,41 @@ __device__ __forceinline__ int wave_inclusive_sum(int v) {
   return v;
 }
 
+// ---- wave-wide float sum, fixed order --------------------------------------
+// Butterfly inside each 16-lane row (DPP quad_perm xor 1, xor 2,
+// row_half_mirror, row_mirror: every lane ends with its row's sum), then the
+// four row sums are added in row order.  The same order on every call.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float wave_sum_f32(float v) {
+  v += dpp_mov_f32<0xB1>(v);   // quad_perm(1,0,3,2)
+  v += dpp_mov_f32<0x4E>(v);   // quad_perm(2,3,0,1)
+  v += dpp_mov_f32<0x141>(v);  // row_half_mirror
+  v += dpp_mov_f32<0x140>(v);  // row_mirror
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return ((r0 + r1) + r2) + r3;
+}
+
+// The exactly rounded bf16 of a * b (fp32 a, b): the fp32 product p and its
+// exact error e = a*b - p (one FMA) decide the one case where rounding p
+// again could differ from rounding a*b directly -- p on a bf16 midpoint.
+__device__ __forceinline__ uint32_t bf16_of_product(float a, float b) {
+  const float p = __fmul_rn(a, b);
+  const float e = __builtin_fmaf(a, b, -p);
+  const uint32_t u = __float_as_uint(p);
+  if ((u & 0xffffu) == 0x8000u && e != 0.f) {
+    const bool away = (e > 0.f) == (p > 0.f);  // |a*b| above the midpoint
+    return (u >> 16) + (away ? 1u : 0u);
+  }
+  return f32_to_bf16_rne(p);
+}
+
 // ---- block-level stable ranking ------------------------------------------
 // For the S slot ids sids[0..S) of one block (in LDS, published by the
 // caller's writes before the call), computes with NWAVES*64 threads:
@@ -157,8 +192,23 @@ hipError_t launch_ep_finish(const int32_t* ids, const int32_t* perm, const int32
                             int K, int E, int R, int32_t* send_tok, int32_t* send_row,
                             int32_t* expand_idx, hipStream_t s);
 
-// Combine.
+// Combine (w may be null: unit weights, the dispatch backward).
 hipError_t launch_combine(const void* y, const int32_t* inv, const float* w, int64_t N, int H,
                           int K, bool bf16, void* out, hipStream_t s);
+
+// Backward (backward.hip).
+hipError_t launch_combine_backward(const void* dout, const void* y, const int32_t* inv,
+                                   const float* w, int64_t N, int H, int K, bool bf16, void* dy,
+                                   float* dw, hipStream_t s);
+// Router backward workspace: gate_t [E][H] (dtype), dlsel [N*K] fp32, chunk
+// bases [E+1] int32, partials [route_bwd_max_chunks][H] fp32, bias partials
+// [route_bwd_max_chunks] fp32 -- laid out by the caller from these sizes.
+int64_t route_bwd_max_chunks(int64_t T, int E);
+hipError_t launch_route_backward(const void* x_perm, const void* gate_w, const int32_t* ids,
+                                 const float* w, const float* dw, const int32_t* perm,
+                                 const int32_t* offsets, const int32_t* inv, const void* dx_perm,
+                                 int64_t N, int H, int E, int K, bool bf16, float* dgate_w,
+                                 float* dbias, void* dx, void* gate_t, float* dlsel,
+                                 int32_t* chunk_base, float* part, float* part_b, hipStream_t s);
 
 }  // namespace moe

@@ -186,6 +186,50 @@ def test_combine_validation(lib):
     assert combine(lib, N=0) == OK             # empty: nothing to do, nothing enqueued
 
 
+def test_backward_validation(lib):
+    cb = lambda **k: lib.moe_combine_backward(
+        k.get("dout", A), k.get("y", A), k.get("inv", A2), k.get("w", A2), k.get("N", 4),
+        k.get("H", 16), k.get("K", 2), k.get("dt", BF16), k.get("dy", A), k.get("dw", A2), None)
+    assert cb(K=0) == INVALID
+    assert cb(dy=None) == INVALID
+    assert cb(dw=None) == INVALID
+    assert cb(H=4) == UNSUPPORTED
+    assert cb(dy=MIS8) == MISALIGNED
+    assert cb(dw=MIS) == MISALIGNED
+    assert cb(N=0) == OK
+    db = lambda **k: lib.moe_dispatch_backward(
+        k.get("dxp", A), k.get("inv", A2), k.get("N", 4), k.get("H", 16), k.get("K", 2),
+        k.get("dt", BF16), k.get("dx", A), None)
+    assert db(dx=None) == INVALID
+    assert db(dt=3) == INVALID
+    assert db(H=6, dt=F32) == UNSUPPORTED
+    assert db(dxp=MIS8) == MISALIGNED
+    assert db(N=0) == OK
+
+    def rb(**k):
+        return lib.moe_route_backward(
+            k.get("xp", A), k.get("gw", A), k.get("ids", A2), k.get("w", A2), k.get("dw", A2),
+            k.get("perm", A2), k.get("off", A2), k.get("inv", A2), k.get("dxp", None),
+            k.get("N", 4), k.get("H", 16), k.get("E", 8), k.get("K", 2), k.get("dt", BF16),
+            k.get("dg", A2), k.get("dbias", None), k.get("dx", A), k.get("ws", A),
+            k.get("wsb", 1 << 24), None)
+    assert rb(K=9) == INVALID
+    assert rb(gw=None) == INVALID
+    assert rb(dg=None) == INVALID
+    assert rb(perm=None) == INVALID
+    assert rb(dxp=A, inv=None) == INVALID
+    assert rb(E=300, K=2) == UNSUPPORTED
+    assert rb(H=12) == UNSUPPORTED
+    assert rb(xp=MIS8) == MISALIGNED
+    assert rb(dbias=MIS) == MISALIGNED
+    assert rb(wsb=64) == WS_SMALL
+    # workspace: the expert-major gate, dl, chunk bases, and one fp32 row of
+    # partials per chunk of 32 dispatched rows (plus one per expert)
+    n = lib.moe_route_backward_workspace_size(16384, 4096, 64, 2, BF16)
+    assert n >= 64 * 4096 * 2 + 32768 * 4 + (32768 // 32 + 64) * 4096 * 4
+    assert lib.moe_route_backward_workspace_size(16, 64, 8, 9, BF16) == 0
+
+
 def test_binding_rejects_host_tensors():
     import torch
     x = torch.zeros((4, 16), dtype=torch.bfloat16)
