@@ -168,6 +168,19 @@ def main():
                   x_send=torch.empty((cap, H), dtype=tdt, device=dev))
     ews = torch.empty((L.moe_ep_dispatch_workspace_size(N, E, K, R),), dtype=torch.uint8,
                       device=dev)
+    # backward of the path (measured on its own): upstream gradients are the
+    # other sets' rows (dout = a token matrix, dx_perm = a dispatched matrix)
+    for s_i, st in enumerate(sets):
+        other = sets[(s_i + 1) % N_SETS] if N_SETS > 1 else st
+        st.update(dout=other["x"], dx_perm=other["y"],
+                  dtopk_w=torch.randn((N, K), dtype=torch.float32, device=dev),
+                  dy=torch.empty((T, H), dtype=tdt, device=dev),
+                  dw=torch.empty((N, K), dtype=torch.float32, device=dev),
+                  dx=torch.empty((N, H), dtype=tdt, device=dev),
+                  dgate=torch.empty((H, E), dtype=torch.float32, device=dev),
+                  dbias=torch.empty((E,), dtype=torch.float32, device=dev))
+    bws = torch.empty((L.moe_route_backward_workspace_size(N, H, E, K, tdt),), dtype=torch.uint8,
+                      device=dev)
     rws = torch.empty((max(1, L.moe_route_workspace_size(H, E, tdt)),), dtype=torch.uint8,
                       device=dev)
     dws = torch.empty((L.moe_dispatch_workspace_size(N, E, K),), dtype=torch.uint8, device=dev)
@@ -185,6 +198,11 @@ def main():
         L.moe_ep_dispatch(st["ids"], st["x"], E, R, st["counts"], st["offsets"], st["perm"],
                           st["inv"], st["send_counts"], st["send_offsets"], st["send_tok"],
                           st["send_row"], st["expand_idx"], st["x_send"], ews)
+        L.moe_combine_backward(st["dout"], st["y"], st["inv"], st["w"], st["dy"], st["dw"])
+        L.moe_dispatch_backward(st["dx_perm"], st["inv"], st["dx"])
+        L.moe_route_backward(st["x_perm"], gw, st["ids"], st["w"], st["dtopk_w"], st["perm"],
+                             st["offsets"], st["inv"], st["dx_perm"], st["dgate"], st["dbias"],
+                             st["dx"], bws)
     torch.cuda.synchronize()
 
     # then call the C ABI directly with the pointers (no per-call Python checks)
@@ -207,10 +225,19 @@ def main():
             ep_dispatch=(P(st["ids"]), P(st["x"]), N, H, E, K, R, dt, P(st["counts"]),
                          P(st["offsets"]), P(st["perm"]), P(st["inv"]), P(st["send_counts"]),
                          P(st["send_offsets"]), P(st["send_tok"]), P(st["send_row"]),
-                         P(st["expand_idx"]), P(st["x_send"]), P(ews), ews.numel(), sp)))
+                         P(st["expand_idx"]), P(st["x_send"]), P(ews), ews.numel(), sp),
+            combine_backward=(P(st["dout"]), P(st["y"]), P(st["inv"]), P(st["w"]), N, H, K, dt,
+                              P(st["dy"]), P(st["dw"]), sp),
+            dispatch_backward=(P(st["dx_perm"]), P(st["inv"]), N, H, K, dt, P(st["dx"]), sp),
+            route_backward=(P(st["x_perm"]), P(gw), P(st["ids"]), P(st["w"]), P(st["dtopk_w"]),
+                            P(st["perm"]), P(st["offsets"]), P(st["inv"]), P(st["dx_perm"]), N,
+                            H, E, K, dt, P(st["dgate"]), P(st["dbias"]), P(st["dx"]), P(bws),
+                            bws.numel(), sp)))
     fn = {"route": lib.moe_route, "dispatch": lib.moe_dispatch,
           "route_dispatch": lib.moe_route_dispatch, "combine": lib.moe_combine,
-          "ep_dispatch": lib.moe_ep_dispatch}
+          "ep_dispatch": lib.moe_ep_dispatch, "combine_backward": lib.moe_combine_backward,
+          "dispatch_backward": lib.moe_dispatch_backward,
+          "route_backward": lib.moe_route_backward}
 
     def call(name, i):
         status = fn[name](*calls[i % N_SETS][name])
@@ -251,7 +278,8 @@ def main():
     # input sets) between one pair of HIP events on the launch stream: the
     # average duration of one call
     stage_ms = {}
-    for name in ("route_dispatch", "combine", "route", "dispatch", "ep_dispatch"):
+    for name in ("route_dispatch", "combine", "route", "dispatch", "ep_dispatch",
+                 "combine_backward", "dispatch_backward", "route_backward"):
         for i in range(3):
             call(name, i)
         _, ms = timed(lambda i, n=name: call(n, i), args.steps)
@@ -272,6 +300,11 @@ def main():
     # ep_dispatch: ids in, x read once, S deduplicated rows out, the expert
     # metadata (counts, offsets, perm, inv) and the send metadata (send
     # counts/offsets, send_tok [S], send_row and expand_idx [N*K])
+    # backward: what each call must move (its scratch excluded)
+    alg["combine_backward"] = N * H * b + 2 * T * H * b + 3 * T * 4
+    alg["dispatch_backward"] = T * H * b + N * H * b + T * 4
+    alg["route_backward"] = (2 * T * H * b + N * H * b + H * E * b + 5 * T * 4 + (E + 1) * 4
+                             + H * E * 4 + E * 4)
     S = int(sets[0]["send_offsets"][R].item())
     alg["ep_dispatch"] = (T * 4 + N * H * b + S * H * b + (2 * E + 1) * 4 + 2 * T * 4
                           + (2 * R + 1) * 4 + S * 4 + 2 * T * 4)
