@@ -37,8 +37,18 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// Tuning knobs (compile-time).
+#ifndef MOE_BWD_U
+#define MOE_BWD_U 2        // row vectors per lane in flight for K <= 2 (combine / dx backward)
+#endif
+#ifndef MOE_BWD_ROWS
+#define MOE_BWD_ROWS 8     // dispatched rows in flight per lane (gate partials)
+#endif
+
 constexpr int kBwdChunk = 32;  // dispatched rows per gate-gradient partial
 constexpr int kBwdVPT = 2;     // 16-byte vectors per thread and row in the partial kernel
+constexpr int kBwdU = MOE_BWD_U;
+constexpr int kBwdRows = MOE_BWD_ROWS;
 
 __device__ __forceinline__ u32x4 ldnt(const u32x4* p) { return __builtin_nontemporal_load(p); }
 __device__ __forceinline__ void stnt(u32x4* p, u32x4 v) { __builtin_nontemporal_store(v, p); }
@@ -116,21 +126,33 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const u32x4* __restric
       wk[kk] = w[n * K + k0 + kk];
       part[kk] = 0.f;
     }
-    for (int c = tid; c < row_vecs; c += 256) {
-      const u32x4 gv = ldnt(grow + c);
-      u32x4 yv[KR];
+    constexpr int U = KR <= 2 ? kBwdU : 1;
+    for (int c0 = tid; c0 < row_vecs; c0 += 256 * U) {
+      // all loads of U vectors first (clamped: the extra ones are not used)
+      u32x4 gv[U], yv[U][KR];
 #pragma unroll
-      for (int kk = 0; kk < KR; ++kk)
-        yv[kk] = row[kk] >= 0 ? ldnt(y + (int64_t)row[kk] * row_vecs + c) : zero;
-      float gf[L];
-      unpack<BF16>(gv, gf);
+      for (int u = 0; u < U; ++u) {
+        const int c = min(c0 + u * 256, row_vecs - 1);
+        gv[u] = ldnt(grow + c);
 #pragma unroll
-      for (int kk = 0; kk < KR; ++kk) {
-        float yf[L];
-        unpack<BF16>(yv[kk], yf);
+        for (int kk = 0; kk < KR; ++kk)
+          yv[u][kk] = row[kk] >= 0 ? ldnt(y + (int64_t)row[kk] * row_vecs + c) : zero;
+      }
 #pragma unroll
-        for (int j = 0; j < L; ++j) part[kk] = fmaf(gf[j], yf[j], part[kk]);
-        if (row[kk] >= 0) stnt(dy + (int64_t)row[kk] * row_vecs + c, scale_exact<BF16>(wk[kk], gf));
+      for (int u = 0; u < U; ++u) {
+        const int c = c0 + u * 256;
+        if (c >= row_vecs) break;
+        float gf[L];
+        unpack<BF16>(gv[u], gf);
+#pragma unroll
+        for (int kk = 0; kk < KR; ++kk) {
+          float yf[L];
+          unpack<BF16>(yv[u][kk], yf);
+#pragma unroll
+          for (int j = 0; j < L; ++j) part[kk] = fmaf(gf[j], yf[j], part[kk]);
+          if (row[kk] >= 0)
+            stnt(dy + (int64_t)row[kk] * row_vecs + c, scale_exact<BF16>(wk[kk], gf));
+        }
       }
     }
 #pragma unroll
@@ -218,46 +240,63 @@ __global__ __launch_bounds__(256) void route_bwd_dx_kernel(
   }
   __syncthreads();
   const u32x4 zero = {0u, 0u, 0u, 0u};
+  if constexpr (KT > 0) {
+    constexpr int U = KT <= 2 ? kBwdU : 1;
+    for (int c0 = tid; c0 < row_vecs; c0 += 256 * U) {
+      u32x4 pv[U][KT], gv[U][KT];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = min(c0 + u * 256, row_vecs - 1);
+#pragma unroll
+        for (int k = 0; k < KT; ++k) {
+          pv[u][k] = prow[k] >= 0 ? ldnt(dx_perm + (int64_t)prow[k] * row_vecs + c) : zero;
+          gv[u][k] = grw[k] >= 0 ? gate_t[(int64_t)grw[k] * row_vecs + c] : zero;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = c0 + u * 256;
+        if (c >= row_vecs) break;
+        float acc[L];
+#pragma unroll
+        for (int j = 0; j < L; ++j) acc[j] = 0.f;
+#pragma unroll
+        for (int k = 0; k < KT; ++k) {
+          float f[L];
+          unpack<BF16>(pv[u][k], f);
+#pragma unroll
+          for (int j = 0; j < L; ++j) acc[j] += f[j];
+        }
+#pragma unroll
+        for (int k = 0; k < KT; ++k) {
+          float f[L];
+          unpack<BF16>(gv[u][k], f);
+#pragma unroll
+          for (int j = 0; j < L; ++j) acc[j] = fmaf(gw[k], f[j], acc[j]);
+        }
+        stnt(dx + n * row_vecs + c, pack<BF16>(acc));
+      }
+    }
+    return;
+  }
+  // any K: one output vector per lane at a time
   for (int c = tid; c < row_vecs; c += 256) {
     float acc[L];
 #pragma unroll
     for (int j = 0; j < L; ++j) acc[j] = 0.f;
-    if constexpr (KT > 0) {
-      u32x4 pv[KT], gv[KT];
+    for (int k = 0; k < K; ++k) {
+      if (prow[k] < 0) continue;
+      float f[L];
+      unpack<BF16>(ldnt(dx_perm + (int64_t)prow[k] * row_vecs + c), f);
 #pragma unroll
-      for (int k = 0; k < KT; ++k) {
-        pv[k] = prow[k] >= 0 ? ldnt(dx_perm + (int64_t)prow[k] * row_vecs + c) : zero;
-        gv[k] = grw[k] >= 0 ? gate_t[(int64_t)grw[k] * row_vecs + c] : zero;
-      }
+      for (int j = 0; j < L; ++j) acc[j] += f[j];
+    }
+    for (int k = 0; k < K; ++k) {
+      if (grw[k] < 0) continue;
+      float f[L];
+      unpack<BF16>(gate_t[(int64_t)grw[k] * row_vecs + c], f);
 #pragma unroll
-      for (int k = 0; k < KT; ++k) {
-        float f[L];
-        unpack<BF16>(pv[k], f);
-#pragma unroll
-        for (int j = 0; j < L; ++j) acc[j] += f[j];
-      }
-#pragma unroll
-      for (int k = 0; k < KT; ++k) {
-        float f[L];
-        unpack<BF16>(gv[k], f);
-#pragma unroll
-        for (int j = 0; j < L; ++j) acc[j] = fmaf(gw[k], f[j], acc[j]);
-      }
-    } else {
-      for (int k = 0; k < K; ++k) {
-        if (prow[k] < 0) continue;
-        float f[L];
-        unpack<BF16>(ldnt(dx_perm + (int64_t)prow[k] * row_vecs + c), f);
-#pragma unroll
-        for (int j = 0; j < L; ++j) acc[j] += f[j];
-      }
-      for (int k = 0; k < K; ++k) {
-        if (grw[k] < 0) continue;
-        float f[L];
-        unpack<BF16>(gate_t[(int64_t)grw[k] * row_vecs + c], f);
-#pragma unroll
-        for (int j = 0; j < L; ++j) acc[j] = fmaf(gw[k], f[j], acc[j]);
-      }
+      for (int j = 0; j < L; ++j) acc[j] = fmaf(gw[k], f[j], acc[j]);
     }
     stnt(dx + n * row_vecs + c, pack<BF16>(acc));
   }
@@ -333,16 +372,17 @@ __global__ __launch_bounds__(256) void route_bwd_wpart_kernel(
 #pragma unroll
     for (int j = 0; j < L; ++j) acc[v][j] = 0.f;
   const u32x4 zero = {0u, 0u, 0u, 0u};
-  for (int r = 0; r < rows; r += 4) {
-    u32x4 xv[4][V];
+  constexpr int RR = kBwdRows;
+  for (int r = 0; r < rows; r += RR) {
+    u32x4 xv[RR][V];
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
+    for (int rr = 0; rr < RR; ++rr) {
       const int64_t p = p0 + min(r + rr, rows - 1);
 #pragma unroll
       for (int v = 0; v < V; ++v) xv[rr][v] = ok[v] ? ldnt(x_perm + p * row_vecs + cv[v]) : zero;
     }
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
+    for (int rr = 0; rr < RR; ++rr) {
       if (r + rr >= rows) break;
       const float c = coef[r + rr];
 #pragma unroll
