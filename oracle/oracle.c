@@ -343,6 +343,80 @@ int oracle_combine(const void *y, const int32_t *inv, const float *w, int64_t N,
   return 0;
 }
 
+/* ---- [A] forward_aggregate: weighted expert output + residual ------------ */
+
+/*
+ * oracle_aggregate: out[n,h] = round( sum_k w[n,k] * y[inv[n*K+k], h]
+ *                                     + residual[n,h] )
+ * the expert terms summed with k ascending from 0.0, then the residual
+ * added, in double, rounded once to `dtype`.
+ */
+int oracle_aggregate(const void *y, const int32_t *inv, const float *w, const void *residual,
+                     int64_t N, int32_t H, int32_t K, int32_t dtype, void *out) {
+  if (N < 0 || H <= 0 || K < 1) return -1;
+  if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return -1;
+  const int64_t T = N * (int64_t)K;
+  for (int64_t n = 0; n < N; ++n) {
+    for (int32_t h = 0; h < H; ++h) {
+      double acc = 0.0;
+      for (int32_t k = 0; k < K; ++k) {
+        const int64_t src = inv[n * K + k];
+        if (src < 0 || src >= T) return -1;
+        acc += (double)w[n * K + k] * load_elem(y, src * H + h, dtype);
+      }
+      acc += load_elem(residual, n * (int64_t)H + h, dtype);
+      if (dtype == ORACLE_BF16)
+        ((uint16_t *)out)[n * (int64_t)H + h] = double_to_bf16(acc);
+      else
+        ((float *)out)[n * (int64_t)H + h] = (float)acc;
+    }
+  }
+  return 0;
+}
+
+/* ---- grouped expert linear layer over the dispatched rows --------------- */
+
+/*
+ * oracle_grouped_linear: the expert layer that runs between dispatch and
+ * combine ([A] 6.1, forward_mlp on the gathered tokens; the MoE GroupLinear
+ * of the same page's layer list), as one linear map per expert:
+ *   y[p, f] = round( sum_h x_perm[p, h] * weight[e][f][h] )
+ * for every dispatched row p of expert e (offsets[e] <= p < offsets[e+1]),
+ * weight [E][F][H] (row f of expert e holds the weights of output f), the
+ * sum in double with h ascending, rounded once to `dtype`.
+ * rows (nrows entries) lists the rows to compute, y receiving them in that
+ * order ([nrows][F]); rows == NULL computes every row p < offsets[E] into
+ * y [offsets[E]][F].
+ */
+int oracle_grouped_linear(const void *x_perm, const void *weight, const int32_t *offsets,
+                          int32_t E, int32_t H, int32_t F, int32_t dtype,
+                          const int32_t *rows, int64_t nrows, void *y) {
+  if (E <= 0 || H <= 0 || F <= 0) return -1;
+  if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return -1;
+  if (offsets[0] != 0) return -1;
+  for (int32_t e = 0; e < E; ++e)
+    if (offsets[e + 1] < offsets[e]) return -1;
+  const int64_t total = offsets[E];
+  const int64_t count = rows ? nrows : total;
+  for (int64_t i = 0; i < count; ++i) {
+    const int64_t p = rows ? rows[i] : i;
+    if (p < 0 || p >= total) return -1;
+    int32_t e = 0;
+    while (!(offsets[e] <= p && p < offsets[e + 1])) ++e; /* the segment holding p */
+    for (int32_t f = 0; f < F; ++f) {
+      double acc = 0.0;
+      for (int32_t h = 0; h < H; ++h)
+        acc += load_elem(x_perm, p * H + h, dtype) *
+               load_elem(weight, ((int64_t)e * F + f) * H + h, dtype);
+      if (dtype == ORACLE_BF16)
+        ((uint16_t *)y)[i * F + f] = double_to_bf16(acc);
+      else
+        ((float *)y)[i * F + f] = (float)acc;
+    }
+  }
+  return 0;
+}
+
 /* ---- backward of the path ([A] 6.2: the stages run backward in training) */
 
 static void store_elem(void *base, int64_t idx, int dtype, double v) {

@@ -8,6 +8,9 @@ float32.  See oracle.c for the definitions and the pages they follow:
   ep_dispatch - the same section: per-rank counts, send metadata, dedup
   *_backward - the gradients of route, dispatch and combine (training runs
                the stages backward; PithTrain page, section 6.2)
+  aggregate - forward_aggregate: weighted expert output + residual (6.1)
+  grouped_linear - one linear map per expert over the dispatched rows (the
+               expert layer between dispatch and combine, 6.1 forward_mlp)
   combine  - PithTrain page, section 6.1 (forward_aggregate)
 """
 import ctypes
@@ -50,6 +53,10 @@ def _load():
         lib.oracle_route_backward.argtypes = [P, P, P, P, P, P, P, i64, i32, i32, i32, i32,
                                               P, P, P, P]
         lib.oracle_route_backward.restype = ctypes.c_int
+        lib.oracle_aggregate.argtypes = [P, P, P, P, i64, i32, i32, i32, P]
+        lib.oracle_aggregate.restype = ctypes.c_int
+        lib.oracle_grouped_linear.argtypes = [P, P, P, i32, i32, i32, i32, P, i64, P]
+        lib.oracle_grouped_linear.restype = ctypes.c_int
         lib.oracle_round_bf16.argtypes = [dbl]
         lib.oracle_round_bf16.restype = ctypes.c_uint16
         lib.oracle_decode_bf16.argtypes = [ctypes.c_uint16]
@@ -246,3 +253,38 @@ def route_backward(x, gate_w, bias, ids, dw, dx_perm, inv, dtype):
     if rc != 0:
         raise ValueError("oracle_route_backward rejected its arguments")
     return dlogits, dgate_w, dbias, dx
+
+
+def aggregate(y, inv, w, residual, dtype):
+    """forward_aggregate: the weighted expert output plus the residual [N,H]."""
+    y = _storage(y, dtype)
+    residual = _storage(residual, dtype)
+    inv = np.ascontiguousarray(inv, dtype=np.int32)
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    N, K = w.shape
+    H = y.shape[1]
+    out = np.empty((N, H), y.dtype)
+    rc = _load().oracle_aggregate(_ptr(y), _ptr(inv), _ptr(w), _ptr(residual), N, H, K,
+                                  DTYPES[dtype], _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle_aggregate rejected its arguments")
+    return out
+
+
+def grouped_linear(x_perm, weight, offsets, dtype, rows=None):
+    """One linear map per expert over its dispatched rows: y[p] =
+    weight[e] @ x_perm[p] for offsets[e] <= p < offsets[e+1]; weight
+    [E,F,H].  With rows given, only those rows are computed (y [len(rows),F])."""
+    x_perm = _storage(x_perm, dtype)
+    weight = _storage(weight, dtype)
+    E, F, H = weight.shape
+    offsets = np.ascontiguousarray(offsets, dtype=np.int32)
+    if rows is not None:
+        rows = np.ascontiguousarray(rows, dtype=np.int32)
+    n = len(rows) if rows is not None else int(offsets[E])
+    y = np.empty((n, F), x_perm.dtype)
+    rc = _load().oracle_grouped_linear(_ptr(x_perm), _ptr(weight), _ptr(offsets), E, H, F,
+                                       DTYPES[dtype], _ptr(rows), n, _ptr(y))
+    if rc != 0:
+        raise ValueError("oracle_grouped_linear rejected its arguments")
+    return y

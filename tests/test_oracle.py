@@ -600,3 +600,93 @@ def test_route_backward_adds_the_dispatch_backward():
     _, _, _, dx1 = O.route_backward(d["x"], d["gate_w"], None, ids, dw, g, inv, "f32")
     np.testing.assert_allclose(dx1.astype(np.float64) - dx0,
                                O.dispatch_backward(g, inv, 2, "f32"), rtol=1e-5, atol=1e-6)
+
+
+# ---------------------------------------------------------------- aggregate
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_aggregate_with_zero_residual_is_the_combine(dtype):
+    d = I.random_case(50, 60, 40, 8, 3, dtype, bias=False)
+    ids = I.random_ids(50, 60, 8, 3)
+    _, _, _, inv = O.dispatch(ids, 8)
+    w = np.random.default_rng(50).random((60, 3)).astype(np.float32)
+    zero = np.zeros((60, 40), np.float32 if dtype == "f32" else np.uint16)
+    np.testing.assert_array_equal(O.aggregate(d["y"], inv, w, zero, dtype),
+                                  O.combine(d["y"], inv, w, dtype))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_aggregate_with_zero_weights_is_the_residual(dtype):
+    d = I.random_case(51, 30, 24, 6, 2, dtype, bias=False)
+    ids = I.random_ids(51, 30, 6, 2)
+    _, _, _, inv = O.dispatch(ids, 6)
+    res = d["x"]
+    np.testing.assert_array_equal(O.aggregate(d["y"], inv, np.zeros((30, 2), np.float32), res,
+                                              dtype), res)
+
+
+def test_aggregate_exact_on_dyadic_data():
+    rng = np.random.default_rng(52)
+    N, H, E, K = 25, 10, 5, 2
+    ids = I.random_ids(52, N, E, K)
+    _, _, perm, inv = O.dispatch(ids, E)
+    y = _dyadic(rng, (N * K, H))
+    res = _dyadic(rng, (N, H))
+    w = rng.choice([0.5, 0.25, -1.0], size=(N, K)).astype(np.float32)
+    want = (w[:, :, None].astype(np.float64) * y[inv.reshape(N, K)]).sum(axis=1) + res
+    np.testing.assert_array_equal(O.aggregate(y, inv, w, res, "f32"), want.astype(np.float32))
+
+
+# ---------------------------------------------------------------- grouped linear
+
+def _segments(counts):
+    return np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_grouped_linear_is_a_matmul_per_expert(dtype):
+    rng = np.random.default_rng(60)
+    E, H, F = 5, 24, 12
+    counts = np.array([7, 0, 13, 1, 9])
+    off = _segments(counts)
+    x = _store(rng.standard_normal((off[-1], H)), dtype)
+    W = _store(rng.standard_normal((E, F, H)) / np.sqrt(H), dtype)
+    y = O.grouped_linear(x, W, off, dtype)
+    xd, Wd = _decode(x, dtype), _decode(W, dtype)
+    u = 2.0 ** -8 if dtype == "bf16" else 2.0 ** -24
+    for e in range(E):
+        want = xd[off[e]:off[e + 1]] @ Wd[e].T          # library matmul, float64
+        got = _decode(y[off[e]:off[e + 1]], dtype)
+        assert (np.abs(got - want) <= u * np.abs(want) + 1e-12).all()
+
+
+def test_grouped_linear_exact_on_dyadic_data_and_row_subsets():
+    rng = np.random.default_rng(61)
+    E, H, F = 4, 8, 6
+    off = _segments([3, 5, 0, 4])
+    x = _dyadic(rng, (12, H))
+    W = _dyadic(rng, (E, F, H), -2, 3)
+    y = O.grouped_linear(x, W, off, "f32")
+    seg = np.repeat(np.arange(E), np.diff(off))
+    want = np.einsum("ph,pfh->pf", x.astype(np.float64), W[seg].astype(np.float64))
+    np.testing.assert_array_equal(y, want.astype(np.float32))
+    rows = np.array([11, 0, 7, 3], np.int32)
+    np.testing.assert_array_equal(O.grouped_linear(x, W, off, "f32", rows=rows), y[rows])
+
+
+def test_grouped_linear_identity_experts_return_their_rows():
+    rng = np.random.default_rng(62)
+    E, H = 3, 16
+    off = _segments([4, 6, 2])
+    x = _store(rng.standard_normal((12, H)), "bf16")
+    eye = _store(np.broadcast_to(np.eye(H), (E, H, H)), "bf16")
+    np.testing.assert_array_equal(O.grouped_linear(x, eye, off, "bf16"), x)
+
+
+def test_grouped_linear_rejects_bad_offsets():
+    x = np.zeros((4, 8), np.float32)
+    W = np.zeros((2, 3, 8), np.float32)
+    with pytest.raises(ValueError):
+        O.grouped_linear(x, W, np.array([0, 3, 2], np.int32), "f32")   # decreasing
+    with pytest.raises(ValueError):
+        O.grouped_linear(x, W, np.array([1, 2, 4], np.int32), "f32")   # not from 0

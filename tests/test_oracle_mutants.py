@@ -88,6 +88,15 @@ MUTANTS = [
     ("backward: dispatch gradient takes one slot",
      "acc += load_elem(dx_perm, rw * H + h, dtype);",
      "acc = load_elem(dx_perm, rw * H + h, dtype);"),
+    ("aggregate drops the residual",
+     "acc += load_elem(residual, n * (int64_t)H + h, dtype);",
+     "acc += 0.0;"),
+    ("grouped linear uses the next expert",
+     "while (!(offsets[e] <= p && p < offsets[e + 1])) ++e; /* the segment holding p */",
+     "while (!(offsets[e] <= p && p < offsets[e + 1])) ++e; e = (e + 1) % E;"),
+    ("grouped linear weight transposed",
+     "load_elem(weight, ((int64_t)e * F + f) * H + h, dtype);",
+     "load_elem(weight, ((int64_t)e * H + h % H) * F + f % F, dtype);"),
     ("bf16 decode shifted",
      "uint32_t u = (uint32_t)b << 16;",
      "uint32_t u = (uint32_t)b << 15;"),
