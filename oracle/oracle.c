@@ -81,6 +81,14 @@ static uint16_t double_to_bf16(double v) {
   return (uint16_t)(u >> 16);
 }
 
+/* Rounds v once to `dtype` and stores it at base[idx]. */
+static void store_elem(void *base, int64_t idx, int dtype, double v) {
+  if (dtype == ORACLE_BF16)
+    ((uint16_t *)base)[idx] = double_to_bf16(v);
+  else
+    ((float *)base)[idx] = (float)v;
+}
+
 /* ---- [R] router -------------------------------------------------------- */
 
 /*
@@ -365,10 +373,7 @@ int oracle_aggregate(const void *y, const int32_t *inv, const float *w, const vo
         acc += (double)w[n * K + k] * load_elem(y, src * H + h, dtype);
       }
       acc += load_elem(residual, n * (int64_t)H + h, dtype);
-      if (dtype == ORACLE_BF16)
-        ((uint16_t *)out)[n * (int64_t)H + h] = double_to_bf16(acc);
-      else
-        ((float *)out)[n * (int64_t)H + h] = (float)acc;
+      store_elem(out, n * (int64_t)H + h, dtype, acc);
     }
   }
   return 0;
@@ -408,23 +413,13 @@ int oracle_grouped_linear(const void *x_perm, const void *weight, const int32_t 
       for (int32_t h = 0; h < H; ++h)
         acc += load_elem(x_perm, p * H + h, dtype) *
                load_elem(weight, ((int64_t)e * F + f) * H + h, dtype);
-      if (dtype == ORACLE_BF16)
-        ((uint16_t *)y)[i * F + f] = double_to_bf16(acc);
-      else
-        ((float *)y)[i * F + f] = (float)acc;
+      store_elem(y, i * F + f, dtype, acc);
     }
   }
   return 0;
 }
 
 /* ---- backward of the path ([A] 6.2: the stages run backward in training) */
-
-static void store_elem(void *base, int64_t idx, int dtype, double v) {
-  if (dtype == ORACLE_BF16)
-    ((uint16_t *)base)[idx] = double_to_bf16(v);
-  else
-    ((float *)base)[idx] = (float)v;
-}
 
 /*
  * oracle_combine_backward: the gradient of out[n,:] = sum_k w[n,k] *
