@@ -209,6 +209,17 @@ moe_status_t moe_combine(const void *y, const int32_t *inv, const float *topk_w,
                          int64_t N, int32_t H, int32_t K, moe_dtype_t dtype,
                          void *out, void *stream);
 
+/*
+ * moe_aggregate -- forward_aggregate of [A]: the weighted expert output plus
+ * the residual connection
+ *   out[n,:] = sum_{k=0..K-1} topk_w[n,k] * y[inv[n*K+k], :]  +  residual[n,:]
+ * accumulated in fp32 (k ascending from 0, then the residual), rounded once
+ * to dtype.  Arguments as moe_combine; residual [N,H] dtype (may alias out).
+ */
+moe_status_t moe_aggregate(const void *y, const int32_t *inv, const float *topk_w,
+                           const void *residual, int64_t N, int32_t H, int32_t K,
+                           moe_dtype_t dtype, void *out, void *stream);
+
 /* ---------------------------------------------------------------- backward
  * Training runs the path's stages backward ([A], section 6.2 "The five
  * stages").  Each call below is the exact gradient of the forward call named

@@ -28,7 +28,7 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARGUMENT", 2: "MOE_ERR_UNSUPPORTED",
 EXPORTS = ("moe_status_string", "moe_route_workspace_size", "moe_route",
            "moe_dispatch_workspace_size", "moe_dispatch", "moe_route_dispatch_workspace_size",
            "moe_route_dispatch", "moe_ep_dispatch_workspace_size", "moe_ep_dispatch",
-           "moe_combine", "moe_combine_backward", "moe_dispatch_backward",
+           "moe_combine", "moe_aggregate", "moe_combine_backward", "moe_dispatch_backward",
            "moe_route_backward_workspace_size", "moe_route_backward")
 
 
@@ -74,6 +74,8 @@ def library() -> ctypes.CDLL:
         lib.moe_ep_dispatch.restype = ctypes.c_int
         lib.moe_combine.argtypes = [P, P, P, i64, i32, i32, ctypes.c_int, P, P]
         lib.moe_combine.restype = ctypes.c_int
+        lib.moe_aggregate.argtypes = [P, P, P, P, i64, i32, i32, ctypes.c_int, P, P]
+        lib.moe_aggregate.restype = ctypes.c_int
         lib.moe_combine_backward.argtypes = [P, P, P, P, i64, i32, i32, ctypes.c_int, P, P, P]
         lib.moe_combine_backward.restype = ctypes.c_int
         lib.moe_dispatch_backward.argtypes = [P, P, i64, i32, i32, ctypes.c_int, P, P]
@@ -271,6 +273,19 @@ def moe_combine(y: torch.Tensor, inv: torch.Tensor, topk_w: torch.Tensor,
         _dev(out, "out", y.dtype, N * H, dev), _stream(dev)))
 
 
+def moe_aggregate(y: torch.Tensor, inv: torch.Tensor, topk_w: torch.Tensor,
+                  residual: torch.Tensor, out: torch.Tensor) -> None:
+    """forward_aggregate: out [N,H] = sum_k topk_w[n,k] * y[inv[n*K+k]] + residual."""
+    N, K = topk_w.shape
+    H = y.shape[1]
+    dev = y.device
+    _check("moe_aggregate", library().moe_aggregate(
+        _dev(y, "y", y.dtype, N * K * H, dev), _dev(inv, "inv", torch.int32, N * K, dev),
+        _dev(topk_w, "topk_w", torch.float32, N * K, dev),
+        _dev(residual, "residual", y.dtype, N * H, dev), N, H, K, _dtype_code(y.dtype),
+        _dev(out, "out", y.dtype, N * H, dev), _stream(dev)))
+
+
 def moe_combine_backward(dout: torch.Tensor, y: torch.Tensor, inv: torch.Tensor,
                          topk_w: torch.Tensor, dy: torch.Tensor, dtopk_w: torch.Tensor) -> None:
     """Gradient of moe_combine: dy [N*K,H] (dispatched order), dtopk_w [N,K]."""
@@ -444,3 +459,11 @@ def route_backward(x_perm: torch.Tensor, gate_w: torch.Tensor, topk_ids: torch.T
     moe_route_backward(x_perm, gate_w, topk_ids, topk_w, dtopk_w, perm, offsets, inv, dx_perm,
                        dgate_w, dbias, dx, ws)
     return dgate_w, dbias, dx
+
+
+def aggregate(y: torch.Tensor, inv: torch.Tensor, topk_w: torch.Tensor,
+              residual: torch.Tensor) -> torch.Tensor:
+    """Allocate the output and run moe_aggregate."""
+    out = torch.empty_like(residual)
+    moe_aggregate(y, inv, topk_w, residual, out)
+    return out

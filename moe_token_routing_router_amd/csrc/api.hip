@@ -276,6 +276,21 @@ moe_status_t moe_combine(const void* y, const int32_t* inv, const float* topk_w,
                                       reinterpret_cast<hipStream_t>(stream)));
 }
 
+moe_status_t moe_aggregate(const void* y, const int32_t* inv, const float* topk_w,
+                           const void* residual, int64_t N, int32_t H, int32_t K,
+                           moe_dtype_t dtype, void* out, void* stream) {
+  if (!valid_dtype(dtype) || N < 0 || H <= 0 || K < 1) return MOE_ERR_INVALID_ARGUMENT;
+  if (N > 0 && (!y || !inv || !topk_w || !residual || !out)) return MOE_ERR_INVALID_ARGUMENT;
+  if (K > moe::kMaxExperts || N * (int64_t)K >= kMaxSlots || !row_ok(H, dtype))
+    return MOE_ERR_UNSUPPORTED;
+  if (!aligned(y, 16) || !aligned(out, 16) || !aligned(residual, 16) || !aligned(inv, 4) ||
+      !aligned(topk_w, 4))
+    return MOE_ERR_MISALIGNED;
+  if (N == 0) return MOE_OK;
+  return from_hip(moe::launch_combine(y, inv, topk_w, N, H, K, dtype == MOE_BF16, out,
+                                      reinterpret_cast<hipStream_t>(stream), residual));
+}
+
 // ---------------------------------------------------------------- backward
 
 moe_status_t moe_combine_backward(const void* dout, const void* y, const int32_t* inv,

@@ -82,12 +82,29 @@ __device__ __forceinline__ u32x4 pack_vec(const float (&acc)[BF16 ? 8 : 4]) {
 // KT > 0: K known at compile time; U output vectors per iteration, so U*KT
 // independent 16-byte gathers are in flight per lane.  KT == 0: any K, one
 // output vector per iteration, gathers in groups of 4.
+// With `res`, the residual row is added after the K expert terms (the
+// forward_aggregate of the same page: weighted expert output + residual).
+template <bool BF16>
+__device__ __forceinline__ void add_vec(float (&acc)[BF16 ? 8 : 4], u32x4 v) {
+  if constexpr (BF16) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc[2 * j] += bf16_lo(v[j]);
+      acc[2 * j + 1] += bf16_hi(v[j]);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j] += __uint_as_float(v[j]);
+  }
+}
+
 template <bool BF16, int KT, int U>
 __global__ __launch_bounds__(256) void combine_kernel(const u32x4* __restrict__ y,
                                                       const int32_t* __restrict__ inv,
                                                       const float* __restrict__ w, int64_t N,
                                                       int Krt, int row_vecs,
-                                                      u32x4* __restrict__ out) {
+                                                      const u32x4* res,  // may alias out
+                                                      u32x4* out) {
   constexpr int L = BF16 ? 8 : 4;
   const int K = KT > 0 ? KT : Krt;
   extern __shared__ int dyn[];  // rows[kCombineTokens*K] then weights
@@ -106,10 +123,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4* __restrict__ 
 
   const int total = ntok * row_vecs;
   u32x4* os = out + n0 * (int64_t)row_vecs;
+  const u32x4* rs = res ? res + n0 * (int64_t)row_vecs : nullptr;
   const u32x4 zero = {0u, 0u, 0u, 0u};
   if constexpr (KT > 0) {
     for (int base = tid; base < total; base += 256 * U) {
-      u32x4 v[U][KT];
+      u32x4 v[U][KT], rv[U];
       int tt[U], c[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -121,6 +139,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4* __restrict__ 
           const int rrow = lrow[tt[u] * KT + k];
           v[u][k] = rrow >= 0 ? ld_vec(y + (int64_t)rrow * row_vecs + c[u]) : zero;
         }
+        rv[u] = rs ? ld_vec(rs + idx) : zero;
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -130,6 +149,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4* __restrict__ 
 #pragma unroll
         for (int k = 0; k < KT; ++k)
           if (lrow[tt[u] * KT + k] >= 0) fma_vec<BF16>(acc, lw[tt[u] * KT + k], v[u][k]);
+        if (rs) add_vec<BF16>(acc, rv[u]);
         if (base + u * 256 < total) st_vec(os + (int64_t)tt[u] * row_vecs + c[u], pack_vec<BF16>(acc));
       }
     }
@@ -154,6 +174,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4* __restrict__ 
       }
       for (; k < K; ++k)
         if (rr[k] >= 0) fma_vec<BF16>(acc, ww[k], ld_vec(y + (int64_t)rr[k] * row_vecs + c));
+      if (rs) add_vec<BF16>(acc, ld_vec(rs + idx));
       st_vec(os + (int64_t)tt * row_vecs + c, pack_vec<BF16>(acc));
     }
   }
@@ -161,34 +182,34 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4* __restrict__ 
 
 template <bool BF16, int KT, int U>
 hipError_t launch_k(const void* y, const int32_t* inv, const float* w, int64_t N, int H, int K,
-                    void* out, hipStream_t s) {
+                    const void* res, void* out, hipStream_t s) {
   const int64_t blocks = (N + kCombineTokens - 1) / kCombineTokens;
   const int row_vecs = BF16 ? H / 8 : H / 4;
   const size_t dyn = (sizeof(int) + sizeof(float)) * (size_t)kCombineTokens * K;
   hipLaunchKernelGGL((combine_kernel<BF16, KT, U>), dim3((unsigned)blocks), dim3(256), dyn, s,
                      reinterpret_cast<const u32x4*>(y), inv, w, N, K, row_vecs,
-                     reinterpret_cast<u32x4*>(out));
+                     reinterpret_cast<const u32x4*>(res), reinterpret_cast<u32x4*>(out));
   return hipGetLastError();
 }
 
 template <bool BF16>
 hipError_t launch_dtype(const void* y, const int32_t* inv, const float* w, int64_t N, int H,
-                        int K, void* out, hipStream_t s) {
+                        int K, const void* res, void* out, hipStream_t s) {
   switch (K) {
-    case 1: return launch_k<BF16, 1, 8>(y, inv, w, N, H, K, out, s);
-    case 2: return launch_k<BF16, 2, MOE_COMBINE_U2>(y, inv, w, N, H, K, out, s);
-    case 4: return launch_k<BF16, 4, 2>(y, inv, w, N, H, K, out, s);
-    case 8: return launch_k<BF16, 8, 2>(y, inv, w, N, H, K, out, s);
-    default: return launch_k<BF16, 0, 1>(y, inv, w, N, H, K, out, s);
+    case 1: return launch_k<BF16, 1, 8>(y, inv, w, N, H, K, res, out, s);
+    case 2: return launch_k<BF16, 2, MOE_COMBINE_U2>(y, inv, w, N, H, K, res, out, s);
+    case 4: return launch_k<BF16, 4, 2>(y, inv, w, N, H, K, res, out, s);
+    case 8: return launch_k<BF16, 8, 2>(y, inv, w, N, H, K, res, out, s);
+    default: return launch_k<BF16, 0, 1>(y, inv, w, N, H, K, res, out, s);
   }
 }
 
 }  // namespace
 
 hipError_t launch_combine(const void* y, const int32_t* inv, const float* w, int64_t N, int H,
-                          int K, bool bf16, void* out, hipStream_t s) {
-  return bf16 ? launch_dtype<true>(y, inv, w, N, H, K, out, s)
-              : launch_dtype<false>(y, inv, w, N, H, K, out, s);
+                          int K, bool bf16, void* out, hipStream_t s, const void* residual) {
+  return bf16 ? launch_dtype<true>(y, inv, w, N, H, K, residual, out, s)
+              : launch_dtype<false>(y, inv, w, N, H, K, residual, out, s);
 }
 
 }  // namespace moe

@@ -192,9 +192,11 @@ hipError_t launch_ep_finish(const int32_t* ids, const int32_t* perm, const int32
                             int K, int E, int R, int32_t* send_tok, int32_t* send_row,
                             int32_t* expand_idx, hipStream_t s);
 
-// Combine (w may be null: unit weights, the dispatch backward).
+// Combine (w may be null: unit weights, the dispatch backward; residual, if
+// given, is added after the expert terms: forward_aggregate).
 hipError_t launch_combine(const void* y, const int32_t* inv, const float* w, int64_t N, int H,
-                          int K, bool bf16, void* out, hipStream_t s);
+                          int K, bool bf16, void* out, hipStream_t s,
+                          const void* residual = nullptr);
 
 // Backward (backward.hip).
 hipError_t launch_combine_backward(const void* dout, const void* y, const int32_t* inv,

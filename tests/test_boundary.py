@@ -186,6 +186,17 @@ def test_combine_validation(lib):
     assert combine(lib, N=0) == OK             # empty: nothing to do, nothing enqueued
 
 
+def test_aggregate_validation(lib):
+    ag = lambda **k: lib.moe_aggregate(
+        k.get("y", A), k.get("inv", A2), k.get("w", A2), k.get("res", A), k.get("N", 4),
+        k.get("H", 16), k.get("K", 2), k.get("dt", BF16), k.get("out", A), None)
+    assert ag(res=None) == INVALID
+    assert ag(K=0) == INVALID
+    assert ag(H=4) == UNSUPPORTED
+    assert ag(res=MIS8) == MISALIGNED
+    assert ag(N=0) == OK
+
+
 def test_backward_validation(lib):
     cb = lambda **k: lib.moe_combine_backward(
         k.get("dout", A), k.get("y", A), k.get("inv", A2), k.get("w", A2), k.get("N", 4),

@@ -372,3 +372,32 @@ def test_ep_dispatch_out_of_range_ids():
     np.testing.assert_array_equal(gsc, np.bincount([r for _, r in pairs], minlength=R))
     slots = np.nonzero(valid)[0]
     np.testing.assert_array_equal(gxs[gsr[slots]], x[slots // K])
+
+
+# ------------------------------------------------------------ forward_aggregate
+
+@pytest.mark.parametrize("name", WORKLOADS)
+def test_aggregate_full_size(name):
+    d = workload(name)
+    o = d["o"]
+    print(f"[aggregate] {name}", flush=True)
+    dt = d["dtype"]
+    out = L.aggregate(to_dev(d["y"], dt), torch.from_numpy(o["inv"]).cuda(),
+                      torch.from_numpy(o["w"]).cuda(), to_dev(d["x"], dt))
+    torch.cuda.synchronize()
+    check_combine(from_dev(out), O.aggregate(d["y"], o["inv"], o["w"], d["x"], dt), dt)
+
+
+@pytest.mark.parametrize("N,H,E,K,dtype,bias", EDGE[:6])
+def test_aggregate_edge_cases_and_in_place(N, H, E, K, dtype, bias):
+    print(f"[aggregate edge] N={N} H={H} E={E} K={K} {dtype}", flush=True)
+    d = I.random_case(N * 3 + H, N, H, E, K, dtype, bias=bias)
+    ids = I.random_ids(N, N, E, K)
+    _, _, _, inv = O.dispatch(ids, E)
+    w = np.random.default_rng(N).random((N, K)).astype(np.float32)
+    ref = O.aggregate(d["y"], inv, w, d["x"], dtype)
+    res = to_dev(d["x"], dtype)
+    L.moe_aggregate(to_dev(d["y"], dtype), torch.from_numpy(inv).cuda(),
+                    torch.from_numpy(w).cuda(), res, res)  # out aliases the residual
+    torch.cuda.synchronize()
+    check_combine(from_dev(res), ref, dtype)
