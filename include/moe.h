@@ -220,6 +220,27 @@ moe_status_t moe_aggregate(const void *y, const int32_t *inv, const float *topk_
                            const void *residual, int64_t N, int32_t H, int32_t K,
                            moe_dtype_t dtype, void *out, void *stream);
 
+/*
+ * moe_grouped_linear -- the expert layer between dispatch and combine ([A]
+ * section 6.1, forward_mlp on the gathered tokens; the MoE GroupLinear of the
+ * same page), one linear map per expert over its contiguous segment of the
+ * dispatched rows:
+ *   y[p, f] = sum_h x_perm[p, h] * weight[e][f][h]   for offsets[e] <= p < offsets[e+1]
+ * bf16: products exact, fp32 accumulation on the matrix cores, one rounding;
+ * fp32: fp32 FMAs with h ascending.
+ *   x_perm [T,H] dtype   dispatched rows (moe_dispatch's x_perm)
+ *   weight [E,F,H] dtype row f of expert e holds the weights of output f
+ *   offsets [E+1] int32  moe_dispatch's offsets (PRECONDITION 0 = offsets[0]
+ *                        <= ... <= offsets[E] <= T; values are clamped to
+ *                        [0, T], so inconsistent offsets give wrong rows but
+ *                        never an access outside the buffers)
+ *   y [T,F] dtype        out; rows p >= offsets[E] are not written
+ * F must make a row a multiple of 16 bytes, like H.
+ */
+moe_status_t moe_grouped_linear(const void *x_perm, const void *weight, const int32_t *offsets,
+                                int64_t T, int32_t H, int32_t E, int32_t F, moe_dtype_t dtype,
+                                void *y, void *stream);
+
 /* ---------------------------------------------------------------- backward
  * Training runs the path's stages backward ([A], section 6.2 "The five
  * stages").  Each call below is the exact gradient of the forward call named

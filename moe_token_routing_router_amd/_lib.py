@@ -28,7 +28,8 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARGUMENT", 2: "MOE_ERR_UNSUPPORTED",
 EXPORTS = ("moe_status_string", "moe_route_workspace_size", "moe_route",
            "moe_dispatch_workspace_size", "moe_dispatch", "moe_route_dispatch_workspace_size",
            "moe_route_dispatch", "moe_ep_dispatch_workspace_size", "moe_ep_dispatch",
-           "moe_combine", "moe_aggregate", "moe_combine_backward", "moe_dispatch_backward",
+           "moe_combine", "moe_aggregate", "moe_grouped_linear", "moe_combine_backward",
+           "moe_dispatch_backward",
            "moe_route_backward_workspace_size", "moe_route_backward")
 
 
@@ -74,6 +75,8 @@ def library() -> ctypes.CDLL:
         lib.moe_ep_dispatch.restype = ctypes.c_int
         lib.moe_combine.argtypes = [P, P, P, i64, i32, i32, ctypes.c_int, P, P]
         lib.moe_combine.restype = ctypes.c_int
+        lib.moe_grouped_linear.argtypes = [P, P, P, i64, i32, i32, i32, ctypes.c_int, P, P]
+        lib.moe_grouped_linear.restype = ctypes.c_int
         lib.moe_aggregate.argtypes = [P, P, P, P, i64, i32, i32, ctypes.c_int, P, P]
         lib.moe_aggregate.restype = ctypes.c_int
         lib.moe_combine_backward.argtypes = [P, P, P, P, i64, i32, i32, ctypes.c_int, P, P, P]
@@ -286,6 +289,22 @@ def moe_aggregate(y: torch.Tensor, inv: torch.Tensor, topk_w: torch.Tensor,
         _dev(out, "out", y.dtype, N * H, dev), _stream(dev)))
 
 
+def moe_grouped_linear(x_perm: torch.Tensor, weight: torch.Tensor, offsets: torch.Tensor,
+                       y: torch.Tensor) -> None:
+    """Expert layer: y[p] = weight[e] @ x_perm[p] for the rows of expert e's
+    segment (offsets); weight [E,F,H]."""
+    T, H = x_perm.shape
+    E, F, H2 = weight.shape
+    if H2 != H:
+        raise ValueError("weight must be [E, F, H]")
+    dev = x_perm.device
+    dt = x_perm.dtype
+    _check("moe_grouped_linear", library().moe_grouped_linear(
+        _dev(x_perm, "x_perm", dt, T * H, dev), _dev(weight, "weight", dt, E * F * H, dev),
+        _dev(offsets, "offsets", torch.int32, E + 1, dev), T, H, E, F, _dtype_code(dt),
+        _dev(y, "y", dt, T * F, dev), _stream(dev)))
+
+
 def moe_combine_backward(dout: torch.Tensor, y: torch.Tensor, inv: torch.Tensor,
                          topk_w: torch.Tensor, dy: torch.Tensor, dtopk_w: torch.Tensor) -> None:
     """Gradient of moe_combine: dy [N*K,H] (dispatched order), dtopk_w [N,K]."""
@@ -467,3 +486,12 @@ def aggregate(y: torch.Tensor, inv: torch.Tensor, topk_w: torch.Tensor,
     out = torch.empty_like(residual)
     moe_aggregate(y, inv, topk_w, residual, out)
     return out
+
+
+def grouped_linear(x_perm: torch.Tensor, weight: torch.Tensor,
+                   offsets: torch.Tensor) -> torch.Tensor:
+    """Allocate y [T,F] (zero-filled: rows past offsets[E] are not written)
+    and run moe_grouped_linear."""
+    y = torch.zeros((x_perm.shape[0], weight.shape[1]), dtype=x_perm.dtype, device=x_perm.device)
+    moe_grouped_linear(x_perm, weight, offsets, y)
+    return y

@@ -291,6 +291,22 @@ moe_status_t moe_aggregate(const void* y, const int32_t* inv, const float* topk_
                                       reinterpret_cast<hipStream_t>(stream), residual));
 }
 
+moe_status_t moe_grouped_linear(const void* x_perm, const void* weight, const int32_t* offsets,
+                                int64_t T, int32_t H, int32_t E, int32_t F, moe_dtype_t dtype,
+                                void* y, void* stream) {
+  if (!valid_dtype(dtype) || T < 0 || H <= 0 || E <= 0 || F <= 0) return MOE_ERR_INVALID_ARGUMENT;
+  if (!offsets || (T > 0 && (!x_perm || !weight || !y))) return MOE_ERR_INVALID_ARGUMENT;
+  if (E > moe::kMaxExperts || T >= kMaxSlots || !row_ok(H, dtype) || !row_ok(F, dtype))
+    return MOE_ERR_UNSUPPORTED;
+  if (dtype == MOE_F32 && (T * (int64_t)F + 255) / 256 >= kMaxSlots) return MOE_ERR_UNSUPPORTED;
+  if (!aligned(x_perm, 16) || !aligned(weight, 16) || !aligned(y, 16) || !aligned(offsets, 4))
+    return MOE_ERR_MISALIGNED;
+  if (T == 0) return MOE_OK;
+  return from_hip(moe::launch_grouped_linear(x_perm, weight, offsets, T, H, E, F,
+                                             dtype == MOE_BF16, y,
+                                             reinterpret_cast<hipStream_t>(stream)));
+}
+
 // ---------------------------------------------------------------- backward
 
 moe_status_t moe_combine_backward(const void* dout, const void* y, const int32_t* inv,

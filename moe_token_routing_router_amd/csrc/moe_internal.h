@@ -198,6 +198,13 @@ hipError_t launch_combine(const void* y, const int32_t* inv, const float* w, int
                           int K, bool bf16, void* out, hipStream_t s,
                           const void* residual = nullptr);
 
+// Grouped expert linear layer (grouped_gemm.hip): y rows p < offsets[E]
+// (offsets clamped to [0, T]) of x_perm [T,H] times weight[e] [F,H]^T.
+int64_t grouped_gemm_max_tiles(int64_t T, int E);
+hipError_t launch_grouped_linear(const void* x_perm, const void* weight, const int32_t* offsets,
+                                 int64_t T, int H, int E, int F, bool bf16, void* y,
+                                 hipStream_t s);
+
 // Backward (backward.hip).
 hipError_t launch_combine_backward(const void* dout, const void* y, const int32_t* inv,
                                    const float* w, int64_t N, int H, int K, bool bf16, void* dy,

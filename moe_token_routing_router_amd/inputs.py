@@ -152,6 +152,16 @@ def random_case(seed: int, N: int, H: int, E: int, K: int, dtype: str,
     return d
 
 
+def expert_weights(seed: int, E: int, F: int, H: int, dtype: str) -> np.ndarray:
+    """Synthetic expert-layer weights [E,F,H] ~ N(0, 1/H) (random init of the
+    expert layer; no checkpoint), drawn expert by expert."""
+    rng = np.random.default_rng(seed)
+    out = np.empty((E, F, H), np.float32 if dtype == "f32" else np.uint16)
+    for e in range(E):
+        out[e] = _normal_rows(rng, F, H, dtype, scale=1.0 / math.sqrt(H))
+    return out
+
+
 def random_ids(seed: int, N: int, E: int, K: int, skew: float = 0.0) -> np.ndarray:
     """Distinct expert ids per token, [N,K] int32; with skew > 0 the experts
     are drawn with Zipf-like weights so some segments are large and some

@@ -197,6 +197,21 @@ def test_aggregate_validation(lib):
     assert ag(N=0) == OK
 
 
+def test_grouped_linear_validation(lib):
+    gl = lambda **k: lib.moe_grouped_linear(
+        k.get("x", A), k.get("w", A), k.get("off", A2), k.get("T", 64), k.get("H", 16),
+        k.get("E", 4), k.get("F", 32), k.get("dt", BF16), k.get("y", A), None)
+    assert gl(off=None) == INVALID
+    assert gl(w=None) == INVALID
+    assert gl(F=0) == INVALID
+    assert gl(T=-1) == INVALID
+    assert gl(E=257) == UNSUPPORTED
+    assert gl(F=12) == UNSUPPORTED          # 24-byte output rows
+    assert gl(y=MIS8) == MISALIGNED
+    assert gl(off=MIS) == MISALIGNED
+    assert gl(T=0) == OK
+
+
 def test_backward_validation(lib):
     cb = lambda **k: lib.moe_combine_backward(
         k.get("dout", A), k.get("y", A), k.get("inv", A2), k.get("w", A2), k.get("N", 4),
