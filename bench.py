@@ -19,6 +19,7 @@ HIP events on the stream it runs on) and the CPU oracle's throughput on a
 bounded sample of the same workload, timed on this host (cpu_baseline).
 """
 import argparse
+import math
 import ctypes
 import hashlib
 import json
@@ -156,31 +157,6 @@ def main():
                   x_perm=torch.empty((T, H), dtype=tdt, device=dev),
                   out=torch.empty((N, H), dtype=tdt, device=dev))
         sets.append(st)
-    # expert-parallel send metadata (measured on its own, not part of the step)
-    R = EP_RANKS if E % EP_RANKS == 0 else 1
-    cap = N * min(K, R)
-    for st in sets:
-        st.update(send_counts=torch.empty((R,), dtype=torch.int32, device=dev),
-                  send_offsets=torch.empty((R + 1,), dtype=torch.int32, device=dev),
-                  send_tok=torch.empty((cap,), dtype=torch.int32, device=dev),
-                  send_row=torch.empty((T,), dtype=torch.int32, device=dev),
-                  expand_idx=torch.empty((T,), dtype=torch.int32, device=dev),
-                  x_send=torch.empty((cap, H), dtype=tdt, device=dev))
-    ews = torch.empty((L.moe_ep_dispatch_workspace_size(N, E, K, R),), dtype=torch.uint8,
-                      device=dev)
-    # backward of the path (measured on its own): upstream gradients are the
-    # other sets' rows (dout = a token matrix, dx_perm = a dispatched matrix)
-    for s_i, st in enumerate(sets):
-        other = sets[(s_i + 1) % N_SETS] if N_SETS > 1 else st
-        st.update(dout=other["x"], dx_perm=other["y"],
-                  dtopk_w=torch.randn((N, K), dtype=torch.float32, device=dev),
-                  dy=torch.empty((T, H), dtype=tdt, device=dev),
-                  dw=torch.empty((N, K), dtype=torch.float32, device=dev),
-                  dx=torch.empty((N, H), dtype=tdt, device=dev),
-                  dgate=torch.empty((H, E), dtype=torch.float32, device=dev),
-                  dbias=torch.empty((E,), dtype=torch.float32, device=dev))
-    bws = torch.empty((L.moe_route_backward_workspace_size(N, H, E, K, tdt),), dtype=torch.uint8,
-                      device=dev)
     rws = torch.empty((max(1, L.moe_route_workspace_size(H, E, tdt)),), dtype=torch.uint8,
                       device=dev)
     dws = torch.empty((L.moe_dispatch_workspace_size(N, E, K),), dtype=torch.uint8, device=dev)
@@ -195,14 +171,6 @@ def main():
         L.moe_route_dispatch(st["x"], gw, bias, K, st["ids"], st["w"], st["counts"],
                              st["offsets"], st["perm"], st["inv"], st["x_perm"], fws)
         L.moe_combine(st["y"], st["inv"], st["w"], st["out"])
-        L.moe_ep_dispatch(st["ids"], st["x"], E, R, st["counts"], st["offsets"], st["perm"],
-                          st["inv"], st["send_counts"], st["send_offsets"], st["send_tok"],
-                          st["send_row"], st["expand_idx"], st["x_send"], ews)
-        L.moe_combine_backward(st["dout"], st["y"], st["inv"], st["w"], st["dy"], st["dw"])
-        L.moe_dispatch_backward(st["dx_perm"], st["inv"], st["dx"])
-        L.moe_route_backward(st["x_perm"], gw, st["ids"], st["w"], st["dtopk_w"], st["perm"],
-                             st["offsets"], st["inv"], st["dx_perm"], st["dgate"], st["dbias"],
-                             st["dx"], bws)
     torch.cuda.synchronize()
 
     # then call the C ABI directly with the pointers (no per-call Python checks)
@@ -221,23 +189,9 @@ def main():
             route_dispatch=(P(st["x"]), P(gw), P(bias), N, H, E, K, dt, P(st["ids"]),
                             P(st["w"]), P(st["counts"]), P(st["offsets"]), P(st["perm"]),
                             P(st["inv"]), P(st["x_perm"]), P(fws), fws.numel(), sp),
-            combine=(P(st["y"]), P(st["inv"]), P(st["w"]), N, H, K, dt, P(st["out"]), sp),
-            ep_dispatch=(P(st["ids"]), P(st["x"]), N, H, E, K, R, dt, P(st["counts"]),
-                         P(st["offsets"]), P(st["perm"]), P(st["inv"]), P(st["send_counts"]),
-                         P(st["send_offsets"]), P(st["send_tok"]), P(st["send_row"]),
-                         P(st["expand_idx"]), P(st["x_send"]), P(ews), ews.numel(), sp),
-            combine_backward=(P(st["dout"]), P(st["y"]), P(st["inv"]), P(st["w"]), N, H, K, dt,
-                              P(st["dy"]), P(st["dw"]), sp),
-            dispatch_backward=(P(st["dx_perm"]), P(st["inv"]), N, H, K, dt, P(st["dx"]), sp),
-            route_backward=(P(st["x_perm"]), P(gw), P(st["ids"]), P(st["w"]), P(st["dtopk_w"]),
-                            P(st["perm"]), P(st["offsets"]), P(st["inv"]), P(st["dx_perm"]), N,
-                            H, E, K, dt, P(st["dgate"]), P(st["dbias"]), P(st["dx"]), P(bws),
-                            bws.numel(), sp)))
+            combine=(P(st["y"]), P(st["inv"]), P(st["w"]), N, H, K, dt, P(st["out"]), sp)))
     fn = {"route": lib.moe_route, "dispatch": lib.moe_dispatch,
-          "route_dispatch": lib.moe_route_dispatch, "combine": lib.moe_combine,
-          "ep_dispatch": lib.moe_ep_dispatch, "combine_backward": lib.moe_combine_backward,
-          "dispatch_backward": lib.moe_dispatch_backward,
-          "route_backward": lib.moe_route_backward}
+          "route_dispatch": lib.moe_route_dispatch, "combine": lib.moe_combine}
 
     def call(name, i):
         status = fn[name](*calls[i % N_SETS][name])
@@ -278,8 +232,85 @@ def main():
     # input sets) between one pair of HIP events on the launch stream: the
     # average duration of one call
     stage_ms = {}
-    for name in ("route_dispatch", "combine", "route", "dispatch", "ep_dispatch",
-                 "combine_backward", "dispatch_backward", "route_backward"):
+    for name in ("route_dispatch", "combine", "route", "dispatch"):
+        for i in range(3):
+            call(name, i)
+        _, ms = timed(lambda i, n=name: call(n, i), args.steps)
+        stage_ms[name] = ms / args.steps
+
+    # The other calls of the library, each measured on its own.  Their
+    # buffers are allocated only now, so the timed regions above run with the
+    # same memory layout whether or not these exist.
+    # expert-parallel send metadata (measured on its own, not part of the step)
+    R = EP_RANKS if E % EP_RANKS == 0 else 1
+    cap = N * min(K, R)
+    for st in sets:
+        st.update(send_counts=torch.empty((R,), dtype=torch.int32, device=dev),
+                  send_offsets=torch.empty((R + 1,), dtype=torch.int32, device=dev),
+                  send_tok=torch.empty((cap,), dtype=torch.int32, device=dev),
+                  send_row=torch.empty((T,), dtype=torch.int32, device=dev),
+                  expand_idx=torch.empty((T,), dtype=torch.int32, device=dev),
+                  x_send=torch.empty((cap, H), dtype=tdt, device=dev))
+    ews = torch.empty((L.moe_ep_dispatch_workspace_size(N, E, K, R),), dtype=torch.uint8,
+                      device=dev)
+    # backward of the path (measured on its own): upstream gradients are the
+    # other sets' rows (dout = a token matrix, dx_perm = a dispatched matrix)
+    for s_i, st in enumerate(sets):
+        other = sets[(s_i + 1) % N_SETS] if N_SETS > 1 else st
+        st.update(dout=other["x"], dx_perm=other["y"],
+                  dtopk_w=torch.randn((N, K), dtype=torch.float32, device=dev),
+                  dy=torch.empty((T, H), dtype=tdt, device=dev),
+                  dw=torch.empty((N, K), dtype=torch.float32, device=dev),
+                  dx=torch.empty((N, H), dtype=tdt, device=dev),
+                  dgate=torch.empty((H, E), dtype=torch.float32, device=dev),
+                  dbias=torch.empty((E,), dtype=torch.float32, device=dev))
+    bws = torch.empty((L.moe_route_backward_workspace_size(N, H, E, K, tdt),), dtype=torch.uint8,
+                      device=dev)
+    # the expert layer between dispatch and combine (measured on its own):
+    # one linear map per expert, F = H outputs, synthetic N(0, 1/H) weights
+    # drawn on the device from a seeded generator (no checkpoint)
+    F = H
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1234)
+    wexp = (torch.randn((E, F, H), generator=gen, device=dev, dtype=torch.float32)
+            / math.sqrt(H)).to(tdt)
+    for st in sets:
+        st.update(yexp=torch.empty((T, F), dtype=tdt, device=dev),
+                  agg=torch.empty((N, H), dtype=tdt, device=dev))
+    for st in sets:
+        L.moe_ep_dispatch(st["ids"], st["x"], E, R, st["counts"], st["offsets"], st["perm"],
+                          st["inv"], st["send_counts"], st["send_offsets"], st["send_tok"],
+                          st["send_row"], st["expand_idx"], st["x_send"], ews)
+        L.moe_grouped_linear(st["x_perm"], wexp, st["offsets"], st["yexp"])
+        L.moe_aggregate(st["y"], st["inv"], st["w"], st["x"], st["agg"])
+        L.moe_combine_backward(st["dout"], st["y"], st["inv"], st["w"], st["dy"], st["dw"])
+        L.moe_dispatch_backward(st["dx_perm"], st["inv"], st["dx"])
+        L.moe_route_backward(st["x_perm"], gw, st["ids"], st["w"], st["dtopk_w"], st["perm"],
+                             st["offsets"], st["inv"], st["dx_perm"], st["dgate"], st["dbias"],
+                             st["dx"], bws)
+    torch.cuda.synchronize()
+    for c, st in zip(calls, sets):
+        c.update(
+            ep_dispatch=(P(st["ids"]), P(st["x"]), N, H, E, K, R, dt, P(st["counts"]),
+                         P(st["offsets"]), P(st["perm"]), P(st["inv"]), P(st["send_counts"]),
+                         P(st["send_offsets"]), P(st["send_tok"]), P(st["send_row"]),
+                         P(st["expand_idx"]), P(st["x_send"]), P(ews), ews.numel(), sp),
+            grouped_linear=(P(st["x_perm"]), P(wexp), P(st["offsets"]), T, H, E, F, dt,
+                            P(st["yexp"]), sp),
+            aggregate=(P(st["y"]), P(st["inv"]), P(st["w"]), P(st["x"]), N, H, K, dt,
+                       P(st["agg"]), sp),
+            combine_backward=(P(st["dout"]), P(st["y"]), P(st["inv"]), P(st["w"]), N, H, K, dt,
+                              P(st["dy"]), P(st["dw"]), sp),
+            dispatch_backward=(P(st["dx_perm"]), P(st["inv"]), N, H, K, dt, P(st["dx"]), sp),
+            route_backward=(P(st["x_perm"]), P(gw), P(st["ids"]), P(st["w"]), P(st["dtopk_w"]),
+                            P(st["perm"]), P(st["offsets"]), P(st["inv"]), P(st["dx_perm"]), N,
+                            H, E, K, dt, P(st["dgate"]), P(st["dbias"]), P(st["dx"]), P(bws),
+                            bws.numel(), sp))
+    fn.update(ep_dispatch=lib.moe_ep_dispatch, combine_backward=lib.moe_combine_backward,
+              grouped_linear=lib.moe_grouped_linear, aggregate=lib.moe_aggregate,
+              dispatch_backward=lib.moe_dispatch_backward, route_backward=lib.moe_route_backward)
+    for name in ("ep_dispatch", "combine_backward", "dispatch_backward", "route_backward",
+                 "aggregate", "grouped_linear"):
         for i in range(3):
             call(name, i)
         _, ms = timed(lambda i, n=name: call(n, i), args.steps)
@@ -300,6 +331,8 @@ def main():
     # ep_dispatch: ids in, x read once, S deduplicated rows out, the expert
     # metadata (counts, offsets, perm, inv) and the send metadata (send
     # counts/offsets, send_tok [S], send_row and expand_idx [N*K])
+    alg["aggregate"] = alg["combine"] + N * H * b
+    alg["grouped_linear"] = T * H * b + E * F * H * b + T * F * b + (E + 1) * 4
     # backward: what each call must move (its scratch excluded)
     alg["combine_backward"] = N * H * b + 2 * T * H * b + 3 * T * 4
     alg["dispatch_backward"] = T * H * b + N * H * b + T * 4
@@ -322,6 +355,11 @@ def main():
             "alg_GBs": round(alg["dispatch"] / marg / 1e6, 1),
             "hbm_frac": round(alg["dispatch"] / marg / 1e6 / HBM_PEAK_GBS, 4)}
     stages["ep_dispatch"].update(ep_size=R, send_rows=S, slots=T)
+    g_flops = 2.0 * T * H * F
+    stages["grouped_linear"].update(
+        F=F, tflops=round(g_flops / (stage_ms["grouped_linear"] * 1e-3) / 1e12, 1),
+        mfma_frac=round(g_flops / (stage_ms["grouped_linear"] * 1e-3)
+                        / (BF16_MFMA_PEAK_TFLOPS * 1e12), 4))
     r_flops = 2.0 * N * H * E
     stages["route"]["mfma_util"] = round(
         r_flops / (stage_ms["route"] * 1e-3) / (BF16_MFMA_PEAK_TFLOPS * 1e12), 4)
