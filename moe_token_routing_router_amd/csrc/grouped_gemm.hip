@@ -9,17 +9,22 @@
 // the expert-contiguous layout is what makes the rows of one expert a dense
 // operand.  The pages' GroupLinear is an FP8 DeepGEMM kernel for NVIDIA
 // parts; this one is bf16 on CDNA4 matrix cores:
-//  * a workgroup computes a 128 x 128 tile of one expert's output; its
-//    m-tiles are numbered expert by expert (the 128-row tiles of expert e
-//    start at tile sum_{e'<e} ceil(count[e'] / 128)), so each expert's
-//    ragged last tile stays inside its segment;
+//  * a workgroup computes a BM x BN tile of one expert's output (256 x 256
+//    once there are enough tiles to fill the chip, else 128 x 128); its
+//    m-tiles are numbered expert by expert (the BM-row tiles of expert e
+//    start at tile sum_{e'<e} ceil(count[e'] / BM)), so each expert's ragged
+//    last tile stays inside its segment;
+//  * tiles are ordered for the 8 XCDs: each XCD gets whole groups of two
+//    consecutive m-tiles with all their n-tiles, so a group's token rows and
+//    its expert's weight rows are fetched into that XCD's L2 once;
 //  * both operands are K-contiguous rows (token rows of x_perm, weight rows
 //    of one output each), loaded with coalesced 16-byte loads into LDS tiles
 //    with an XOR swizzle (16-byte chunk c of row r at c ^ (r & 7)), double
-//    buffered: the next 64-wide K step is loaded into registers while the
-//    current one feeds the matrix cores;
-//  * 4 waves, each a 64 x 64 quarter: 4 x 4 v_mfma_f32_16x16x32_bf16 tiles,
-//    fp32 accumulation, one rounding to bf16 at the end.
+//    buffered: the next 64-wide K step is loaded while the current one feeds
+//    the matrix cores (through registers, or with MOE_GEMM_DMA straight into
+//    LDS with global_load_lds_dwordx4 -- measured equal);
+//  * 4 waves, each a (BM/2) x (BN/2) block of v_mfma_f32_16x16x32_bf16
+//    tiles, fp32 accumulation, one rounding to bf16 at the end.
 // fp32 inputs use a plain fp32 FMA kernel (one output per thread).
 #include "moe_internal.h"
 
@@ -29,15 +34,28 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int GBM = 128;  // rows (tokens) per tile
-constexpr int GBN = 128;  // outputs per tile
 constexpr int GBK = 64;   // K step (h)
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4 u) { return __builtin_bit_cast(bf16x8_t, u); }
 
-// This workgroup's expert and rows: tiles are numbered expert by expert.
-// Offsets are clamped to [0, T] (inconsistent ones give wrong rows, never an
-// access outside x_perm or y).  Returns false if the id is past the last tile.
+#ifndef MOE_GEMM_SWZ
+#define MOE_GEMM_SWZ 0
+#endif
+// LDS swizzle of a 128-byte tile row: 16-byte chunk c of row r is stored in
+// slot c ^ swz(r)
+__device__ __forceinline__ int swz(int r) { return MOE_GEMM_SWZ ? (r >> 1) & 7 : r & 7; }
+
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes land
+// at lds_base + 16*l (lds_base must be the same in every lane of the wave).
+__device__ __forceinline__ void lds_dma16(const void* src, char* lds_base) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_base, 16, 0,
+                                   0);
+}
+
+// This workgroup's expert and rows: tiles of BM rows are numbered expert by
+// expert.  Offsets are clamped to [0, T] (inconsistent ones give wrong rows,
+// never an access outside x_perm or y).  Returns false past the last tile.
+template <int BM>
 __device__ __forceinline__ bool tile_of(const int32_t* offsets, int E, int64_t T, int id,
                                         int* s_e, int64_t* s_m0, int* s_rows, int* s_scan) {
   const int tid = threadIdx.x;
@@ -45,7 +63,7 @@ __device__ __forceinline__ bool tile_of(const int32_t* offsets, int E, int64_t T
   const int wid = tid >> 6;
   const int64_t o0 = tid < E ? min(max((int64_t)offsets[tid], (int64_t)0), T) : 0;
   const int64_t o1 = tid < E ? min(max((int64_t)offsets[tid + 1], o0), T) : 0;
-  const int nt = (int)((o1 - o0 + GBM - 1) / GBM);
+  const int nt = (int)((o1 - o0 + BM - 1) / BM);
   const int incl = wave_inclusive_sum(nt);
   if (lane == 63) s_scan[wid] = incl;
   if (tid == 0) *s_e = -1;
@@ -56,27 +74,64 @@ __device__ __forceinline__ bool tile_of(const int32_t* offsets, int E, int64_t T
   const int cb = base + incl - nt;
   if (tid < E && id >= cb && id < cb + nt) {
     *s_e = tid;
-    *s_m0 = o0 + (int64_t)(id - cb) * GBM;
-    *s_rows = (int)min((int64_t)GBM, o1 - *s_m0);
+    *s_m0 = o0 + (int64_t)(id - cb) * BM;
+    *s_rows = (int)min((int64_t)BM, o1 - *s_m0);
   }
   __syncthreads();
   return *s_e >= 0;
 }
 
+// Tile order.  Workgroup b runs on XCD b % 8 (the dispatcher's round robin)
+// and, on that XCD, in the order of b / 8.  Each XCD is given whole groups
+// of kGroupM consecutive m-tiles (consecutive m-tiles are mostly one expert)
+// with all their n-tiles, m-tile group j going to XCD j % 8: the group's
+// token rows and its expert's weight rows are then fetched into that XCD's
+// L2 once and reused by every n-tile, instead of every XCD streaming every
+// operand.  Padding ids (past the last group) do nothing.
+constexpr int kGroupM = 2;
+
+__device__ __forceinline__ bool tile_coords(int ntn, int* mt, int* nt) {
+  const int b = blockIdx.x;
+  const int xcd = b & 7;
+  const int slot = b >> 3;
+  const int per_group = kGroupM * ntn;
+  const int j = slot / per_group;          // this XCD's j-th group
+  const int t = slot - j * per_group;
+  *mt = (j * 8 + xcd) * kGroupM + t / ntn;
+  *nt = t - (t / ntn) * ntn;
+  return true;
+}
+
+// BM x BN output tile of one expert, 4 waves in a 2 x 2 grid, each wave a
+// (BM/2) x (BN/2) block of 16 x 16 MFMA tiles.
+// DMA: full K steps go global -> LDS directly (global_load_lds_dwordx4, no
+// register staging): load i of wave w fills rows 32*i + 8*w .. +8 of the
+// tile, lane l writing 16 bytes at (LDS base) + 16*l, i.e. row +l/8, slot
+// l%8; the lane loads global chunk (l%8) ^ (l/8) so slot s of row r holds
+// chunk s ^ (r%8), the same swizzle as the register path.  These writes are
+// not tracked by the compiler's LDS wait counts: each wave waits for its own
+// loads (vmcnt) before the workgroup barrier that precedes the reads.
+template <int BM, int BN, bool DMA>
 __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
-    const int32_t* __restrict__ offsets, int E, int64_t T, int H, int F,
+    const int32_t* __restrict__ offsets, int E, int64_t T, int H, int F, int ntn,
     uint16_t* __restrict__ y) {
-  __shared__ __align__(16) char sA[2][GBM * 128];
-  __shared__ __align__(16) char sB[2][GBN * 128];
+  constexpr int MT = BM / 32;  // 16-row MFMA tiles per wave (rows)
+  constexpr int NT = BN / 32;  // ... (outputs)
+  constexpr int LA = BM / 32;  // 16-byte global loads per thread and step (A)
+  constexpr int LB = BN / 32;  // ... (B)
+  __shared__ __align__(16) char sA[2][BM * 128];
+  __shared__ __align__(16) char sB[2][BN * 128];
   __shared__ int s_e, s_rows;
   __shared__ int64_t s_m0;
   __shared__ int s_scan[4];
-  if (!tile_of(offsets, E, T, blockIdx.x, &s_e, &s_m0, &s_rows, s_scan)) return;
+  int mt, nt;
+  if (!tile_coords(ntn, &mt, &nt)) return;
+  if (!tile_of<BM>(offsets, E, T, mt, &s_e, &s_m0, &s_rows, s_scan)) return;
   const int e = s_e;
   const int64_t m0 = s_m0;
   const int rows = s_rows;
-  const int n0 = blockIdx.y * GBN;
+  const int n0 = nt * BN;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -86,83 +141,91 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(
   const int wm = wid & 1;
   const int wn = wid >> 1;
 
-  // global -> LDS mapping: 4 chunks of 16 bytes per thread and operand; 8
-  // threads cover one 128-byte row segment.  Rows past the tile's valid rows
-  // (outputs past F) reload the last valid one; they are never stored.
-  const uint16_t* ap[4];
-  const uint16_t* bp[4];
-  int loff[4], lch[4];
+  // global -> LDS: 8 threads per 128-byte row segment of a 64-wide K step.
+  // Rows past the tile's valid rows (outputs past F) reload the last valid
+  // one; they are never stored.  Offsets are 32-bit from the tile's bases.
+  // Thread t loads chunk lch = t % 8 of rows t/8 + 32*i, so its LDS slot of
+  // load i is lof + 4096*i (the swizzle depends on the row mod 8 only).
+  const uint16_t* xa = x + m0 * H;
+  const uint16_t* wb = w + ((int64_t)e * F) * H;
+  const int lch = tid & 7;
+  const int rr0 = tid >> 3;
+  const int lof = rr0 * 128 + ((lch ^ swz(rr0)) << 4);
+  int aof[LA], bof[LB];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int idx = tid + 256 * i;
-    const int rr = idx >> 3;
-    const int ch = idx & 7;
-    lch[i] = ch;
-    ap[i] = x + (m0 + min(rr, rows - 1)) * H + 8 * ch;
-    bp[i] = w + ((int64_t)e * F + min(n0 + rr, F - 1)) * H + 8 * ch;
-    loff[i] = rr * 128 + ((ch ^ (rr & 7)) << 4);
+  for (int i = 0; i < LA; ++i) aof[i] = min(rr0 + 32 * i, rows - 1) * H + 8 * lch;
+#pragma unroll
+  for (int i = 0; i < LB; ++i) bof[i] = min(n0 + rr0 + 32 * i, F - 1) * H + 8 * lch;
+  int daof[DMA ? LA : 1], dbof[DMA ? LB : 1];
+  if constexpr (DMA) {
+    const int dr = lane >> 3;
+    const int dch = (lane & 7) ^ swz(8 * wid + dr);  // rows 32*i + 8*w + dr: swz ignores 32*i
+#pragma unroll
+    for (int i = 0; i < LA; ++i) daof[i] = min(32 * i + 8 * wid + dr, rows - 1) * H + 8 * dch;
+#pragma unroll
+    for (int i = 0; i < LB; ++i) dbof[i] = min(n0 + 32 * i + 8 * wid + dr, F - 1) * H + 8 * dch;
   }
-  // fragment offsets: A rows 64*wm + 16*mi + r, B rows 64*wn + 16*ni + r,
-  // chunk 4*kh + g of the 64-wide step
-  int aoff[4][2], boff[4][2];
+  auto gload_dma = [&](int buf, int kt) {
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
+    for (int i = 0; i < LA; ++i)
+      lds_dma16(xa + daof[i] + kt * GBK, sA[buf] + (32 * i + 8 * wid) * 128);
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
-      const int ra = 64 * wm + 16 * t + r;
-      const int rb = 64 * wn + 16 * t + r;
-      aoff[t][kh] = ra * 128 + (((4 * kh + g) ^ (ra & 7)) << 4);
-      boff[t][kh] = rb * 128 + (((4 * kh + g) ^ (rb & 7)) << 4);
-    }
+    for (int i = 0; i < LB; ++i)
+      lds_dma16(wb + dbof[i] + kt * GBK, sB[buf] + (32 * i + 8 * wid) * 128);
+  };
+  auto wait_vm = [] { __builtin_amdgcn_s_waitcnt(0x0F70); };  // vmcnt(0) only
+  // fragment rows: A (BM/2)*wm + 16*t + r, B (BN/2)*wn + 16*t + r; chunk 4*kh + g
+  auto frag_off = [&](int row, int kh) { return row * 128 + (((4 * kh + g) ^ swz(row)) << 4); };
 
-  f32x4_t acc[4][4];
+  f32x4_t acc[MT][NT];
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
+  for (int mi = 0; mi < MT; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int ni = 0; ni < NT; ++ni) acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const u32x4 zero = {0u, 0u, 0u, 0u};
-  // a full K step: plain loads, consumed only by the LDS stores
-  auto gload = [&](u32x4 (&ra)[4], u32x4 (&rb)[4], int kt) {
+  auto gload = [&](u32x4 (&ra)[LA], u32x4 (&rb)[LB], int kt) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ra[i] = *reinterpret_cast<const u32x4*>(ap[i] + kt * GBK);
-      rb[i] = *reinterpret_cast<const u32x4*>(bp[i] + kt * GBK);
-    }
+    for (int i = 0; i < LA; ++i) ra[i] = *reinterpret_cast<const u32x4*>(xa + aof[i] + kt * GBK);
+#pragma unroll
+    for (int i = 0; i < LB; ++i) rb[i] = *reinterpret_cast<const u32x4*>(wb + bof[i] + kt * GBK);
   };
   // the ragged last K step (H % 64 != 0; H % 8 == 0): chunks with h >= H are
   // zero, their loads read column 0 of the row instead
-  auto gload_masked = [&](u32x4 (&ra)[4], u32x4 (&rb)[4], int kt) {
+  auto gload_masked = [&](u32x4 (&ra)[LA], u32x4 (&rb)[LB], int kt) {
+    const bool ok = kt * GBK + 8 * lch < H;
+    const int ko = ok ? kt * GBK : -8 * lch;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bool ok = kt * GBK + 8 * lch[i] < H;
-      const int ko = ok ? kt * GBK : -8 * lch[i];
-      const u32x4 va = *reinterpret_cast<const u32x4*>(ap[i] + ko);
-      const u32x4 vb = *reinterpret_cast<const u32x4*>(bp[i] + ko);
-      ra[i] = ok ? va : zero;
-      rb[i] = ok ? vb : zero;
+    for (int i = 0; i < LA; ++i) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(xa + aof[i] + ko);
+      ra[i] = ok ? v : zero;
+    }
+#pragma unroll
+    for (int i = 0; i < LB; ++i) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(wb + bof[i] + ko);
+      rb[i] = ok ? v : zero;
     }
   };
-  auto lstore = [&](int buf, const u32x4 (&ra)[4], const u32x4 (&rb)[4]) {
+  auto lstore = [&](int buf, const u32x4 (&ra)[LA], const u32x4 (&rb)[LB]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *reinterpret_cast<u32x4*>(sA[buf] + loff[i]) = ra[i];
-      *reinterpret_cast<u32x4*>(sB[buf] + loff[i]) = rb[i];
-    }
+    for (int i = 0; i < LA; ++i) *reinterpret_cast<u32x4*>(sA[buf] + lof + 4096 * i) = ra[i];
+#pragma unroll
+    for (int i = 0; i < LB; ++i) *reinterpret_cast<u32x4*>(sB[buf] + lof + 4096 * i) = rb[i];
   };
   auto compute = [&](int buf) {
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
-      u32x4 af[4], bf[4];
+      u32x4 af[MT], bf[NT];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        af[t] = *reinterpret_cast<const u32x4*>(sA[buf] + aoff[t][kh]);
-        bf[t] = *reinterpret_cast<const u32x4*>(sB[buf] + boff[t][kh]);
-      }
+      for (int t = 0; t < MT; ++t)
+        af[t] = *reinterpret_cast<const u32x4*>(sA[buf] + frag_off((BM / 2) * wm + 16 * t + r, kh));
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
+      for (int t = 0; t < NT; ++t)
+        bf[t] = *reinterpret_cast<const u32x4*>(sB[buf] + frag_off((BN / 2) * wn + 16 * t + r, kh));
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni)
+      for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NT; ++ni)
           acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(af[mi]),
                                                                 as_bf16x8(bf[ni]), acc[mi][ni],
                                                                 0, 0, 0);
@@ -175,8 +238,23 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(
   // and always stored to the other buffer, which nothing reads after the
   // last step.  The loads stay in flight under the MFMAs of the current step.
   const int nfull = H / GBK;
-  u32x4 ra[4], rb[4];
-  if (nfull > 0) {
+  u32x4 ra[LA], rb[LB];
+  if constexpr (DMA) {
+    if (nfull > 0) {
+      gload_dma(0, 0);
+      wait_vm();
+      __syncthreads();
+      for (int kt = 0; kt < nfull; ++kt) {
+        const int cur = kt & 1;
+        gload_dma(cur ^ 1, min(kt + 1, nfull - 1));
+        __builtin_amdgcn_sched_barrier(0);
+        compute(cur);
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vm();
+        __syncthreads();
+      }
+    }
+  } else if (nfull > 0) {
     gload(ra, rb, 0);
     lstore(0, ra, rb);
     __syncthreads();
@@ -197,16 +275,16 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(
     compute(0);
   }
 
-  // lane (g, r), tile (mi, ni), element i: output row 64*wm + 16*mi + 4*g + i,
-  // column n0 + 64*wn + 16*ni + r
+  // lane (g, r), tile (mi, ni), element i: output row (BM/2)*wm + 16*mi +
+  // 4*g + i, column n0 + (BN/2)*wn + 16*ni + r
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
+  for (int mi = 0; mi < MT; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni) {
-      const int col = n0 + 64 * wn + 16 * ni + r;
+    for (int ni = 0; ni < NT; ++ni) {
+      const int col = n0 + (BN / 2) * wn + 16 * ni + r;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int row = 64 * wm + 16 * mi + 4 * g + i;
+        const int row = (BM / 2) * wm + 16 * mi + 4 * g + i;
         if (row < rows && col < F)
           y[(m0 + row) * F + col] = (uint16_t)f32_to_bf16_rne(acc[mi][ni][i]);
       }
@@ -240,19 +318,41 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(const float* __re
   y[p * F + f] = acc;
 }
 
-}  // namespace
+#ifndef MOE_GEMM_TILE
+#define MOE_GEMM_TILE 256   // 256 x 256 output tiles (128 x 128 for small problems)
+#endif
+#ifndef MOE_GEMM_DMA
+#define MOE_GEMM_DMA 0      // 1: global -> LDS without register staging (measured equal)
+#endif
 
-int64_t grouped_gemm_max_tiles(int64_t T, int E) { return (T + GBM - 1) / GBM + E; }
+template <int BM, int BN>
+hipError_t launch_gg(const void* x_perm, const void* weight, const int32_t* offsets, int64_t T,
+                     int H, int E, int F, void* y, hipStream_t s) {
+  // m-tiles: at most ceil(T / BM) + E (one ragged tile per expert); whole
+  // groups of kGroupM on each of the 8 XCDs, every n-tile of each
+  const int64_t mtiles = (T + BM - 1) / BM + E;
+  const int ntn = (F + BN - 1) / BN;
+  const int64_t groups = (mtiles + kGroupM - 1) / kGroupM;
+  const int64_t blocks = ((groups + 7) / 8) * 8 * kGroupM * ntn;
+  hipLaunchKernelGGL((grouped_gemm_bf16_kernel<BM, BN, MOE_GEMM_DMA != 0>),
+                     dim3((unsigned)blocks), dim3(256), 0, s,
+                     reinterpret_cast<const uint16_t*>(x_perm),
+                     reinterpret_cast<const uint16_t*>(weight), offsets, E, T, H, F, ntn,
+                     reinterpret_cast<uint16_t*>(y));
+  return hipGetLastError();
+}
+
+}  // namespace
 
 hipError_t launch_grouped_linear(const void* x_perm, const void* weight, const int32_t* offsets,
                                  int64_t T, int H, int E, int F, bool bf16, void* y,
                                  hipStream_t s) {
   if (bf16) {
-    const dim3 grid((unsigned)grouped_gemm_max_tiles(T, E), (unsigned)((F + GBN - 1) / GBN));
-    hipLaunchKernelGGL(grouped_gemm_bf16_kernel, grid, dim3(256), 0, s,
-                       reinterpret_cast<const uint16_t*>(x_perm),
-                       reinterpret_cast<const uint16_t*>(weight), offsets, E, T, H, F,
-                       reinterpret_cast<uint16_t*>(y));
+    // large tiles once every CU gets several of them, small ones otherwise
+    const int64_t big = ((T + 255) / 256) * ((F + 255) / 256);
+    if (MOE_GEMM_TILE == 256 && big >= 1024)
+      return launch_gg<256, 256>(x_perm, weight, offsets, T, H, E, F, y, s);
+    return launch_gg<128, 128>(x_perm, weight, offsets, T, H, E, F, y, s);
   } else {
     hipLaunchKernelGGL(grouped_gemm_f32_kernel, dim3((unsigned)((T * F + 255) / 256)), dim3(256),
                        0, s, reinterpret_cast<const float*>(x_perm),

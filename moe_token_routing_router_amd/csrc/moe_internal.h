@@ -200,7 +200,6 @@ hipError_t launch_combine(const void* y, const int32_t* inv, const float* w, int
 
 // Grouped expert linear layer (grouped_gemm.hip): y rows p < offsets[E]
 // (offsets clamped to [0, T]) of x_perm [T,H] times weight[e] [F,H]^T.
-int64_t grouped_gemm_max_tiles(int64_t T, int E);
 hipError_t launch_grouped_linear(const void* x_perm, const void* weight, const int32_t* offsets,
                                  int64_t T, int H, int E, int F, bool bf16, void* y,
                                  hipStream_t s);
