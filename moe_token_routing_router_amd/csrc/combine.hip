@@ -98,7 +98,7 @@ __device__ __forceinline__ void add_vec(float (&acc)[BF16 ? 8 : 4], u32x4 v) {
   }
 }
 
-template <bool BF16, int KT, int U>
+template <bool BF16, int KT, int U, bool RES>
 __global__ __launch_bounds__(256) void combine_kernel(const u32x4* __restrict__ y,
                                                       const int32_t* __restrict__ inv,
                                                       const float* __restrict__ w, int64_t N,
@@ -123,11 +123,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4* __restrict__ 
 
   const int total = ntok * row_vecs;
   u32x4* os = out + n0 * (int64_t)row_vecs;
-  const u32x4* rs = res ? res + n0 * (int64_t)row_vecs : nullptr;
+  const u32x4* rs = RES ? res + n0 * (int64_t)row_vecs : nullptr;
   const u32x4 zero = {0u, 0u, 0u, 0u};
   if constexpr (KT > 0) {
     for (int base = tid; base < total; base += 256 * U) {
-      u32x4 v[U][KT], rv[U];
+      u32x4 v[U][KT], rv[RES ? U : 1];
       int tt[U], c[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -139,7 +139,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4* __restrict__ 
           const int rrow = lrow[tt[u] * KT + k];
           v[u][k] = rrow >= 0 ? ld_vec(y + (int64_t)rrow * row_vecs + c[u]) : zero;
         }
-        rv[u] = rs ? ld_vec(rs + idx) : zero;
+        if constexpr (RES) rv[u] = ld_vec(rs + idx);
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -149,7 +149,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4* __restrict__ 
 #pragma unroll
         for (int k = 0; k < KT; ++k)
           if (lrow[tt[u] * KT + k] >= 0) fma_vec<BF16>(acc, lw[tt[u] * KT + k], v[u][k]);
-        if (rs) add_vec<BF16>(acc, rv[u]);
+        if constexpr (RES) add_vec<BF16>(acc, rv[u]);
         if (base + u * 256 < total) st_vec(os + (int64_t)tt[u] * row_vecs + c[u], pack_vec<BF16>(acc));
       }
     }
@@ -174,7 +174,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4* __restrict__ 
       }
       for (; k < K; ++k)
         if (rr[k] >= 0) fma_vec<BF16>(acc, ww[k], ld_vec(y + (int64_t)rr[k] * row_vecs + c));
-      if (rs) add_vec<BF16>(acc, ld_vec(rs + idx));
+      if constexpr (RES) add_vec<BF16>(acc, ld_vec(rs + idx));
       st_vec(os + (int64_t)tt * row_vecs + c, pack_vec<BF16>(acc));
     }
   }
@@ -186,9 +186,14 @@ hipError_t launch_k(const void* y, const int32_t* inv, const float* w, int64_t N
   const int64_t blocks = (N + kCombineTokens - 1) / kCombineTokens;
   const int row_vecs = BF16 ? H / 8 : H / 4;
   const size_t dyn = (sizeof(int) + sizeof(float)) * (size_t)kCombineTokens * K;
-  hipLaunchKernelGGL((combine_kernel<BF16, KT, U>), dim3((unsigned)blocks), dim3(256), dyn, s,
-                     reinterpret_cast<const u32x4*>(y), inv, w, N, K, row_vecs,
-                     reinterpret_cast<const u32x4*>(res), reinterpret_cast<u32x4*>(out));
+  if (res)
+    hipLaunchKernelGGL((combine_kernel<BF16, KT, U, true>), dim3((unsigned)blocks), dim3(256), dyn,
+                       s, reinterpret_cast<const u32x4*>(y), inv, w, N, K, row_vecs,
+                       reinterpret_cast<const u32x4*>(res), reinterpret_cast<u32x4*>(out));
+  else
+    hipLaunchKernelGGL((combine_kernel<BF16, KT, U, false>), dim3((unsigned)blocks), dim3(256),
+                       dyn, s, reinterpret_cast<const u32x4*>(y), inv, w, N, K, row_vecs,
+                       nullptr, reinterpret_cast<u32x4*>(out));
   return hipGetLastError();
 }
 
