@@ -235,7 +235,8 @@ moe_status_t moe_aggregate(const void *y, const int32_t *inv, const float *topk_
  *                        [0, T], so inconsistent offsets give wrong rows but
  *                        never an access outside the buffers)
  *   y [T,F] dtype        out; rows p >= offsets[E] are not written
- * F must make a row a multiple of 16 bytes, like H.
+ * F must make a row a multiple of 16 bytes, like H; F*H < 2^31 (one
+ * expert's weights) and H < 2^23 (UNSUPPORTED otherwise).
  */
 moe_status_t moe_grouped_linear(const void *x_perm, const void *weight, const int32_t *offsets,
                                 int64_t T, int32_t H, int32_t E, int32_t F, moe_dtype_t dtype,

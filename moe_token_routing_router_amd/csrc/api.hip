@@ -296,7 +296,10 @@ moe_status_t moe_grouped_linear(const void* x_perm, const void* weight, const in
                                 void* y, void* stream) {
   if (!valid_dtype(dtype) || T < 0 || H <= 0 || E <= 0 || F <= 0) return MOE_ERR_INVALID_ARGUMENT;
   if (!offsets || (T > 0 && (!x_perm || !weight || !y))) return MOE_ERR_INVALID_ARGUMENT;
-  if (E > moe::kMaxExperts || T >= kMaxSlots || !row_ok(H, dtype) || !row_ok(F, dtype))
+  // one expert's weights and one 256-row tile of x_perm are indexed with
+  // 32-bit offsets
+  if (E > moe::kMaxExperts || T >= kMaxSlots || !row_ok(H, dtype) || !row_ok(F, dtype) ||
+      (int64_t)F * H >= kMaxSlots || 256LL * H >= kMaxSlots)
     return MOE_ERR_UNSUPPORTED;
   if (dtype == MOE_F32 && (T * (int64_t)F + 255) / 256 >= kMaxSlots) return MOE_ERR_UNSUPPORTED;
   if (!aligned(x_perm, 16) || !aligned(weight, 16) || !aligned(y, 16) || !aligned(offsets, 4))

@@ -207,6 +207,7 @@ def test_grouped_linear_validation(lib):
     assert gl(T=-1) == INVALID
     assert gl(E=257) == UNSUPPORTED
     assert gl(F=12) == UNSUPPORTED          # 24-byte output rows
+    assert gl(F=1 << 16, H=1 << 15) == UNSUPPORTED  # one expert's weights >= 2^31
     assert gl(y=MIS8) == MISALIGNED
     assert gl(off=MIS) == MISALIGNED
     assert gl(T=0) == OK
