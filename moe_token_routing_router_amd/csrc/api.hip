@@ -80,6 +80,13 @@ moe_status_t moe_route(const void* x, const void* gate_w, const float* bias, int
 
 namespace {
 
+// Fused bf16 route+dispatch: up to this many router blocks, the scatter sums
+// the per-block counts itself instead of running the scan kernel.
+#ifndef MOE_PREFIX_MAX_BLOCKS
+#define MOE_PREFIX_MAX_BLOCKS 512
+#endif
+constexpr int64_t kPrefixMaxBlocks = MOE_PREFIX_MAX_BLOCKS;
+
 // dispatch scratch: bhist [E][blocks of bt tokens] then lrank [N*K]
 size_t bhist_bytes(int64_t N, int32_t E, int bt) {
   return round_up((size_t)moe::dispatch_num_blocks(N, bt) * (size_t)E * sizeof(int32_t), 256);
@@ -178,12 +185,21 @@ moe_status_t moe_route_dispatch(const void* x, const void* gate_w, const float* 
       base + rws + round_up((size_t)moe::dispatch_num_blocks(N, bt) * E * sizeof(int32_t), 256));
   hipError_t e;
   if (dtype == MOE_BF16) {
+    // Few blocks: the pack zeroes counts, the router adds its per-block
+    // histograms into them, and each scatter workgroup sums the blocks before
+    // its own, so no scan kernel runs.  Many blocks: the scan kernel.
+    const bool prefix = moe::dispatch_num_blocks(N, bt) <= kPrefixMaxBlocks && K <= 2;
     uint16_t* wgt = reinterpret_cast<uint16_t*>(workspace);
-    e = moe::launch_gate_transpose(reinterpret_cast<const uint16_t*>(gate_w), H, E, wgt, nullptr,
-                                   s);
+    e = moe::launch_gate_transpose(reinterpret_cast<const uint16_t*>(gate_w), H, E, wgt,
+                                   prefix ? counts : nullptr, s);
     if (e != hipSuccess) return MOE_ERR_HIP;
     e = moe::launch_route_bf16(reinterpret_cast<const uint16_t*>(x), wgt, bias, N, H, E, K,
-                               topk_ids, topk_w, nullptr, lrank, bhist, s);
+                               topk_ids, topk_w, prefix ? counts : nullptr, lrank, bhist, s);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    if (prefix)
+      return from_hip(moe::launch_dispatch_scatter_prefix(
+          topk_ids, x, N, (int64_t)H * elem_bytes(dtype), E, K, bt, counts, offsets, perm, inv,
+          x_perm, lrank, bhist, s));
   } else {
     e = moe::launch_route_f32(reinterpret_cast<const float*>(x),
                               reinterpret_cast<const float*>(gate_w), bias, N, H, E, K, topk_ids,

@@ -128,18 +128,23 @@ __global__ __launch_bounds__(256) void dispatch_scan_kernel(int32_t* __restrict_
 // One workgroup per kScatterTokens tokens.  The rows' first loads are issued
 // before the index work (they do not depend on it), so the E-wide offset
 // scan and the index arithmetic overlap them.
+// PREFIX: bhist holds the raw per-block counts (no scan kernel ran) and
+// counts their totals; each workgroup sums the blocks before its own for the
+// experts of its slots (at most nb entries of one bhist row per slot).
+template <bool PREFIX>
 __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
     const int32_t* __restrict__ ids, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ bhist, const int32_t* __restrict__ lrank, int64_t N, int K,
     int E, int nb, int bt, int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
     int32_t* __restrict__ inv, const u32x4* __restrict__ x, u32x4* __restrict__ x_perm,
     int row_vecs, int64_t dlim) {
-  extern __shared__ int dst[];  // [kScatterTokens*K]
+  extern __shared__ int dst[];  // [kScatterTokens*K], then (PREFIX) red[4][kScatterTokens*K]
   __shared__ int off[kMaxExperts];
   __shared__ int scan_lds[4];
   const int tid = threadIdx.x;
   const int64_t n0 = (int64_t)blockIdx.x * kScatterTokens;
   const int ntok = (int)min((int64_t)kScatterTokens, N - n0);
+  int* red = dst + kScatterTokens * K;
 
   constexpr int U = MOE_SCATTER_U;
   const int total = ntok * row_vecs;
@@ -150,6 +155,23 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
     for (int u = 0; u < U; ++u) {
       const int idx = min(tid + u * 256, total - 1);
       v[u] = ld_row(xs + idx);
+    }
+  }
+
+  const int S = ntok * K;
+  const int64_t s0 = n0 * K;
+  if constexpr (PREFIX) {
+    // per slot: the counts of its expert in the blocks before its own (the
+    // barriers of the offset scan below publish red)
+    for (int j = 0; j < S; ++j) {
+      const int64_t slot = s0 + j;
+      const int e = ids[slot];
+      const int64_t b = (slot / K) / bt;
+      int part = 0;
+      if ((unsigned)e < (unsigned)E)
+        for (int64_t bb = tid; bb < b; bb += 256) part += bhist[(int64_t)e * nb + bb];
+      part = __builtin_amdgcn_readlane(wave_inclusive_sum(part), 63);
+      if ((tid & 63) == 0) red[(tid >> 6) * S + j] = part;
     }
   }
 
@@ -166,15 +188,15 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
   }
   __syncthreads();
 
-  const int S = ntok * K;
-  const int64_t s0 = n0 * K;
   for (int j = tid; j < S; j += 256) {
     const int64_t slot = s0 + j;
     const int e = ids[slot];
     int d = -1;
     if ((unsigned)e < (unsigned)E) {
       const int64_t b = (slot / K) / bt;
-      const int64_t dd = (int64_t)off[e] + bhist[(int64_t)e * nb + b] + lrank[slot];
+      const int64_t base = PREFIX ? (int64_t)((red[j] + red[S + j]) + red[2 * S + j]) + red[3 * S + j]
+                                  : (int64_t)bhist[(int64_t)e * nb + b];
+      const int64_t dd = (int64_t)off[e] + base + lrank[slot];
       if (dd >= 0 && dd < dlim) {  // always true for consistent inputs
         d = (int)dd;
         perm[d] = (int32_t)slot;
@@ -232,6 +254,21 @@ hipError_t launch_dispatch_finish(const int32_t* ids, const void* x, int64_t N, 
                                 lrank, bhist, N * K, s);
 }
 
+hipError_t launch_dispatch_scatter_prefix(const int32_t* ids, const void* x, int64_t N,
+                                          int64_t row_bytes, int E, int K, int bt,
+                                          const int32_t* counts, int32_t* offsets, int32_t* perm,
+                                          int32_t* inv, void* x_perm, const int32_t* lrank,
+                                          const int32_t* bhist, hipStream_t s) {
+  const int nb = (int)dispatch_num_blocks(N, bt);
+  const int64_t blocks = (N + kScatterTokens - 1) / kScatterTokens;
+  const size_t dyn = sizeof(int) * 5 * (size_t)kScatterTokens * K;
+  hipLaunchKernelGGL(dispatch_scatter_kernel<true>, dim3((unsigned)blocks), dim3(256), dyn, s, ids,
+                     counts, bhist, lrank, N, K, E, nb, bt, offsets, perm, inv,
+                     reinterpret_cast<const u32x4*>(x), reinterpret_cast<u32x4*>(x_perm),
+                     (int)(row_bytes / 16), N * K);
+  return hipGetLastError();
+}
+
 hipError_t launch_dispatch_finish(const int32_t* ids, const void* x, int64_t N, int64_t row_bytes,
                                   int E, int K, int bt, int32_t* counts, int32_t* offsets,
                                   int32_t* perm, int32_t* inv, void* x_perm,
@@ -243,7 +280,7 @@ hipError_t launch_dispatch_finish(const int32_t* ids, const void* x, int64_t N, 
   if (err != hipSuccess) return err;
   const int64_t blocks = (N + kScatterTokens - 1) / kScatterTokens;
   const size_t dyn = sizeof(int) * (size_t)kScatterTokens * K;
-  hipLaunchKernelGGL(dispatch_scatter_kernel, dim3((unsigned)blocks), dim3(256), dyn, s, ids,
+  hipLaunchKernelGGL(dispatch_scatter_kernel<false>, dim3((unsigned)blocks), dim3(256), dyn, s, ids,
                      counts, bhist, lrank, N, K, E, nb, bt, offsets, perm, inv,
                      reinterpret_cast<const u32x4*>(x), reinterpret_cast<u32x4*>(x_perm),
                      (int)(row_bytes / 16), dlim);

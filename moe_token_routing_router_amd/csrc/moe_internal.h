@@ -181,6 +181,15 @@ hipError_t launch_dispatch_finish(const int32_t* ids, const void* x, int64_t N, 
                                   const int32_t* lrank, int32_t* bhist, int64_t dlim,
                                   hipStream_t s);
 
+// scatter only, for the fused path: bhist holds raw per-block counts and
+// counts their totals (the router's atomic histogram); each scatter
+// workgroup sums the blocks before its own.
+hipError_t launch_dispatch_scatter_prefix(const int32_t* ids, const void* x, int64_t N,
+                                          int64_t row_bytes, int E, int K, int bt,
+                                          const int32_t* counts, int32_t* offsets, int32_t* perm,
+                                          int32_t* inv, void* x_perm, const int32_t* lrank,
+                                          const int32_t* bhist, hipStream_t s);
+
 // Expert-parallel metadata (ep.hip).  keys[i] = rank of ids[i] if slot i is
 // the first of its token on that rank, else -1 (invalid ids: -1).
 hipError_t launch_ep_keys(const int32_t* ids, int64_t N, int K, int E, int per_rank,

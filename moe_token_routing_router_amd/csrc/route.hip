@@ -405,15 +405,17 @@ __global__ __launch_bounds__(NW * 64) void route_bf16_kernel(
     }
   }
   int pick[U];
-  select_topk_store<NT, U>(v, r, E, K, tt, N, ids, topw, counts ? hist : nullptr, pick);
+  // with lrank the dispatch histogram below also gives the counts
+  select_topk_store<NT, U>(v, r, E, K, tt, N, ids, topw, (counts && !lrank) ? hist : nullptr,
+                           pick);
 
   // For the fused dispatch: stable rank of every selected slot among the
   // equal ids of this workgroup's BM tokens, and the workgroup's per-expert
   // histogram (the dispatch count kernel's outputs for blocks of BM tokens).
+  int* sids = reinterpret_cast<int*>(smem);
+  int* rhist = sids + BM * kMaxRouteK;
   if (lrank) {
     __syncthreads();  // every wave is done reading the partial sums
-    int* sids = reinterpret_cast<int*>(smem);
-    int* rhist = sids + BM * kMaxRouteK;
     int* wcnt = rhist + kMaxExperts;
     if (r < K) {
 #pragma unroll
@@ -429,8 +431,9 @@ __global__ __launch_bounds__(NW * 64) void route_bf16_kernel(
 
   if (counts) {
     __syncthreads();
+    const int* h = lrank ? rhist : hist;
     for (int e = tid; e < E; e += NW * 64)
-      if (hist[e]) atomicAdd(&counts[e], hist[e]);
+      if (h[e]) atomicAdd(&counts[e], h[e]);
   }
 }
 
