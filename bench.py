@@ -96,6 +96,77 @@ def cpu_baseline(d, min_seconds):
                       f"{el:.1f} s on 1 thread of {cpu_model()}"}
 
 
+def small_step_graph(L, I, name, steps, dev):
+    """One fused forward step (moe_route_dispatch + moe_combine) of a small
+    workload: launched call by call through the C ABI, then captured once in
+    a HIP graph and replayed.  Returns wall-clock steps/s of both."""
+    import torch
+    wl = I.WORKLOADS[name]
+    d = I.make_inputs(wl)
+    N, H, E, K = wl.N, wl.H, wl.E, wl.K
+    tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+
+    def to_dev(a):
+        if wl.dtype == "bf16":
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    x, y, gw = to_dev(d["x"]), to_dev(d["y"]), to_dev(d["gate_w"])
+    bias = None if d["bias"] is None else torch.from_numpy(d["bias"]).to(dev)
+    i32 = dict(dtype=torch.int32, device=dev)
+    ids, w = torch.empty((N, K), **i32), torch.empty((N, K), dtype=torch.float32, device=dev)
+    counts, offsets = torch.empty((E,), **i32), torch.empty((E + 1,), **i32)
+    perm, inv = torch.empty((N * K,), **i32), torch.empty((N * K,), **i32)
+    x_perm = torch.empty((N * K, H), dtype=tdt, device=dev)
+    out = torch.empty((N, H), dtype=tdt, device=dev)
+    ws = torch.empty((L.moe_route_dispatch_workspace_size(N, H, E, K, tdt),), dtype=torch.uint8,
+                     device=dev)
+    L.moe_route_dispatch(x, gw, bias, K, ids, w, counts, offsets, perm, inv, x_perm, ws)
+    L.moe_combine(y, inv, w, out)
+    torch.cuda.synchronize()
+    lib = L.library()
+    P = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None
+    dt = L.MOE_BF16 if wl.dtype == "bf16" else L.MOE_F32
+
+    def args_on(stream_ptr):
+        sp = ctypes.c_void_p(stream_ptr)
+        return ((P(x), P(gw), P(bias), N, H, E, K, dt, P(ids), P(w), P(counts), P(offsets),
+                 P(perm), P(inv), P(x_perm), P(ws), ws.numel(), sp),
+                (P(y), P(inv), P(w), N, H, K, dt, P(out), sp))
+
+    def launch(a):
+        if lib.moe_route_dispatch(*a[0]) or lib.moe_combine(*a[1]):
+            raise RuntimeError("small-workload step failed")
+
+    eager = args_on(torch.cuda.current_stream(dev).cuda_stream)
+    for _ in range(10):
+        launch(eager)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        launch(eager)
+    torch.cuda.synchronize()
+    t_eager = time.perf_counter() - t0
+    ref = out.clone()
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        launch(args_on(torch.cuda.current_stream(dev).cuda_stream))
+    for _ in range(10):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    t_graph = time.perf_counter() - t0
+    assert torch.equal(out.view(torch.uint8), ref.view(torch.uint8)), "graph replay differs"
+    return {"workload": wl.describe(), "eager_steps_per_s": round(steps / t_eager, 1),
+            "graph_steps_per_s": round(steps / t_graph, 1),
+            "eager_us_per_step": round(t_eager / steps * 1e6, 2),
+            "graph_us_per_step": round(t_graph / steps * 1e6, 2)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -319,6 +390,10 @@ def main():
     for i in range(N_SETS):
         step(i)
     torch.cuda.synchronize()
+    # the small workloads are launch-bound: one step launched call by call
+    # against the same step replayed from a HIP graph
+    graphs = {n: small_step_graph(L, I, n, max(args.steps, 200), dev)
+              for n in ("tiny-fp32", "small-bf16")}
 
     # correctness guard on the outputs (cheap invariants only)
     last = sets[0]
@@ -406,6 +481,7 @@ def main():
                              "tokens_per_s": round(N * args.steps / wall_u, 1)},
         "stages": stages,
         "load_max_over_mean": round(float(load.max() / load.mean()), 3),
+        "small_workloads_graph": graphs,
         "roofline": roofline,
         "cpu_baseline": None,
     }

@@ -505,9 +505,12 @@ __global__ __launch_bounds__(256) void route_f32_kernel(const float* __restrict_
 // 16 bytes at lane l = 16g + r hold gate[h0 .. h0+8][16q + r] with
 // h0 = 64s + 16g + 8hf -- exactly one MFMA B fragment.  Values with h >= H or
 // e >= E are zero, so the router needs no masking on this operand.
-// Each thread moves one 8(h) x 8(e) block: eight 16-byte row loads, a
-// register transpose, eight 16-byte stores.  Threads 0..E-1 also zero
-// `counts` (the router then adds into it).
+// Each thread builds one fragment entry: expert e, eight rows h0 .. h0+7
+// (eight 2-byte loads -- the 64 lanes of a wave read 64 consecutive experts
+// of a row, so each load instruction is one coalesced row segment -- and one
+// 16-byte store).  One thread per entry keeps the launch wide (HP/8 * EP
+// threads), which is what the latency of this small re-layout needs.
+// Threads 0..E-1 also zero `counts` (the router then adds into it).
 __global__ __launch_bounds__(64) void gate_pack_kernel(const uint16_t* __restrict__ gate_w, int H,
                                                        int E, int EP, int HP,
                                                        u32x4* __restrict__ gfrag,
@@ -515,48 +518,22 @@ __global__ __launch_bounds__(64) void gate_pack_kernel(const uint16_t* __restric
   const int64_t idx = (int64_t)blockIdx.x * 64 + threadIdx.x;
   if (counts && idx < E) counts[idx] = 0;
   const int nhb = HP / 8;  // 8-row blocks of h, including the zero padding up to HP
-  if (idx >= (int64_t)nhb * (EP / 8)) return;
-  const int eb = (int)(idx / nhb);
-  const int hb = (int)(idx - (int64_t)eb * nhb);
-  const int h0 = hb * 8, e0 = eb * 8;
-  uint32_t v[8][4];  // v[i] = 8 bf16 of gate row h0+i, experts e0..e0+7 (2 per word)
-  const bool vec = (E % 8 == 0) && (e0 + 8 <= E);
+  if (idx >= (int64_t)nhb * EP) return;
+  const int hb = (int)(idx / EP);
+  const int e = (int)(idx - (int64_t)hb * EP);
+  const int h0 = hb * 8;
+  uint32_t t[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int h = h0 + i;
-    if (h >= H) {
-      v[i][0] = v[i][1] = v[i][2] = v[i][3] = 0u;
-      continue;
-    }
-    const uint16_t* src = gate_w + (int64_t)h * E + e0;
-    if (vec) {
-      const u32x4 u = *reinterpret_cast<const u32x4*>(src);
-      v[i][0] = u[0]; v[i][1] = u[1]; v[i][2] = u[2]; v[i][3] = u[3];
-    } else {
-      uint16_t t[8];
+  for (int i = 0; i < 8; ++i)
+    t[i] = (e < E && h0 + i < H) ? (uint32_t)gate_w[(int64_t)(h0 + i) * E + e] : 0u;
+  u32x4 o;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) t[j] = (e0 + j < E) ? src[j] : (uint16_t)0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) v[i][j] = (uint32_t)t[2 * j] | ((uint32_t)t[2 * j + 1] << 16);
-    }
-  }
+  for (int p = 0; p < 4; ++p) o[p] = t[2 * p] | (t[2 * p + 1] << 16);
   const int s = h0 >> 6;
   const int g = (h0 >> 4) & 3;
   const int hf = (h0 >> 3) & 1;
   const int NTL = EP / 16;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {  // expert e0+j: its 8 values of h0..h0+7
-    const int e = e0 + j;
-    u32x4 o;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const uint32_t lo = (v[2 * p][j >> 1] >> (16 * (j & 1))) & 0xffffu;
-      const uint32_t hi = (v[2 * p + 1][j >> 1] >> (16 * (j & 1))) & 0xffffu;
-      o[p] = lo | (hi << 16);
-    }
-    const int q = e >> 4;
-    gfrag[((int64_t)(s * NTL + q) * 2 + hf) * 64 + 16 * g + (e & 15)] = o;
-  }
+  gfrag[((int64_t)(s * NTL + (e >> 4)) * 2 + hf) * 64 + 16 * g + (e & 15)] = o;
 }
 
 __global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
@@ -612,7 +589,7 @@ hipError_t launch_gate_transpose(const uint16_t* gate_w, int H, int E, uint16_t*
                                  int32_t* counts, hipStream_t s) {
   const int EP = route_padded_experts(E);
   const int HP = route_gate_rows(H);
-  int64_t threads = (int64_t)(HP / 8) * (EP / 8);
+  int64_t threads = (int64_t)(HP / 8) * EP;
   if (threads < E) threads = E;
   hipLaunchKernelGGL(gate_pack_kernel, dim3((unsigned)((threads + 63) / 64)), dim3(64), 0, s,
                      gate_w, H, E, EP, HP, reinterpret_cast<u32x4*>(wgt), counts);
