@@ -216,9 +216,9 @@ moe_status_t moe_route_dispatch(const void* x, const void* gate_w, const float* 
 size_t moe_ep_dispatch_workspace_size(int64_t N, int32_t E, int32_t K, int32_t ep_size) {
   if (N < 0 || E <= 0 || E > moe::kMaxExperts || K < 1 || ep_size < 1 || E % ep_size != 0)
     return 0;
-  // dispatch scratch (shared by the expert- and the rank-level passes), then
-  // the rank keys and the owner slots' send rows
-  return dispatch_scratch_bytes(N, E, K, moe::dispatch_count_tokens(K)) +
+  // block histograms of both levels [E + R][blocks], then the slots' ranks
+  // among equal experts and among equal rank keys [N*K] each
+  return bhist_bytes(N, E + ep_size, moe::dispatch_count_tokens(K)) +
          2 * round_up((size_t)N * (size_t)K * sizeof(int32_t), 256);
 }
 
@@ -251,32 +251,16 @@ moe_status_t moe_ep_dispatch(const int32_t* topk_ids, const void* x, int64_t N, 
   if (workspace_bytes < moe_ep_dispatch_workspace_size(N, E, K, ep_size))
     return MOE_ERR_WORKSPACE_TOO_SMALL;
   const int64_t T = N * K;
-  const int bt = moe::dispatch_count_tokens(K);
   char* base = reinterpret_cast<char*>(workspace);
+  const size_t hb = bhist_bytes(N, E + ep_size, moe::dispatch_count_tokens(K));
   int32_t* bhist = reinterpret_cast<int32_t*>(base);
-  int32_t* lrank = reinterpret_cast<int32_t*>(base + bhist_bytes(N, E, bt));
-  int32_t* keys = reinterpret_cast<int32_t*>(base + dispatch_scratch_bytes(N, E, K, bt));
-  int32_t* owner_row = reinterpret_cast<int32_t*>(
-      base + dispatch_scratch_bytes(N, E, K, bt) + round_up((size_t)T * sizeof(int32_t), 256));
-  const int64_t row_bytes = (int64_t)H * elem_bytes(dtype);
-  // expert level: counts, offsets, perm, inv (no rows)
-  hipError_t e = moe::launch_dispatch_count(topk_ids, N, E, K, lrank, bhist, s);
-  if (e != hipSuccess) return MOE_ERR_HIP;
-  e = moe::launch_dispatch_finish(topk_ids, nullptr, N, row_bytes, E, K, bt, counts, offsets,
-                                  perm, inv, nullptr, lrank, bhist, s);
-  if (e != hipSuccess) return MOE_ERR_HIP;
-  // rank level on the deduplicated keys: send counts/offsets, send slots (in
-  // send_tok), owner rows, and the rows themselves
-  e = moe::launch_ep_keys(topk_ids, N, K, E, E / ep_size, keys, s);
-  if (e != hipSuccess) return MOE_ERR_HIP;
-  e = moe::launch_dispatch_count(keys, N, ep_size, K, lrank, bhist, s);
-  if (e != hipSuccess) return MOE_ERR_HIP;
-  e = moe::launch_dispatch_finish(keys, x, N, row_bytes, ep_size, K, bt, send_counts,
-                                  send_offsets, send_tok, owner_row, x_send, lrank, bhist,
-                                  N * (int64_t)(K < ep_size ? K : ep_size), s);
-  if (e != hipSuccess) return MOE_ERR_HIP;
-  return from_hip(moe::launch_ep_finish(topk_ids, perm, offsets, owner_row, send_offsets, N, K, E,
-                                        ep_size, send_tok, send_row, expand_idx, s));
+  int32_t* lrank_e = reinterpret_cast<int32_t*>(base + hb);
+  int32_t* lrank_r =
+      reinterpret_cast<int32_t*>(base + hb + round_up((size_t)T * sizeof(int32_t), 256));
+  return from_hip(moe::launch_ep_dispatch(
+      topk_ids, x, N, (int64_t)H * elem_bytes(dtype), E, K, ep_size, counts, offsets, perm, inv,
+      send_counts, send_offsets, send_tok, send_row, expand_idx, x_send, bhist, lrank_e, lrank_r,
+      s));
 }
 
 moe_status_t moe_combine(const void* y, const int32_t* inv, const float* topk_w, int64_t N,

@@ -68,26 +68,6 @@ __device__ __forceinline__ void st_row(u32x4* p, u32x4 v) {
 #endif
 }
 
-// Exclusive scan of one int per thread over a 256-thread block.
-// `lds` needs 4 ints.  Returns the exclusive prefix; *total gets the sum.
-__device__ __forceinline__ int block_exclusive_scan_256(int v, int* lds, int* total) {
-  const int lane = threadIdx.x & 63;
-  const int wid = threadIdx.x >> 6;
-  const int incl = wave_inclusive_sum(v);
-  if (lane == 63) lds[wid] = incl;
-  __syncthreads();
-  int wbase = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const int c = lds[w];
-    if (w < wid) wbase += c;
-    tot += c;
-  }
-  __syncthreads();
-  *total = tot;
-  return wbase + incl - v;
-}
-
 __global__ __launch_bounds__(256) void dispatch_count_kernel(const int32_t* __restrict__ ids,
                                                              int64_t N, int K, int E, int bt,
                                                              int nb, int32_t* __restrict__ lrank,
@@ -105,9 +85,12 @@ __global__ __launch_bounds__(256) void dispatch_count_kernel(const int32_t* __re
   for (int e = tid; e < E; e += 256) bhist[(int64_t)e * nb + blockIdx.x] = hist[e];
 }
 
+// rows below `split` total into counts[row], the others into counts2[row - split]
 __global__ __launch_bounds__(256) void dispatch_scan_kernel(int32_t* __restrict__ bhist,
                                                             int nb,
-                                                            int32_t* __restrict__ counts) {
+                                                            int32_t* __restrict__ counts,
+                                                            int split,
+                                                            int32_t* __restrict__ counts2) {
   __shared__ int lds[4];
   int32_t* row = bhist + (int64_t)blockIdx.x * nb;
   const int per = (nb + 255) / 256;
@@ -122,7 +105,11 @@ __global__ __launch_bounds__(256) void dispatch_scan_kernel(int32_t* __restrict_
     row[b] = run;
     run += c;
   }
-  if (threadIdx.x == 0) counts[blockIdx.x] = total;
+  if (threadIdx.x == 0) {
+    const int rr = (int)blockIdx.x;
+    if (rr < split) counts[rr] = total;
+    else counts2[rr - split] = total;
+  }
 }
 
 // One workgroup per kScatterTokens tokens.  The rows' first loads are issued
@@ -275,7 +262,8 @@ hipError_t launch_dispatch_finish(const int32_t* ids, const void* x, int64_t N, 
                                   const int32_t* lrank, int32_t* bhist, int64_t dlim,
                                   hipStream_t s) {
   const int nb = (int)dispatch_num_blocks(N, bt);
-  hipLaunchKernelGGL(dispatch_scan_kernel, dim3(E), dim3(256), 0, s, bhist, nb, counts);
+  hipLaunchKernelGGL(dispatch_scan_kernel, dim3(E), dim3(256), 0, s, bhist, nb, counts, E,
+                     (int32_t*)nullptr);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int64_t blocks = (N + kScatterTokens - 1) / kScatterTokens;
@@ -284,6 +272,13 @@ hipError_t launch_dispatch_finish(const int32_t* ids, const void* x, int64_t N, 
                      counts, bhist, lrank, N, K, E, nb, bt, offsets, perm, inv,
                      reinterpret_cast<const u32x4*>(x), reinterpret_cast<u32x4*>(x_perm),
                      (int)(row_bytes / 16), dlim);
+  return hipGetLastError();
+}
+
+hipError_t launch_dispatch_scan(int32_t* bhist, int rows, int nb, int32_t* counts, int split,
+                                int32_t* counts2, hipStream_t s) {
+  hipLaunchKernelGGL(dispatch_scan_kernel, dim3(rows), dim3(256), 0, s, bhist, nb, counts, split,
+                     counts2);
   return hipGetLastError();
 }
 

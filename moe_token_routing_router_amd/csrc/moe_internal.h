@@ -54,6 +54,26 @@ __device__ __forceinline__ int wave_inclusive_sum(int v) {
   return v;
 }
 
+// Exclusive scan of one int per thread over a 256-thread block.
+// `lds` needs 4 ints.  Returns the exclusive prefix; *total gets the sum.
+__device__ __forceinline__ int block_exclusive_scan_256(int v, int* lds, int* total) {
+  const int lane = threadIdx.x & 63;
+  const int wid = threadIdx.x >> 6;
+  const int incl = wave_inclusive_sum(v);
+  if (lane == 63) lds[wid] = incl;
+  __syncthreads();
+  int wbase = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const int c = lds[w];
+    if (w < wid) wbase += c;
+    tot += c;
+  }
+  __syncthreads();
+  *total = tot;
+  return wbase + incl - v;
+}
+
 // ---- wave-wide float sum, fixed order --------------------------------------
 // Butterfly inside each 16-lane row (DPP quad_perm xor 1, xor 2,
 // row_half_mirror, row_mirror: every lane ends with its row's sum), then the
@@ -190,16 +210,20 @@ hipError_t launch_dispatch_scatter_prefix(const int32_t* ids, const void* x, int
                                           int32_t* inv, void* x_perm, const int32_t* lrank,
                                           const int32_t* bhist, hipStream_t s);
 
-// Expert-parallel metadata (ep.hip).  keys[i] = rank of ids[i] if slot i is
-// the first of its token on that rank, else -1 (invalid ids: -1).
-hipError_t launch_ep_keys(const int32_t* ids, int64_t N, int K, int E, int per_rank,
-                          int32_t* keys, hipStream_t s);
-// send_tok holds send slots on entry (from the rank-keyed scatter) and
-// tokens on exit; owner_row[i] is the send row of owner slot i (-1 otherwise).
-hipError_t launch_ep_finish(const int32_t* ids, const int32_t* perm, const int32_t* offsets,
-                            const int32_t* owner_row, const int32_t* send_offsets, int64_t N,
-                            int K, int E, int R, int32_t* send_tok, int32_t* send_row,
-                            int32_t* expand_idx, hipStream_t s);
+// Scan of `rows` bhist rows of nb blocks (in place, exclusive); the totals
+// of rows below `split` go to counts[row], the others to counts2[row - split].
+hipError_t launch_dispatch_scan(int32_t* bhist, int rows, int nb, int32_t* counts, int split,
+                                int32_t* counts2, hipStream_t s);
+
+// Expert-parallel metadata (ep.hip): count, scan and scatter of both levels
+// (experts and deduplicated ranks).  Scratch: bhist [E+R][dispatch_num_blocks(
+// N, dispatch_count_tokens(K))], lrank_e and lrank_r [N*K].
+hipError_t launch_ep_dispatch(const int32_t* ids, const void* x, int64_t N, int64_t row_bytes,
+                              int E, int K, int R, int32_t* counts, int32_t* offsets,
+                              int32_t* perm, int32_t* inv, int32_t* send_counts,
+                              int32_t* send_offsets, int32_t* send_tok, int32_t* send_row,
+                              int32_t* expand_idx, void* x_send, int32_t* bhist,
+                              int32_t* lrank_e, int32_t* lrank_r, hipStream_t s);
 
 // Combine (w may be null: unit weights, the dispatch backward; residual, if
 // given, is added after the expert terms: forward_aggregate).

@@ -164,10 +164,12 @@ def test_ep_dispatch_validation(lib):
     assert ep(lib, xs=MIS8) == MISALIGNED
     assert ep(lib, st=MIS) == MISALIGNED
     assert ep(lib, wsb=8) == WS_SMALL
-    # sizes: the dispatch scratch plus the rank keys and owner rows
+    # sizes: block histograms of both levels [E + R][blocks of 64 tokens]
+    # plus the two slot-rank arrays [N*K]
     for N, E, K, R in ((16384, 64, 2, 8), (17, 6, 2, 3), (32768, 128, 8, 8)):
         n = lib.moe_ep_dispatch_workspace_size(N, E, K, R)
-        assert n >= lib.moe_dispatch_workspace_size(N, E, K) + 2 * N * K * 4 and n % 256 == 0
+        nb = -(-N // 64)
+        assert n >= (E + R) * nb * 4 + 2 * N * K * 4 and n % 256 == 0
     assert lib.moe_ep_dispatch_workspace_size(16, 6, 2, 4) == 0
 
 
