@@ -45,6 +45,9 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4 u) { return __builtin_bit_ca
 // slot c ^ swz(r)
 __device__ __forceinline__ int swz(int r) { return MOE_GEMM_SWZ ? (r >> 1) & 7 : r & 7; }
 
+// s_waitcnt immediate for vmcnt(v) alone (expcnt and lgkmcnt left at their maxima)
+constexpr int vmcnt_imm(int v) { return (v & 15) | 0x70 | 0xF00 | (((v >> 4) & 3) << 14); }
+
 // 16 bytes per lane from global memory straight into LDS: lane l's bytes land
 // at lds_base + 16*l (lds_base must be the same in every lane of the wave).
 __device__ __forceinline__ void lds_dma16(const void* src, char* lds_base) {
@@ -291,6 +294,143 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(
     }
 }
 
+// 256 x 256 tiles with a 4-slot ring of 32-wide K steps in LDS (H % 32 == 0):
+// each step's A and B tiles (256 rows x 64 bytes each) are copied
+// global -> LDS with global_load_lds (no registers), three steps ahead of
+// the MFMAs.  Slot layout: 16-byte chunk c of row r at chunk
+// c ^ ((r >> 1) & 3), so the eight lanes of one LDS read phase (rows r..r+7
+// of one chunk column) hit eight different 16-byte bank groups.
+// Per step and wave: 8 copies (4 row blocks of A, 4 of B), counted by vmcnt
+// in issue order; the ring keeps each wait count constant (the last steps
+// re-copy the last step into slots nothing reads any more).
+//
+// The copies are issued from inline asm, so the compiler does not see them:
+// it would otherwise treat every LDS read as possibly aliasing a copy still
+// in flight and wait for all of them (vmcnt(0)) before each read.  The
+// explicit vmcnt wait plus a bare workgroup barrier (no release fence, which
+// would also wait for every copy) order each slot's copies before its reads.
+// M0 holds the LDS destination of a copy; nothing else in this kernel uses it.
+__device__ __forceinline__ void lds_copy16(const void* src, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(lds_base), "v"(src)
+               : "memory");
+}
+__device__ __forceinline__ uint32_t lds_addr(const char* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+__device__ __forceinline__ void wg_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__global__ __launch_bounds__(256) void grouped_gemm_ring_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
+    const int32_t* __restrict__ offsets, int E, int64_t T, int H, int F, int ntn,
+    uint16_t* __restrict__ y) {
+  constexpr int BM = 256, BN = 256, RK = 32;  // K step (h) of one ring slot
+  constexpr int SLOT = 2 * BM * 64;           // A then B, 64 bytes per row
+  constexpr int RING = 4;
+  constexpr int MT = 8, NT = 8;               // 16 x 16 tiles per wave (rows, outputs)
+  __shared__ __align__(1024) char smem[RING * SLOT];
+  __shared__ int s_e, s_rows;
+  __shared__ int64_t s_m0;
+  __shared__ int s_scan[4];
+  int mt, nt;
+  if (!tile_coords(ntn, &mt, &nt)) return;
+  if (!tile_of<BM>(offsets, E, T, mt, &s_e, &s_m0, &s_rows, s_scan)) return;
+  const int e = s_e;
+  const int64_t m0 = s_m0;
+  const int rows = s_rows;
+  const int n0 = nt * BN;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wid = tid >> 6;
+  const int g = lane >> 4;
+  const int r = lane & 15;
+  const int wm = wid & 1;
+  const int wn = wid >> 1;
+
+  // copies: instruction i of wave w fills rows 64i + 16w .. +16 of a tile;
+  // lane l -> row +l/4, slot chunk l%4, which holds global chunk
+  // (l%4) ^ ((row >> 1) & 3).  Offsets are 32-bit from the tile's bases.
+  const uint16_t* xa = x + m0 * H;
+  const uint16_t* wb = w + ((int64_t)e * F) * H;
+  const int dr = lane >> 2;
+  const int dch = (lane & 3) ^ ((dr >> 1) & 3);
+  int aof[4], bof[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    aof[i] = min(64 * i + 16 * wid + dr, rows - 1) * H + 8 * dch;
+    bof[i] = min(n0 + 64 * i + 16 * wid + dr, F - 1) * H + 8 * dch;
+  }
+  const uint32_t base = lds_addr(smem);
+  // (the LDS destination of a copy is wave-uniform: M0 takes a scalar)
+  const uint32_t wbase = __builtin_amdgcn_readfirstlane(base + (uint32_t)(16 * wid * 64));
+  auto copy_step = [&](int slot, int kt) {
+    const uint32_t sa = wbase + (uint32_t)(slot * SLOT);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lds_copy16(xa + aof[i] + kt * RK, sa + (uint32_t)(64 * i * 64));
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      lds_copy16(wb + bof[i] + kt * RK, sa + (uint32_t)(BM * 64 + 64 * i * 64));
+  };
+  // fragment reads: A rows 128*wm + 16*t + r, B rows 128*wn + 16*t + r, chunk g
+  const int aoff = (128 * wm + r) * 64 + ((g ^ ((r >> 1) & 3)) << 4);
+  const int boff = BM * 64 + (128 * wn + r) * 64 + ((g ^ ((r >> 1) & 3)) << 4);
+  f32x4_t acc[MT][NT];
+#pragma unroll
+  for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < NT; ++ni) acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = H / RK;
+  const int last = nk - 1;
+  copy_step(0, 0);
+  copy_step(1, min(1, last));
+  copy_step(2, min(2, last));
+  // step s: its copies landed (steps s+1, s+2 may still be in flight) ->
+  // barrier -> refill the slot of step s-1 with step s+3 -> read step s's
+  // fragments -> its MFMAs (which drain while the next step's wait, barrier
+  // and reads proceed)
+  for (int s = 0; s < nk; ++s) {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(16));
+    wg_barrier();
+    copy_step((s + 3) & 3, min(s + 3, last));
+    // A fragments of all eight row tiles, then one B fragment at a time
+    // (fewer live registers: the 256 accumulators fill the AGPRs)
+    const char* sl = smem + (s & 3) * SLOT;
+    u32x4 af[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) af[t] = *reinterpret_cast<const u32x4*>(sl + aoff + t * 1024);
+#pragma unroll
+    for (int ni = 0; ni < NT; ++ni) {
+      const u32x4 bv = *reinterpret_cast<const u32x4*>(sl + boff + ni * 1024);
+#pragma unroll
+      for (int mi = 0; mi < MT; ++mi)
+        acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(af[mi]), as_bf16x8(bv),
+                                                              acc[mi][ni], 0, 0, 0);
+    }
+  }
+  // no copy may still be landing in LDS when the workgroup ends
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+
+#pragma unroll
+  for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < NT; ++ni) {
+      const int col = n0 + 128 * wn + 16 * ni + r;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 128 * wm + 16 * mi + 4 * g + i;
+        if (row < rows && col < F)
+          y[(m0 + row) * F + col] = (uint16_t)f32_to_bf16_rne(acc[mi][ni][i]);
+      }
+    }
+}
+
 // fp32: one output per thread, h ascending (small shapes).
 __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(const float* __restrict__ x,
                                                                const float* __restrict__ w,
@@ -321,6 +461,9 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(const float* __re
 #ifndef MOE_GEMM_TILE
 #define MOE_GEMM_TILE 256   // 256 x 256 output tiles (128 x 128 for small problems)
 #endif
+#ifndef MOE_GEMM_RING
+#define MOE_GEMM_RING 1     // the 4-slot LDS ring kernel for 256 x 256 tiles (H % 32 == 0)
+#endif
 #ifndef MOE_GEMM_DMA
 #define MOE_GEMM_DMA 0      // 1: global -> LDS without register staging (measured equal)
 #endif
@@ -350,8 +493,20 @@ hipError_t launch_grouped_linear(const void* x_perm, const void* weight, const i
   if (bf16) {
     // large tiles once every CU gets several of them, small ones otherwise
     const int64_t big = ((T + 255) / 256) * ((F + 255) / 256);
-    if (MOE_GEMM_TILE == 256 && big >= 1024)
+    if (MOE_GEMM_TILE == 256 && big >= 1024) {
+      if (MOE_GEMM_RING && H % 32 == 0) {
+        const int64_t mtiles = (T + 255) / 256 + E;
+        const int ntn = (F + 255) / 256;
+        const int64_t groups = (mtiles + kGroupM - 1) / kGroupM;
+        const int64_t blocks = ((groups + 7) / 8) * 8 * kGroupM * ntn;
+        hipLaunchKernelGGL(grouped_gemm_ring_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                           reinterpret_cast<const uint16_t*>(x_perm),
+                           reinterpret_cast<const uint16_t*>(weight), offsets, E, T, H, F, ntn,
+                           reinterpret_cast<uint16_t*>(y));
+        return hipGetLastError();
+      }
       return launch_gg<256, 256>(x_perm, weight, offsets, T, H, E, F, y, s);
+    }
     return launch_gg<128, 128>(x_perm, weight, offsets, T, H, E, F, y, s);
   } else {
     hipLaunchKernelGGL(grouped_gemm_f32_kernel, dim3((unsigned)((T * F + 255) / 256)), dim3(256),
