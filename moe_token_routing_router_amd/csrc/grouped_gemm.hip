@@ -58,6 +58,8 @@ __device__ __forceinline__ void lds_dma16(const void* src, char* lds_base) {
 // This workgroup's expert and rows: tiles of BM rows are numbered expert by
 // expert.  Offsets are clamped to [0, T] (inconsistent ones give wrong rows,
 // never an access outside x_perm or y).  Returns false past the last tile.
+// Works for any workgroup size: experts are taken one per thread by the first
+// four waves (E <= 256); s_scan holds 4 ints.
 template <int BM>
 __device__ __forceinline__ bool tile_of(const int32_t* offsets, int E, int64_t T, int id,
                                         int* s_e, int64_t* s_m0, int* s_rows, int* s_scan) {
@@ -68,7 +70,7 @@ __device__ __forceinline__ bool tile_of(const int32_t* offsets, int E, int64_t T
   const int64_t o1 = tid < E ? min(max((int64_t)offsets[tid + 1], o0), T) : 0;
   const int nt = (int)((o1 - o0 + BM - 1) / BM);
   const int incl = wave_inclusive_sum(nt);
-  if (lane == 63) s_scan[wid] = incl;
+  if (lane == 63 && wid < 4) s_scan[wid] = incl;
   if (tid == 0) *s_e = -1;
   __syncthreads();
   int base = 0;
@@ -300,7 +302,11 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(
 // the MFMAs.  Slot layout: 16-byte chunk c of row r at chunk
 // c ^ ((r >> 1) & 3), so the eight lanes of one LDS read phase (rows r..r+7
 // of one chunk column) hit eight different 16-byte bank groups.
-// Per step and wave: 8 copies (4 row blocks of A, 4 of B), counted by vmcnt
+// 8 waves (two per SIMD) in a 2 x 4 grid of 128 x 64 blocks: 128 accumulator
+// registers per wave leave the register allocator room (a 4-wave 128 x 128
+// layout fills all 256 AGPRs and the compiler shuffles accumulators), and
+// one wave's MFMAs cover the other's barrier and LDS reads.
+// Per step and wave: 4 copies (2 row blocks of A, 2 of B), counted by vmcnt
 // in issue order; the ring keeps each wait count constant (the last steps
 // re-copy the last step into slots nothing reads any more).
 //
@@ -325,14 +331,14 @@ __device__ __forceinline__ void wg_barrier() {
   asm volatile("" ::: "memory");
 }
 
-__global__ __launch_bounds__(256) void grouped_gemm_ring_kernel(
+__global__ __launch_bounds__(512) void grouped_gemm_ring_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
     const int32_t* __restrict__ offsets, int E, int64_t T, int H, int F, int ntn,
     uint16_t* __restrict__ y) {
   constexpr int BM = 256, BN = 256, RK = 32;  // K step (h) of one ring slot
   constexpr int SLOT = 2 * BM * 64;           // A then B, 64 bytes per row
   constexpr int RING = 4;
-  constexpr int MT = 8, NT = 8;               // 16 x 16 tiles per wave (rows, outputs)
+  constexpr int MT = 8, NT = 4;               // 16 x 16 tiles per wave (rows, outputs)
   __shared__ __align__(1024) char smem[RING * SLOT];
   __shared__ int s_e, s_rows;
   __shared__ int64_t s_m0;
@@ -347,39 +353,39 @@ __global__ __launch_bounds__(256) void grouped_gemm_ring_kernel(
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wid = tid >> 6;
+  const int wid = tid >> 6;   // 8 waves: a 2 x 4 grid of 128 x 64 blocks
   const int g = lane >> 4;
   const int r = lane & 15;
   const int wm = wid & 1;
   const int wn = wid >> 1;
 
-  // copies: instruction i of wave w fills rows 64i + 16w .. +16 of a tile;
+  // copies: wave w fills rows 32w + 16i .. +16 (i = 0, 1) of both tiles;
   // lane l -> row +l/4, slot chunk l%4, which holds global chunk
   // (l%4) ^ ((row >> 1) & 3).  Offsets are 32-bit from the tile's bases.
   const uint16_t* xa = x + m0 * H;
   const uint16_t* wb = w + ((int64_t)e * F) * H;
   const int dr = lane >> 2;
   const int dch = (lane & 3) ^ ((dr >> 1) & 3);
-  int aof[4], bof[4];
+  int aof[2], bof[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    aof[i] = min(64 * i + 16 * wid + dr, rows - 1) * H + 8 * dch;
-    bof[i] = min(n0 + 64 * i + 16 * wid + dr, F - 1) * H + 8 * dch;
+  for (int i = 0; i < 2; ++i) {
+    aof[i] = min(32 * wid + 16 * i + dr, rows - 1) * H + 8 * dch;
+    bof[i] = min(n0 + 32 * wid + 16 * i + dr, F - 1) * H + 8 * dch;
   }
   const uint32_t base = lds_addr(smem);
   // (the LDS destination of a copy is wave-uniform: M0 takes a scalar)
-  const uint32_t wbase = __builtin_amdgcn_readfirstlane(base + (uint32_t)(16 * wid * 64));
+  const uint32_t wbase = __builtin_amdgcn_readfirstlane(base + (uint32_t)(32 * wid * 64));
   auto copy_step = [&](int slot, int kt) {
     const uint32_t sa = wbase + (uint32_t)(slot * SLOT);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) lds_copy16(xa + aof[i] + kt * RK, sa + (uint32_t)(64 * i * 64));
+    for (int i = 0; i < 2; ++i) lds_copy16(xa + aof[i] + kt * RK, sa + (uint32_t)(16 * i * 64));
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      lds_copy16(wb + bof[i] + kt * RK, sa + (uint32_t)(BM * 64 + 64 * i * 64));
+    for (int i = 0; i < 2; ++i)
+      lds_copy16(wb + bof[i] + kt * RK, sa + (uint32_t)(BM * 64 + 16 * i * 64));
   };
-  // fragment reads: A rows 128*wm + 16*t + r, B rows 128*wn + 16*t + r, chunk g
+  // fragment reads: A rows 128*wm + 16*t + r, B rows 64*wn + 16*t + r, chunk g
   const int aoff = (128 * wm + r) * 64 + ((g ^ ((r >> 1) & 3)) << 4);
-  const int boff = BM * 64 + (128 * wn + r) * 64 + ((g ^ ((r >> 1) & 3)) << 4);
+  const int boff = BM * 64 + (64 * wn + r) * 64 + ((g ^ ((r >> 1) & 3)) << 4);
   f32x4_t acc[MT][NT];
 #pragma unroll
   for (int mi = 0; mi < MT; ++mi)
@@ -393,26 +399,24 @@ __global__ __launch_bounds__(256) void grouped_gemm_ring_kernel(
   copy_step(2, min(2, last));
   // step s: its copies landed (steps s+1, s+2 may still be in flight) ->
   // barrier -> refill the slot of step s-1 with step s+3 -> read step s's
-  // fragments -> its MFMAs (which drain while the next step's wait, barrier
-  // and reads proceed)
+  // fragments -> its MFMAs.  Two waves share each SIMD, so one's MFMAs cover
+  // the other's wait, barrier and reads.
   for (int s = 0; s < nk; ++s) {
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(16));
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(8));
     wg_barrier();
     copy_step((s + 3) & 3, min(s + 3, last));
-    // A fragments of all eight row tiles, then one B fragment at a time
-    // (fewer live registers: the 256 accumulators fill the AGPRs)
     const char* sl = smem + (s & 3) * SLOT;
-    u32x4 af[MT];
+    u32x4 af[MT], bf[NT];
 #pragma unroll
     for (int t = 0; t < MT; ++t) af[t] = *reinterpret_cast<const u32x4*>(sl + aoff + t * 1024);
 #pragma unroll
-    for (int ni = 0; ni < NT; ++ni) {
-      const u32x4 bv = *reinterpret_cast<const u32x4*>(sl + boff + ni * 1024);
+    for (int t = 0; t < NT; ++t) bf[t] = *reinterpret_cast<const u32x4*>(sl + boff + t * 1024);
 #pragma unroll
-      for (int mi = 0; mi < MT; ++mi)
-        acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(af[mi]), as_bf16x8(bv),
+    for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NT; ++ni)
+        acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(af[mi]), as_bf16x8(bf[ni]),
                                                               acc[mi][ni], 0, 0, 0);
-    }
   }
   // no copy may still be landing in LDS when the workgroup ends
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -421,7 +425,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_ring_kernel(
   for (int mi = 0; mi < MT; ++mi)
 #pragma unroll
     for (int ni = 0; ni < NT; ++ni) {
-      const int col = n0 + 128 * wn + 16 * ni + r;
+      const int col = n0 + 64 * wn + 16 * ni + r;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = 128 * wm + 16 * mi + 4 * g + i;
@@ -499,7 +503,7 @@ hipError_t launch_grouped_linear(const void* x_perm, const void* weight, const i
         const int ntn = (F + 255) / 256;
         const int64_t groups = (mtiles + kGroupM - 1) / kGroupM;
         const int64_t blocks = ((groups + 7) / 8) * 8 * kGroupM * ntn;
-        hipLaunchKernelGGL(grouped_gemm_ring_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+        hipLaunchKernelGGL(grouped_gemm_ring_kernel, dim3((unsigned)blocks), dim3(512), 0, s,
                            reinterpret_cast<const uint16_t*>(x_perm),
                            reinterpret_cast<const uint16_t*>(weight), offsets, E, T, H, F, ntn,
                            reinterpret_cast<uint16_t*>(y));
