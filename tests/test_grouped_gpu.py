@@ -95,3 +95,27 @@ def test_grouped_linear_headline_shape_sampled_rows():
     rows = np.unique(np.concatenate([edges, rng.integers(0, T, 64)])).astype(np.int32)
     ref = O.grouped_linear(x, W, off, "bf16", rows=rows)
     _check(got[rows], ref, x, W, off, rows, "bf16")
+
+
+@pytest.mark.parametrize("H,F", [(96, 1000), (32, 1024)])
+def test_grouped_linear_large_tiles_ragged_sampled_rows(H, F):
+    # enough tiles for the 256 x 256 path (its 32-wide K ring: H = 96 takes
+    # three steps, H = 32 one), a ragged last n-tile (F = 1000) and experts
+    # of every size including empty ones; sampled rows against the oracle
+    N, E, K = 33000, 40, 2
+    print(f"[grouped] large tiles H={H} F={F}", flush=True)
+    ids = I.random_ids(H + F, N, E, K, skew=0.8)
+    counts = np.bincount(ids.ravel(), minlength=E)
+    counts[[3, 17]] = 0
+    off = _offsets(counts)
+    T = int(off[-1]) + 3
+    x = I.random_case(H, T, H, 4, 1, "bf16", with_y=False)["x"]
+    W = I.expert_weights(F, E, F, H, "bf16")
+    got = _run(x, W, off, T, "bf16")
+    rng = np.random.default_rng(H)
+    n = int(off[-1])
+    edges = np.concatenate([off[:-1][counts > 0], off[1:][counts > 0] - 1])
+    rows = np.unique(np.concatenate([edges, rng.integers(0, n, 64)])).astype(np.int32)
+    ref = O.grouped_linear(x, W, off, "bf16", rows=rows)
+    _check(got[rows], ref, x, W, off, rows, "bf16")
+    assert (got[n:] == 0).all()

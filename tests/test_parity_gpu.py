@@ -293,6 +293,19 @@ def test_route_dispatch_edge_cases(N, H, E, K, dtype, bias):
     check_route(gids, gw_, ids_o, w_o, logits_o, K, dtype)
 
 
+# The fused call's two ways to the block bases: for K <= 2 and up to 512
+# router blocks (64 tokens each) the scatter sums the earlier blocks' counts
+# itself (more than 256 blocks: each thread sums several), beyond that the
+# scan kernel runs.
+@pytest.mark.parametrize("N,K,bias", [(30000, 2, True), (20000, 1, False), (40000, 2, False)])
+def test_route_dispatch_block_counts(N, K, bias):
+    print(f"[route_dispatch blocks] N={N} K={K}", flush=True)
+    d = I.random_case(N + K, N, 64, 64, K, "bf16", bias=bias)
+    ids_o, w_o, logits_o, _ = O.route(d["x"], d["gate_w"], d["bias"], K, "bf16")
+    gids, gw_ = _fused_and_check(d, K, 64, "bf16")
+    check_route(gids, gw_, ids_o, w_o, logits_o, K, "bf16")
+
+
 def test_route_dispatch_metadata_only():
     d = I.random_case(11, 777, 256, 64, 4, "bf16", bias=True)
     _fused_and_check(d, 4, 64, "bf16", with_rows=False)
