@@ -144,9 +144,12 @@ moe_status_t moe_dispatch(const int32_t* topk_ids, const void* x, int64_t N, int
       round_up((size_t)moe::dispatch_num_blocks(N, bt) * E * sizeof(int32_t), 256));
   hipError_t e = moe::launch_dispatch_count(topk_ids, N, E, K, lrank, bhist, s);
   if (e != hipSuccess) return MOE_ERR_HIP;
+  // the usual caller has just run the bf16 router over x: scatter in its
+  // XCD order
+  const int router_bt = dtype == MOE_BF16 ? moe::route_tokens_per_block(E) : 0;
   return from_hip(moe::launch_dispatch_finish(topk_ids, x, N, (int64_t)H * elem_bytes(dtype), E, K,
                                               bt, counts, offsets, perm, inv, x_perm, lrank,
-                                              bhist, s));
+                                              bhist, s, router_bt));
 }
 
 size_t moe_route_dispatch_workspace_size(int64_t N, int32_t H, int32_t E, int32_t K,
@@ -210,7 +213,7 @@ moe_status_t moe_route_dispatch(const void* x, const void* gate_w, const float* 
   if (e != hipSuccess) return MOE_ERR_HIP;
   return from_hip(moe::launch_dispatch_finish(topk_ids, x, N, (int64_t)H * elem_bytes(dtype), E, K,
                                               bt, counts, offsets, perm, inv, x_perm, lrank,
-                                              bhist, s));
+                                              bhist, s, dtype == MOE_BF16 ? bt : 0));
 }
 
 size_t moe_ep_dispatch_workspace_size(int64_t N, int32_t E, int32_t K, int32_t ep_size) {

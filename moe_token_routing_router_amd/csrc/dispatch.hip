@@ -40,6 +40,9 @@
 #ifndef MOE_SCATTER_TOKENS
 #define MOE_SCATTER_TOKENS 1   // tokens per scatter workgroup
 #endif
+#ifndef MOE_SCATTER_XCD
+#define MOE_SCATTER_XCD 1      // scatter tokens in the router's XCD order, last blocks first
+#endif
 #ifndef MOE_SCATTER_U
 #define MOE_SCATTER_U 4        // row vectors per lane loaded before their stores
 #endif
@@ -112,6 +115,20 @@ __global__ __launch_bounds__(256) void dispatch_scan_kernel(int32_t* __restrict_
   }
 }
 
+// Token of scatter workgroup g.  With xbt > 0 (one token per workgroup, N a
+// multiple of 8 * xbt): the router has just read x in blocks of xbt tokens,
+// block j on XCD j % 8 (the dispatcher's round robin), so the last blocks'
+// rows may still sit in that XCD's L2.  Workgroup g runs on XCD g % 8 and is
+// given a token of a block of that XCD, the XCD's last blocks first.
+// Otherwise tokens are taken in order.
+__device__ __forceinline__ int64_t scatter_token(int64_t g, int64_t N, int xbt) {
+  if (xbt == 0) return g * kScatterTokens;
+  const int64_t x = g & 7, q = g >> 3;
+  const int64_t per = N / (8 * (int64_t)xbt);  // blocks per XCD
+  const int64_t i = per - 1 - q / xbt;
+  return (int64_t)xbt * (x + 8 * i) + q % xbt;
+}
+
 // One workgroup per kScatterTokens tokens.  The rows' first loads are issued
 // before the index work (they do not depend on it), so the E-wide offset
 // scan and the index arithmetic overlap them.
@@ -124,12 +141,12 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
     const int32_t* __restrict__ bhist, const int32_t* __restrict__ lrank, int64_t N, int K,
     int E, int nb, int bt, int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
     int32_t* __restrict__ inv, const u32x4* __restrict__ x, u32x4* __restrict__ x_perm,
-    int row_vecs, int64_t dlim) {
+    int row_vecs, int64_t dlim, int xbt) {
   extern __shared__ int dst[];  // [kScatterTokens*K], then (PREFIX) red[4][kScatterTokens*K]
   __shared__ int off[kMaxExperts];
   __shared__ int scan_lds[4];
   const int tid = threadIdx.x;
-  const int64_t n0 = (int64_t)blockIdx.x * kScatterTokens;
+  const int64_t n0 = scatter_token(blockIdx.x, N, xbt);
   const int ntok = (int)min((int64_t)kScatterTokens, N - n0);
   int* red = dst + kScatterTokens * K;
 
@@ -236,9 +253,17 @@ hipError_t launch_dispatch_count(const int32_t* ids, int64_t N, int E, int K, in
 hipError_t launch_dispatch_finish(const int32_t* ids, const void* x, int64_t N, int64_t row_bytes,
                                   int E, int K, int bt, int32_t* counts, int32_t* offsets,
                                   int32_t* perm, int32_t* inv, void* x_perm,
-                                  const int32_t* lrank, int32_t* bhist, hipStream_t s) {
+                                  const int32_t* lrank, int32_t* bhist, hipStream_t s,
+                                  int router_bt) {
   return launch_dispatch_finish(ids, x, N, row_bytes, E, K, bt, counts, offsets, perm, inv, x_perm,
-                                lrank, bhist, N * K, s);
+                                lrank, bhist, N * K, s, router_bt);
+}
+
+// the token order of the scatter: XCD-matched to the router's blocks of
+// router_bt tokens when that is a bijection, else in order
+static int scatter_xbt(int64_t N, int router_bt) {
+  if (MOE_SCATTER_XCD == 0 || router_bt <= 0 || kScatterTokens != 1) return 0;
+  return N % (8 * (int64_t)router_bt) == 0 ? router_bt : 0;
 }
 
 hipError_t launch_dispatch_scatter_prefix(const int32_t* ids, const void* x, int64_t N,
@@ -252,7 +277,7 @@ hipError_t launch_dispatch_scatter_prefix(const int32_t* ids, const void* x, int
   hipLaunchKernelGGL(dispatch_scatter_kernel<true>, dim3((unsigned)blocks), dim3(256), dyn, s, ids,
                      counts, bhist, lrank, N, K, E, nb, bt, offsets, perm, inv,
                      reinterpret_cast<const u32x4*>(x), reinterpret_cast<u32x4*>(x_perm),
-                     (int)(row_bytes / 16), N * K);
+                     (int)(row_bytes / 16), N * K, scatter_xbt(N, bt));
   return hipGetLastError();
 }
 
@@ -260,7 +285,7 @@ hipError_t launch_dispatch_finish(const int32_t* ids, const void* x, int64_t N, 
                                   int E, int K, int bt, int32_t* counts, int32_t* offsets,
                                   int32_t* perm, int32_t* inv, void* x_perm,
                                   const int32_t* lrank, int32_t* bhist, int64_t dlim,
-                                  hipStream_t s) {
+                                  hipStream_t s, int router_bt) {
   const int nb = (int)dispatch_num_blocks(N, bt);
   hipLaunchKernelGGL(dispatch_scan_kernel, dim3(E), dim3(256), 0, s, bhist, nb, counts, E,
                      (int32_t*)nullptr);
@@ -271,7 +296,7 @@ hipError_t launch_dispatch_finish(const int32_t* ids, const void* x, int64_t N, 
   hipLaunchKernelGGL(dispatch_scatter_kernel<false>, dim3((unsigned)blocks), dim3(256), dyn, s, ids,
                      counts, bhist, lrank, N, K, E, nb, bt, offsets, perm, inv,
                      reinterpret_cast<const u32x4*>(x), reinterpret_cast<u32x4*>(x_perm),
-                     (int)(row_bytes / 16), dlim);
+                     (int)(row_bytes / 16), dlim, scatter_xbt(N, router_bt));
   return hipGetLastError();
 }
 

@@ -190,20 +190,24 @@ hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
 int64_t dispatch_num_blocks(int64_t N, int bt);
 hipError_t launch_dispatch_count(const int32_t* ids, int64_t N, int E, int K, int32_t* lrank,
                                  int32_t* bhist, hipStream_t s);
+// router_bt > 0: x was just read by the router in blocks of that many
+// tokens; the scatter then takes its tokens in the router's XCD order.
 hipError_t launch_dispatch_finish(const int32_t* ids, const void* x, int64_t N, int64_t row_bytes,
                                   int E, int K, int bt, int32_t* counts, int32_t* offsets,
                                   int32_t* perm, int32_t* inv, void* x_perm,
-                                  const int32_t* lrank, int32_t* bhist, hipStream_t s);
+                                  const int32_t* lrank, int32_t* bhist, hipStream_t s,
+                                  int router_bt = 0);
 // ... with destinations limited to [0, dlim) (perm, x_perm capacity; N*K above)
 hipError_t launch_dispatch_finish(const int32_t* ids, const void* x, int64_t N, int64_t row_bytes,
                                   int E, int K, int bt, int32_t* counts, int32_t* offsets,
                                   int32_t* perm, int32_t* inv, void* x_perm,
                                   const int32_t* lrank, int32_t* bhist, int64_t dlim,
-                                  hipStream_t s);
+                                  hipStream_t s, int router_bt = 0);
 
 // scatter only, for the fused path: bhist holds raw per-block counts and
 // counts their totals (the router's atomic histogram); each scatter
-// workgroup sums the blocks before its own.
+// workgroup sums the blocks before its own.  Tokens in the router's XCD
+// order (blocks of bt tokens).
 hipError_t launch_dispatch_scatter_prefix(const int32_t* ids, const void* x, int64_t N,
                                           int64_t row_bytes, int E, int K, int bt,
                                           const int32_t* counts, int32_t* offsets, int32_t* perm,
