@@ -353,11 +353,6 @@ __global__ __launch_bounds__(256) void route_bwd_wpart_kernel(
   if (e < 0) return;
   const int64_t p0 = s_p0 + (int64_t)(id - s_first) * kBwdChunk;
   const int rows = (int)min((int64_t)kBwdChunk, s_p1 - p0);
-  if (tid < rows) {
-    const int i = perm[p0 + tid];
-    coef[tid] = (unsigned)i < (unsigned long long)T ? dlsel[i] : 0.f;
-  }
-  __syncthreads();
 
   int cv[V];
   bool ok[V];
@@ -366,21 +361,33 @@ __global__ __launch_bounds__(256) void route_bwd_wpart_kernel(
     cv[v] = ((int)blockIdx.y * V + v) * 256 + tid;
     ok[v] = cv[v] < row_vecs;
   }
-  float acc[V][L];
-#pragma unroll
-  for (int v = 0; v < V; ++v)
-#pragma unroll
-    for (int j = 0; j < L; ++j) acc[v][j] = 0.f;
   const u32x4 zero = {0u, 0u, 0u, 0u};
   constexpr int RR = kBwdRows;
-  for (int r = 0; r < rows; r += RR) {
-    u32x4 xv[RR][V];
+  u32x4 xv[RR][V];
+  auto load_rows = [&](int r) {
 #pragma unroll
     for (int rr = 0; rr < RR; ++rr) {
       const int64_t p = p0 + min(r + rr, rows - 1);
 #pragma unroll
       for (int v = 0; v < V; ++v) xv[rr][v] = ok[v] ? ldnt(x_perm + p * row_vecs + cv[v]) : zero;
     }
+  };
+  // the first rows' loads do not depend on the coefficients: issue them
+  // before the perm -> dlsel gather and its barrier
+  load_rows(0);
+  if (tid < rows) {
+    const int i = perm[p0 + tid];
+    coef[tid] = (unsigned)i < (unsigned long long)T ? dlsel[i] : 0.f;
+  }
+  __syncthreads();
+
+  float acc[V][L];
+#pragma unroll
+  for (int v = 0; v < V; ++v)
+#pragma unroll
+    for (int j = 0; j < L; ++j) acc[v][j] = 0.f;
+  for (int r = 0; r < rows; r += RR) {
+    if (r > 0) load_rows(r);
 #pragma unroll
     for (int rr = 0; rr < RR; ++rr) {
       if (r + rr >= rows) break;
@@ -424,8 +431,18 @@ __global__ __launch_bounds__(256) void route_bwd_wreduce_kernel(
   // only) are left out
   const int64_t c0 = min((int64_t)chunk_base[e], nchunks);
   const int64_t c1 = min((int64_t)chunk_base[e + 1], nchunks);
+  // chunks in order; four loads in flight ahead of the (ordered) adds
   float s = 0.f;
-  for (int64_t c = c0; c < c1; ++c) s += part[c * H + h];
+  int64_t c = c0;
+  for (; c + 4 <= c1; c += 4) {
+    const float a0 = part[c * H + h], a1 = part[(c + 1) * H + h];
+    const float a2 = part[(c + 2) * H + h], a3 = part[(c + 3) * H + h];
+    s += a0;
+    s += a1;
+    s += a2;
+    s += a3;
+  }
+  for (; c < c1; ++c) s += part[c * H + h];
   dgate_w[h * E + e] = s;
   if (dbias && h == 0) {
     float b = 0.f;
