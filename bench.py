@@ -308,6 +308,23 @@ def main():
             call(name, i)
         _, ms = timed(lambda i, n=name: call(n, i), args.steps)
         stage_ms[name] = ms / args.steps
+    # the spread of single calls: one pair of HIP events around each call
+    # (the events add a little to every call, so the back-to-back average
+    # above is the figure of record)
+    stage_dist = {}
+    for name in ("route_dispatch", "combine", "route", "dispatch"):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for i, (a, z) in enumerate(evs):
+            a.record(stream)
+            call(name, i)
+            z.record(stream)
+        torch.cuda.synchronize()
+        us = np.array([a.elapsed_time(z) * 1e3 for a, z in evs])
+        stage_dist[name] = {"p10_us": round(float(np.percentile(us, 10)), 2),
+                            "p50_us": round(float(np.percentile(us, 50)), 2),
+                            "p90_us": round(float(np.percentile(us, 90)), 2)}
 
     # The other calls of the library, each measured on its own.  Their
     # buffers are allocated only now, so the timed regions above run with the
@@ -451,6 +468,32 @@ def main():
                 "traffic": traffic, "alg_bytes_per_launch": alg[kern],
                 "avg_launch_ms": round(avg_ms, 5)}
 
+    # Context: plain PyTorch kernels with the stages' read:write mixes on
+    # buffers of the same size (rotating three sets, like the path): a 1:1
+    # copy, dispatch's 1:2 fan-out (index_select repeating each row twice) and
+    # combine's 2:1 (the sum of row pairs).  Algorithmic GB/s.
+    def plain_gbs(fn, nbytes, n=20):
+        for i in range(3):
+            fn(i)
+        _, ms = timed(fn, n)
+        return round(nbytes / (ms / n * 1e-3) / 1e9, 1)
+    rep2 = torch.arange(N, device=dev).repeat_interleave(K)
+    ceilings = {
+        "copy_1to1": plain_gbs(lambda i: sets[i % N_SETS]["out"].copy_(sets[i % N_SETS]["x"]),
+                               2 * N * H * b),
+        "fanout_1toK": plain_gbs(
+            lambda i: torch.index_select(sets[i % N_SETS]["x"], 0, rep2,
+                                         out=sets[i % N_SETS]["x_perm"]), N * H * b + T * H * b),
+        "sum_Kto1": plain_gbs(
+            lambda i: torch.sum(sets[i % N_SETS]["y"].view(N, K, H), dim=1,
+                                out=sets[i % N_SETS]["out"]), T * H * b + N * H * b),
+        "note": "plain PyTorch kernels, same sizes, read:write mixes of copy, dispatch, combine",
+    }
+    # leave the outputs of the path consistent for the check below
+    for i in range(N_SETS):
+        step(i)
+    torch.cuda.synchronize()
+
     if args.copy_calibration:
         a = torch.empty((256 << 20,), dtype=torch.uint8, device=dev)
         bb = torch.empty_like(a)
@@ -480,6 +523,8 @@ def main():
                              "gpu_ms_per_step": round(gpu_ms_u / args.steps, 5),
                              "tokens_per_s": round(N * args.steps / wall_u, 1)},
         "stages": stages,
+        "stage_spread_us": stage_dist,
+        "plain_kernel_ceilings_GBs": ceilings,
         "load_max_over_mean": round(float(load.max() / load.mean()), 3),
         "small_workloads_graph": graphs,
         "roofline": roofline,
