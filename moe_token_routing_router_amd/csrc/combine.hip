@@ -16,7 +16,7 @@
 
 // Tuning knobs (compile-time; the defaults are the measured best on MI355X).
 #ifndef MOE_COMBINE_TOKENS
-#define MOE_COMBINE_TOKENS 1   // tokens per workgroup
+#define MOE_COMBINE_TOKENS 2   // tokens per workgroup
 #endif
 #ifndef MOE_COMBINE_U2
 #define MOE_COMBINE_U2 4        // output vectors per lane in flight for K = 2
