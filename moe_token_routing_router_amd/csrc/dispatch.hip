@@ -44,7 +44,7 @@
 #define MOE_SCATTER_XCD 1      // scatter tokens in the router's XCD order, last blocks first
 #endif
 #ifndef MOE_SCATTER_U
-#define MOE_SCATTER_U 4        // row vectors per lane loaded before their stores
+#define MOE_SCATTER_U 2        // row vectors per lane loaded before their stores
 #endif
 
 namespace moe {

@@ -32,7 +32,7 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kEpRowU = 4;  // row vectors per lane loaded before their stores
+constexpr int kEpRowU = 2;  // row vectors per lane loaded before their stores
 
 __device__ __forceinline__ u32x4 ld_nt(const u32x4* p) { return __builtin_nontemporal_load(p); }
 __device__ __forceinline__ void st_nt(u32x4* p, u32x4 v) { __builtin_nontemporal_store(v, p); }
