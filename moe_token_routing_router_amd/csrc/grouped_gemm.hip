@@ -93,7 +93,10 @@ __device__ __forceinline__ bool tile_of(const int32_t* offsets, int E, int64_t T
 // token rows and its expert's weight rows are then fetched into that XCD's
 // L2 once and reused by every n-tile, instead of every XCD streaming every
 // operand.  Padding ids (past the last group) do nothing.
-constexpr int kGroupM = 2;
+#ifndef MOE_GEMM_GROUP_M
+#define MOE_GEMM_GROUP_M 2   // consecutive m-tiles (with all their n-tiles) per XCD group
+#endif
+constexpr int kGroupM = MOE_GEMM_GROUP_M;
 
 __device__ __forceinline__ bool tile_coords(int ntn, int* mt, int* nt) {
   const int b = blockIdx.x;
