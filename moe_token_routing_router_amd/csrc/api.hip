@@ -146,7 +146,7 @@ moe_status_t moe_dispatch(const int32_t* topk_ids, const void* x, int64_t N, int
   if (e != hipSuccess) return MOE_ERR_HIP;
   // the usual caller has just run the bf16 router over x: scatter in its
   // XCD order
-  const int router_bt = dtype == MOE_BF16 ? moe::route_tokens_per_block(E) : 0;
+  const int router_bt = dtype == MOE_BF16 ? moe::route_tokens_per_block(E, N) : 0;
   return from_hip(moe::launch_dispatch_finish(topk_ids, x, N, (int64_t)H * elem_bytes(dtype), E, K,
                                               bt, counts, offsets, perm, inv, x_perm, lrank,
                                               bhist, s, router_bt));
@@ -156,7 +156,7 @@ size_t moe_route_dispatch_workspace_size(int64_t N, int32_t H, int32_t E, int32_
                                          moe_dtype_t dtype) {
   if (N < 0 || H <= 0 || E <= 0 || E > moe::kMaxExperts || K < 1 || !valid_dtype(dtype)) return 0;
   const int bt =
-      dtype == MOE_BF16 ? moe::route_tokens_per_block(E) : moe::dispatch_count_tokens(K);
+      dtype == MOE_BF16 ? moe::route_tokens_per_block(E, N) : moe::dispatch_count_tokens(K);
   return moe_route_workspace_size(H, E, dtype) + dispatch_scratch_bytes(N, E, K, bt);
 }
 
@@ -181,7 +181,7 @@ moe_status_t moe_route_dispatch(const void* x, const void* gate_w, const float* 
     return MOE_ERR_WORKSPACE_TOO_SMALL;
   const size_t rws = moe_route_workspace_size(H, E, dtype);
   const int bt =
-      dtype == MOE_BF16 ? moe::route_tokens_per_block(E) : moe::dispatch_count_tokens(K);
+      dtype == MOE_BF16 ? moe::route_tokens_per_block(E, N) : moe::dispatch_count_tokens(K);
   char* base = reinterpret_cast<char*>(workspace);
   int32_t* bhist = reinterpret_cast<int32_t*>(base + rws);
   int32_t* lrank = reinterpret_cast<int32_t*>(

@@ -172,7 +172,7 @@ __device__ __forceinline__ void block_stable_rank(const int* sids, int S, int E,
 // (blocks of route_tokens_per_block(E) tokens; see launch_dispatch_finish).
 int route_padded_experts(int E);
 int route_gate_rows(int H);  // H rounded up to whole 64-wide steps (packed gate)
-int route_tokens_per_block(int E);
+int route_tokens_per_block(int E, int64_t N);  // tokens per router workgroup
 hipError_t launch_gate_transpose(const uint16_t* gate_w, int H, int E, uint16_t* wgt,
                                  int32_t* counts, hipStream_t s);
 hipError_t launch_route_bf16(const uint16_t* x, const uint16_t* wgt, const float* bias,

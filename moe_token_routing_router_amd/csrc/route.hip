@@ -596,7 +596,16 @@ hipError_t launch_gate_transpose(const uint16_t* gate_w, int H, int E, uint16_t*
   return hipGetLastError();
 }
 
-int route_tokens_per_block(int E) { return 16 * route_mt(route_padded_experts(E)); }
+// For 32 < E <= 128 the workgroup takes 64 tokens only when that still gives
+// every CU a workgroup (N >= 256 * 64); smaller N use 32-token workgroups,
+// twice as many, so more CUs stream x (the gate is read once per workgroup).
+constexpr int64_t kRouteSmallN = 256 * 64;
+static bool route_small(int EP, int64_t N) { return (EP == 64 || EP == 128) && N < kRouteSmallN; }
+
+int route_tokens_per_block(int E, int64_t N) {
+  const int EP = route_padded_experts(E);
+  return route_small(EP, N) ? 32 : 16 * route_mt(EP);
+}
 
 hipError_t launch_route_bf16(const uint16_t* x, const uint16_t* wgt, const float* bias, int64_t N,
                              int H, int E, int K, int32_t* ids, float* w, int32_t* counts,
@@ -609,9 +618,13 @@ hipError_t launch_route_bf16(const uint16_t* x, const uint16_t* wgt, const float
       return launch_bf16_nt<2, route_mt(32)>(x, wgt, bias, N, H, E, K, ids, w, counts, lrank,
                                              bhist, s);
     case 64:
+      if (route_small(64, N))
+        return launch_bf16_nt<4, 2>(x, wgt, bias, N, H, E, K, ids, w, counts, lrank, bhist, s);
       return launch_bf16_nt<4, route_mt(64)>(x, wgt, bias, N, H, E, K, ids, w, counts, lrank,
                                              bhist, s);
     case 128:
+      if (route_small(128, N))
+        return launch_bf16_nt<8, 2>(x, wgt, bias, N, H, E, K, ids, w, counts, lrank, bhist, s);
       return launch_bf16_nt<8, route_mt(128)>(x, wgt, bias, N, H, E, K, ids, w, counts, lrank,
                                               bhist, s);
     case 256:
