@@ -128,6 +128,7 @@ BWD_EDGE = [
     (203, 96, 128, 8, "bf16", True),
     (1000, 264, 32, 3, "f32", False),     # generic K, fp32
     (5000, 128, 64, 6, "bf16", True),
+    (600, 8192, 64, 2, "bf16", False),    # rows wider than one pass of the row loops
 ]
 
 

@@ -138,6 +138,8 @@ EDGE = [
     (1000, 264, 32, 2, "f32", False),
     (5000, 128, 64, 6, "bf16", True),     # many dispatch sub-chunks
     (2000, 64, 256, 4, "bf16", True),     # fused path: histograms too many for the in-router scan
+    (1500, 8192, 64, 2, "bf16", False),   # rows wider than one pass of the row-copy loops
+    (700, 16384, 32, 4, "bf16", True),
 ]
 
 
@@ -329,6 +331,7 @@ EP_CASES = [
     (4096, 2048, 64, 4, 4, "bf16", 0.5),
     (1000, 264, 32, 2, 32, "f32", 0.0),      # one expert per rank: nothing to deduplicate
     (777, 64, 48, 6, 1, "bf16", 0.0),        # one rank: every token once
+    (1200, 8192, 64, 4, 4, "bf16", 0.5),     # rows wider than one pass of the row copy
     (1, 8, 4, 4, 2, "bf16", 0.0),
     (129, 520, 256, 16, 16, "bf16", 0.0),    # E and K at their limits
     (3001, 64, 48, 4, 12, "bf16", 4.0),      # skewed: empty experts and ranks
@@ -401,7 +404,7 @@ def test_aggregate_full_size(name):
     check_combine(from_dev(out), O.aggregate(d["y"], o["inv"], o["w"], d["x"], dt), dt)
 
 
-@pytest.mark.parametrize("N,H,E,K,dtype,bias", EDGE[:6])
+@pytest.mark.parametrize("N,H,E,K,dtype,bias", EDGE[:6] + EDGE[-2:])
 def test_aggregate_edge_cases_and_in_place(N, H, E, K, dtype, bias):
     print(f"[aggregate edge] N={N} H={H} E={E} K={K} {dtype}", flush=True)
     d = I.random_case(N * 3 + H, N, H, E, K, dtype, bias=bias)
