@@ -28,6 +28,13 @@
 // fp32 inputs use a plain fp32 FMA kernel (one output per thread).
 #include "moe_internal.h"
 
+#ifndef MOE_GEMM_SMALL_RING
+#define MOE_GEMM_SMALL_RING 1     // small problems: 128 x 256 ring tiles (0: the 128 x 128 kernel)
+#endif
+#ifndef MOE_GEMM_RING128_SLOTS
+#define MOE_GEMM_RING128_SLOTS 3  // ring slots of the 128-row ring tiles
+#endif
+
 namespace moe {
 
 namespace {
@@ -334,14 +341,19 @@ __device__ __forceinline__ void wg_barrier() {
   asm volatile("" ::: "memory");
 }
 
+template <int BM>
 __global__ __launch_bounds__(512) void grouped_gemm_ring_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
     const int32_t* __restrict__ offsets, int E, int64_t T, int H, int F, int ntn,
     uint16_t* __restrict__ y) {
-  constexpr int BM = 256, BN = 256, RK = 32;  // K step (h) of one ring slot
-  constexpr int SLOT = 2 * BM * 64;           // A then B, 64 bytes per row
-  constexpr int RING = 4;
-  constexpr int MT = 8, NT = 4;               // 16 x 16 tiles per wave (rows, outputs)
+  constexpr int BN = 256, RK = 32;            // K step (h) of one ring slot
+  constexpr int SLOT = (BM + BN) * 64;        // A then B, 64 bytes per row
+  // ring slots: 4 for 256-row tiles (128 KiB, one workgroup per CU); 3 for
+  // 128-row tiles (72 KiB: two workgroups per CU)
+  constexpr int RING = BM == 256 ? 4 : MOE_GEMM_RING128_SLOTS;
+  constexpr int MT = BM / 32, NT = 4;         // 16 x 16 tiles per wave (rows, outputs)
+  constexpr int LA = BM / 128;                // A copies per wave and step (B: 2)
+  constexpr int OPS = LA + 2;
   __shared__ __align__(1024) char smem[RING * SLOT];
   __shared__ int s_e, s_rows;
   __shared__ int64_t s_m0;
@@ -356,38 +368,41 @@ __global__ __launch_bounds__(512) void grouped_gemm_ring_kernel(
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wid = tid >> 6;   // 8 waves: a 2 x 4 grid of 128 x 64 blocks
+  const int wid = tid >> 6;   // 8 waves: a 2 x 4 grid of (BM/2) x 64 blocks
   const int g = lane >> 4;
   const int r = lane & 15;
   const int wm = wid & 1;
   const int wn = wid >> 1;
 
-  // copies: wave w fills rows 32w + 16i .. +16 (i = 0, 1) of both tiles;
-  // lane l -> row +l/4, slot chunk l%4, which holds global chunk
-  // (l%4) ^ ((row >> 1) & 3).  Offsets are 32-bit from the tile's bases.
+  // copies: wave w fills A rows (BM/8)w + 16i .. +16 (i < LA) and B rows
+  // 32w + 16i .. +16 (i < 2); lane l -> row +l/4, slot chunk l%4, which holds
+  // global chunk (l%4) ^ ((row >> 1) & 3).  Offsets are 32-bit from the
+  // tile's bases.
   const uint16_t* xa = x + m0 * H;
   const uint16_t* wb = w + ((int64_t)e * F) * H;
   const int dr = lane >> 2;
   const int dch = (lane & 3) ^ ((dr >> 1) & 3);
-  int aof[2], bof[2];
+  int aof[LA], bof[2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    aof[i] = min(32 * wid + 16 * i + dr, rows - 1) * H + 8 * dch;
-    bof[i] = min(n0 + 32 * wid + 16 * i + dr, F - 1) * H + 8 * dch;
-  }
+  for (int i = 0; i < LA; ++i) aof[i] = min((BM / 8) * wid + 16 * i + dr, rows - 1) * H + 8 * dch;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) bof[i] = min(n0 + 32 * wid + 16 * i + dr, F - 1) * H + 8 * dch;
   const uint32_t base = lds_addr(smem);
   // (the LDS destination of a copy is wave-uniform: M0 takes a scalar)
-  const uint32_t wbase = __builtin_amdgcn_readfirstlane(base + (uint32_t)(32 * wid * 64));
+  const uint32_t abase = __builtin_amdgcn_readfirstlane(base + (uint32_t)((BM / 8) * wid * 64));
+  const uint32_t bbase =
+      __builtin_amdgcn_readfirstlane(base + (uint32_t)(BM * 64 + 32 * wid * 64));
   auto copy_step = [&](int slot, int kt) {
-    const uint32_t sa = wbase + (uint32_t)(slot * SLOT);
+    const uint32_t so = (uint32_t)(slot * SLOT);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) lds_copy16(xa + aof[i] + kt * RK, sa + (uint32_t)(16 * i * 64));
+    for (int i = 0; i < LA; ++i)
+      lds_copy16(xa + aof[i] + kt * RK, abase + so + (uint32_t)(16 * i * 64));
 #pragma unroll
     for (int i = 0; i < 2; ++i)
-      lds_copy16(wb + bof[i] + kt * RK, sa + (uint32_t)(BM * 64 + 16 * i * 64));
+      lds_copy16(wb + bof[i] + kt * RK, bbase + so + (uint32_t)(16 * i * 64));
   };
-  // fragment reads: A rows 128*wm + 16*t + r, B rows 64*wn + 16*t + r, chunk g
-  const int aoff = (128 * wm + r) * 64 + ((g ^ ((r >> 1) & 3)) << 4);
+  // fragment reads: A rows (BM/2)*wm + 16*t + r, B rows 64*wn + 16*t + r, chunk g
+  const int aoff = ((BM / 2) * wm + r) * 64 + ((g ^ ((r >> 1) & 3)) << 4);
   const int boff = BM * 64 + (64 * wn + r) * 64 + ((g ^ ((r >> 1) & 3)) << 4);
   f32x4_t acc[MT][NT];
 #pragma unroll
@@ -397,18 +412,17 @@ __global__ __launch_bounds__(512) void grouped_gemm_ring_kernel(
 
   const int nk = H / RK;
   const int last = nk - 1;
-  copy_step(0, 0);
-  copy_step(1, min(1, last));
-  copy_step(2, min(2, last));
+#pragma unroll
+  for (int j = 0; j < RING - 1; ++j) copy_step(j, min(j, last));
   // step s: its copies landed (steps s+1, s+2 may still be in flight) ->
   // barrier -> refill the slot of step s-1 with step s+3 -> read step s's
   // fragments -> its MFMAs.  Two waves share each SIMD, so one's MFMAs cover
   // the other's wait, barrier and reads.
   for (int s = 0; s < nk; ++s) {
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(8));
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((RING - 2) * OPS));
     wg_barrier();
-    copy_step((s + 3) & 3, min(s + 3, last));
-    const char* sl = smem + (s & 3) * SLOT;
+    copy_step((s + RING - 1) % RING, min(s + RING - 1, last));
+    const char* sl = smem + (s % RING) * SLOT;
     u32x4 af[MT], bf[NT];
 #pragma unroll
     for (int t = 0; t < MT; ++t) af[t] = *reinterpret_cast<const u32x4*>(sl + aoff + t * 1024);
@@ -431,7 +445,7 @@ __global__ __launch_bounds__(512) void grouped_gemm_ring_kernel(
       const int col = n0 + 64 * wn + 16 * ni + r;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int row = 128 * wm + 16 * mi + 4 * g + i;
+        const int row = (BM / 2) * wm + 16 * mi + 4 * g + i;
         if (row < rows && col < F)
           y[(m0 + row) * F + col] = (uint16_t)f32_to_bf16_rne(acc[mi][ni][i]);
       }
@@ -471,6 +485,9 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(const float* __re
 #ifndef MOE_GEMM_RING
 #define MOE_GEMM_RING 1     // the 4-slot LDS ring kernel for 256 x 256 tiles (H % 32 == 0)
 #endif
+#ifndef MOE_GEMM_RING_BM
+#define MOE_GEMM_RING_BM 256  // rows per tile of the ring kernel (256 or 128)
+#endif
 #ifndef MOE_GEMM_DMA
 #define MOE_GEMM_DMA 0      // 1: global -> LDS without register staging (measured equal)
 #endif
@@ -492,6 +509,20 @@ hipError_t launch_gg(const void* x_perm, const void* weight, const int32_t* offs
   return hipGetLastError();
 }
 
+template <int RBM>
+hipError_t launch_ring(const void* x_perm, const void* weight, const int32_t* offsets, int64_t T,
+                       int H, int E, int F, void* y, hipStream_t s) {
+  const int64_t mtiles = (T + RBM - 1) / RBM + E;
+  const int ntn = (F + 255) / 256;
+  const int64_t groups = (mtiles + kGroupM - 1) / kGroupM;
+  const int64_t blocks = ((groups + 7) / 8) * 8 * kGroupM * ntn;
+  hipLaunchKernelGGL(grouped_gemm_ring_kernel<RBM>, dim3((unsigned)blocks), dim3(512), 0, s,
+                     reinterpret_cast<const uint16_t*>(x_perm),
+                     reinterpret_cast<const uint16_t*>(weight), offsets, E, T, H, F, ntn,
+                     reinterpret_cast<uint16_t*>(y));
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_grouped_linear(const void* x_perm, const void* weight, const int32_t* offsets,
@@ -500,20 +531,13 @@ hipError_t launch_grouped_linear(const void* x_perm, const void* weight, const i
   if (bf16) {
     // large tiles once every CU gets several of them, small ones otherwise
     const int64_t big = ((T + 255) / 256) * ((F + 255) / 256);
+    const bool ring = MOE_GEMM_RING && H % 32 == 0;
     if (MOE_GEMM_TILE == 256 && big >= 1024) {
-      if (MOE_GEMM_RING && H % 32 == 0) {
-        const int64_t mtiles = (T + 255) / 256 + E;
-        const int ntn = (F + 255) / 256;
-        const int64_t groups = (mtiles + kGroupM - 1) / kGroupM;
-        const int64_t blocks = ((groups + 7) / 8) * 8 * kGroupM * ntn;
-        hipLaunchKernelGGL(grouped_gemm_ring_kernel, dim3((unsigned)blocks), dim3(512), 0, s,
-                           reinterpret_cast<const uint16_t*>(x_perm),
-                           reinterpret_cast<const uint16_t*>(weight), offsets, E, T, H, F, ntn,
-                           reinterpret_cast<uint16_t*>(y));
-        return hipGetLastError();
-      }
+      if (ring) return launch_ring<MOE_GEMM_RING_BM>(x_perm, weight, offsets, T, H, E, F, y, s);
       return launch_gg<256, 256>(x_perm, weight, offsets, T, H, E, F, y, s);
     }
+    if (ring && MOE_GEMM_SMALL_RING)
+      return launch_ring<128>(x_perm, weight, offsets, T, H, E, F, y, s);
     return launch_gg<128, 128>(x_perm, weight, offsets, T, H, E, F, y, s);
   } else {
     hipLaunchKernelGGL(grouped_gemm_f32_kernel, dim3((unsigned)((T * F + 255) / 256)), dim3(256),
