@@ -22,7 +22,11 @@
 //          index work) and written to its K rows with 16-byte stores.
 //
 // The fused router (route.hip) produces lrank and bhist in its own epilogue,
-// so moe_route_dispatch skips the count kernel.
+// so moe_route_dispatch skips the count kernel; for K <= 2 the router also
+// adds its block histograms into counts and the scatter sums the earlier
+// blocks' counts itself, so the scan kernel is skipped too.  Right after the
+// router, the scatter takes its tokens in the router's XCD order (see
+// scatter_token) so part of its read of x hits L2.
 //
 // Atomics only ever produce counts; every position comes from a deterministic
 // rank, so the output is bitwise reproducible and equal to a stable argsort.

@@ -9,22 +9,24 @@
 // the expert-contiguous layout is what makes the rows of one expert a dense
 // operand.  The pages' GroupLinear is an FP8 DeepGEMM kernel for NVIDIA
 // parts; this one is bf16 on CDNA4 matrix cores:
-//  * a workgroup computes a BM x BN tile of one expert's output (256 x 256
-//    once there are enough tiles to fill the chip, else 128 x 128); its
-//    m-tiles are numbered expert by expert (the BM-row tiles of expert e
-//    start at tile sum_{e'<e} ceil(count[e'] / BM)), so each expert's ragged
-//    last tile stays inside its segment;
+//  * a workgroup computes a BM x 256 tile of one expert's output (BM = 256
+//    once there are enough tiles to fill the chip, else 128); its m-tiles
+//    are numbered expert by expert (the BM-row tiles of expert e start at
+//    tile sum_{e'<e} ceil(count[e'] / BM)), so each expert's ragged last
+//    tile stays inside its segment;
 //  * tiles are ordered for the 8 XCDs: each XCD gets whole groups of two
 //    consecutive m-tiles with all their n-tiles, so a group's token rows and
 //    its expert's weight rows are fetched into that XCD's L2 once;
 //  * both operands are K-contiguous rows (token rows of x_perm, weight rows
-//    of one output each), loaded with coalesced 16-byte loads into LDS tiles
-//    with an XOR swizzle (16-byte chunk c of row r at c ^ (r & 7)), double
-//    buffered: the next 64-wide K step is loaded while the current one feeds
-//    the matrix cores (through registers, or with MOE_GEMM_DMA straight into
-//    LDS with global_load_lds_dwordx4 -- measured equal);
-//  * 4 waves, each a (BM/2) x (BN/2) block of v_mfma_f32_16x16x32_bf16
-//    tiles, fp32 accumulation, one rounding to bf16 at the end.
+//    of one output each), copied global -> LDS with global_load_lds_dwordx4
+//    into a ring of 32-wide K steps three (two) steps ahead of the MFMAs,
+//    16-byte chunk c of row r at chunk c ^ ((r >> 1) & 3);
+//  * 8 waves (two per SIMD) in a 2 x 4 grid of (BM/2) x 64 blocks of
+//    v_mfma_f32_16x16x32_bf16 tiles, fp32 accumulation, one rounding to bf16
+//    at the end.
+// When H % 32 != 0: 256 x 256 or 128 x 128 tiles of 4 waves with 64-wide K
+// steps double-buffered through registers (or, with MOE_GEMM_DMA, straight
+// into LDS -- measured equal), chunk c of row r at c ^ (r & 7).
 // fp32 inputs use a plain fp32 FMA kernel (one output per thread).
 #include "moe_internal.h"
 

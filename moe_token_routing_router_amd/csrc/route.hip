@@ -10,10 +10,11 @@
 // is laid out for CDNA4 instead:
 //  * the contraction runs on v_mfma_f32_16x16x32_bf16 (bf16 products are exact
 //    in fp32, accumulation in fp32);
-//  * the gate is first re-laid out expert-major (wgt[e][h], padded to a
-//    multiple of 16 experts) so both MFMA operands are read straight from
-//    global memory into registers with 16-byte loads -- x from HBM exactly
-//    once, wgt from L2 -- and no LDS staging is needed for the contraction;
+//  * the gate is first re-laid out fragment-major (each MFMA B fragment one
+//    contiguous 1 KiB block, padded to a multiple of 16 experts), so a wave
+//    reads it from L2 with one 16-byte load per lane and fragment;
+//  * token rows are read from HBM exactly once with coalesced 16-byte loads
+//    and pass through the wave's own XOR-swizzled LDS tile into MFMA layout;
 //  * a workgroup owns BM = 16*MT tokens; its NW waves split H and their fp32
 //    partial logits are summed through LDS in a fixed order (deterministic);
 //  * softmax/top-K/renorm happen in registers: a token's logits live in one
