@@ -36,6 +36,9 @@
 #ifndef MOE_GEMM_RING128_SLOTS
 #define MOE_GEMM_RING128_SLOTS 3  // ring slots of the 128-row ring tiles
 #endif
+#ifndef MOE_GEMM_HALF_SKIP
+#define MOE_GEMM_HALF_SKIP 1      // ring tiles: waves whose half of a ragged tile is empty skip MFMAs
+#endif
 
 namespace moe {
 
@@ -420,10 +423,16 @@ __global__ __launch_bounds__(512) void grouped_gemm_ring_kernel(
   // barrier -> refill the slot of step s-1 with step s+3 -> read step s's
   // fragments -> its MFMAs.  Two waves share each SIMD, so one's MFMAs cover
   // the other's wait, barrier and reads.
+  // A ragged tile whose rows all lie in the first half: the waves of the
+  // second half copy and meet every barrier but skip their reads and MFMAs,
+  // which leaves the matrix units of each SIMD to the other wave.
+  const bool live =
+      !MOE_GEMM_HALF_SKIP || __builtin_amdgcn_readfirstlane((int)(wm == 0 || rows > BM / 2)) != 0;
   for (int s = 0; s < nk; ++s) {
     __builtin_amdgcn_s_waitcnt(vmcnt_imm((RING - 2) * OPS));
     wg_barrier();
     copy_step((s + RING - 1) % RING, min(s + RING - 1, last));
+    if (!live) continue;
     const char* sl = smem + (s % RING) * SLOT;
     u32x4 af[MT], bf[NT];
 #pragma unroll
