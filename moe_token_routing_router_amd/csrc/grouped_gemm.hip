@@ -19,8 +19,10 @@
 //    its expert's weight rows are fetched into that XCD's L2 once;
 //  * both operands are K-contiguous rows (token rows of x_perm, weight rows
 //    of one output each), copied global -> LDS with global_load_lds_dwordx4
-//    into a ring of 32-wide K steps three (two) steps ahead of the MFMAs,
-//    16-byte chunk c of row r at chunk c ^ ((r >> 1) & 3);
+//    into a ring of K steps ahead of the MFMAs: 64-wide steps (whole
+//    128-byte lines of each row) in two 64 KiB slots for 256-row tiles when
+//    H % 64 == 0, else 32-wide steps in four (three) slots, the 16-byte
+//    chunks of each row XOR-swizzled;
 //  * 8 waves (two per SIMD) in a 2 x 4 grid of (BM/2) x 64 blocks of
 //    v_mfma_f32_16x16x32_bf16 tiles, fp32 accumulation, one rounding to bf16
 //    at the end.
@@ -311,18 +313,23 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(
     }
 }
 
-// 256 x 256 tiles with a 4-slot ring of 32-wide K steps in LDS (H % 32 == 0):
-// each step's A and B tiles (256 rows x 64 bytes each) are copied
-// global -> LDS with global_load_lds (no registers), three steps ahead of
-// the MFMAs.  Slot layout: 16-byte chunk c of row r at chunk
-// c ^ ((r >> 1) & 3), so the eight lanes of one LDS read phase (rows r..r+7
-// of one chunk column) hit eight different 16-byte bank groups.
-// 8 waves (two per SIMD) in a 2 x 4 grid of 128 x 64 blocks: 128 accumulator
-// registers per wave leave the register allocator room (a 4-wave 128 x 128
-// layout fills all 256 AGPRs and the compiler shuffles accumulators), and
-// one wave's MFMAs cover the other's barrier and LDS reads.
-// Per step and wave: 4 copies (2 row blocks of A, 2 of B), counted by vmcnt
-// in issue order; the ring keeps each wait count constant (the last steps
+// Ring tiles (H % RK == 0): each K step's A and B tiles (BM and 256 rows of
+// 2*RK bytes) are copied global -> LDS with global_load_lds (no registers)
+// into a ring of slots, RING - 1 steps ahead of the MFMAs.
+//  * RK = 64 (256-row tiles when H % 64 == 0): whole 128-byte lines per
+//    row, 2 slots of 64 KiB; chunk c of row r at c ^ (r & 7).  All of a
+//    step's fragments are read before its MFMAs, and the reads of its second
+//    32-wide half are interleaved with the first half's MFMAs.
+//  * RK = 32: 4 slots of 32 KiB (256-row tiles) or 3 of 24 KiB (128-row
+//    tiles, two workgroups per CU); chunk c of row r at c ^ ((r >> 1) & 3).
+// Either way the eight lanes of one LDS read phase (rows r..r+7 of one chunk
+// column) hit eight different 16-byte bank groups.
+// 8 waves (two per SIMD) in a 2 x 4 grid of (BM/2) x 64 blocks: 128
+// accumulator registers per wave leave the register allocator room (a
+// 4-wave 128 x 128 layout fills all 256 AGPRs and the compiler shuffles
+// accumulators), and one wave's MFMAs cover the other's barrier and reads.
+// Per step and wave: (BM + 256) / 8 rows of copies, counted by vmcnt in
+// issue order; the ring keeps each wait count constant (the last steps
 // re-copy the last step into slots nothing reads any more).
 //
 // The copies are issued from inline asm, so the compiler does not see them:
@@ -346,19 +353,23 @@ __device__ __forceinline__ void wg_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <int BM>
+template <int BM, int RK>
 __global__ __launch_bounds__(512) void grouped_gemm_ring_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
     const int32_t* __restrict__ offsets, int E, int64_t T, int H, int F, int ntn,
     uint16_t* __restrict__ y) {
-  constexpr int BN = 256, RK = 32;            // K step (h) of one ring slot
-  constexpr int SLOT = (BM + BN) * 64;        // A then B, 64 bytes per row
-  // ring slots: 4 for 256-row tiles (128 KiB, one workgroup per CU); 3 for
-  // 128-row tiles (72 KiB: two workgroups per CU)
-  constexpr int RING = BM == 256 ? 4 : MOE_GEMM_RING128_SLOTS;
+  static_assert(RK == 32 || RK == 64, "K step of 32 or 64");
+  constexpr int BN = 256;
+  constexpr int RB = 2 * RK;                  // bytes per row and step
+  constexpr int CPR = RB / 16;                // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;               // rows per copy instruction
+  constexpr int SLOT = (BM + BN) * RB;        // A then B
+  constexpr int RING = RK == 64 ? 2 : (BM == 256 ? 4 : MOE_GEMM_RING128_SLOTS);
   constexpr int MT = BM / 32, NT = 4;         // 16 x 16 tiles per wave (rows, outputs)
-  constexpr int LA = BM / 128;                // A copies per wave and step (B: 2)
-  constexpr int OPS = LA + 2;
+  constexpr int KH = RK / 32;                 // 32-wide MFMA steps per K step
+  constexpr int LA = BM / 8 / RPI;            // copies per wave and step: A
+  constexpr int LB = BN / 8 / RPI;            //                           B
+  constexpr int OPS = LA + LB;
   __shared__ __align__(1024) char smem[RING * SLOT];
   __shared__ int s_e, s_rows;
   __shared__ int64_t s_m0;
@@ -378,37 +389,45 @@ __global__ __launch_bounds__(512) void grouped_gemm_ring_kernel(
   const int r = lane & 15;
   const int wm = wid & 1;
   const int wn = wid >> 1;
+  // slot chunk of global chunk c in row rr (rows of one copy instruction
+  // start at a multiple of RPI >= 8, so the swizzle depends on rr % RPI only)
+  auto sw = [](int c, int rr) { return RK == 64 ? c ^ (rr & 7) : c ^ ((rr >> 1) & 3); };
 
-  // copies: wave w fills A rows (BM/8)w + 16i .. +16 (i < LA) and B rows
-  // 32w + 16i .. +16 (i < 2); lane l -> row +l/4, slot chunk l%4, which holds
-  // global chunk (l%4) ^ ((row >> 1) & 3).  Offsets are 32-bit from the
+  // copies: wave w fills A rows (BM/8)w + RPI*i .. +RPI (i < LA) and B rows
+  // 32w + RPI*i .. +RPI (i < LB); lane l -> row +l/CPR, slot chunk l%CPR,
+  // which holds global chunk sw(l%CPR, row).  Offsets are 32-bit from the
   // tile's bases.
   const uint16_t* xa = x + m0 * H;
   const uint16_t* wb = w + ((int64_t)e * F) * H;
-  const int dr = lane >> 2;
-  const int dch = (lane & 3) ^ ((dr >> 1) & 3);
-  int aof[LA], bof[2];
+  const int dr = lane / CPR;
+  const int dch = sw(lane % CPR, dr);
+  int aof[LA], bof[LB];
 #pragma unroll
-  for (int i = 0; i < LA; ++i) aof[i] = min((BM / 8) * wid + 16 * i + dr, rows - 1) * H + 8 * dch;
+  for (int i = 0; i < LA; ++i) aof[i] = min((BM / 8) * wid + RPI * i + dr, rows - 1) * H + 8 * dch;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) bof[i] = min(n0 + 32 * wid + 16 * i + dr, F - 1) * H + 8 * dch;
+  for (int i = 0; i < LB; ++i) bof[i] = min(n0 + 32 * wid + RPI * i + dr, F - 1) * H + 8 * dch;
   const uint32_t base = lds_addr(smem);
   // (the LDS destination of a copy is wave-uniform: M0 takes a scalar)
-  const uint32_t abase = __builtin_amdgcn_readfirstlane(base + (uint32_t)((BM / 8) * wid * 64));
+  const uint32_t abase = __builtin_amdgcn_readfirstlane(base + (uint32_t)((BM / 8) * wid * RB));
   const uint32_t bbase =
-      __builtin_amdgcn_readfirstlane(base + (uint32_t)(BM * 64 + 32 * wid * 64));
+      __builtin_amdgcn_readfirstlane(base + (uint32_t)(BM * RB + 32 * wid * RB));
   auto copy_step = [&](int slot, int kt) {
     const uint32_t so = (uint32_t)(slot * SLOT);
 #pragma unroll
     for (int i = 0; i < LA; ++i)
-      lds_copy16(xa + aof[i] + kt * RK, abase + so + (uint32_t)(16 * i * 64));
+      lds_copy16(xa + aof[i] + kt * RK, abase + so + (uint32_t)(RPI * RB * i));
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      lds_copy16(wb + bof[i] + kt * RK, bbase + so + (uint32_t)(16 * i * 64));
+    for (int i = 0; i < LB; ++i)
+      lds_copy16(wb + bof[i] + kt * RK, bbase + so + (uint32_t)(RPI * RB * i));
   };
-  // fragment reads: A rows (BM/2)*wm + 16*t + r, B rows 64*wn + 16*t + r, chunk g
-  const int aoff = ((BM / 2) * wm + r) * 64 + ((g ^ ((r >> 1) & 3)) << 4);
-  const int boff = BM * 64 + (64 * wn + r) * 64 + ((g ^ ((r >> 1) & 3)) << 4);
+  // fragment reads of MFMA step h: A rows (BM/2)*wm + 16*t + r, B rows
+  // 64*wn + 16*t + r, global chunk 4h + g
+  int aoff[KH], boff[KH];
+#pragma unroll
+  for (int h = 0; h < KH; ++h) {
+    aoff[h] = ((BM / 2) * wm + r) * RB + (sw(4 * h + g, r) << 4);
+    boff[h] = BM * RB + (64 * wn + r) * RB + (sw(4 * h + g, r) << 4);
+  }
   f32x4_t acc[MT][NT];
 #pragma unroll
   for (int mi = 0; mi < MT; ++mi)
@@ -419,32 +438,50 @@ __global__ __launch_bounds__(512) void grouped_gemm_ring_kernel(
   const int last = nk - 1;
 #pragma unroll
   for (int j = 0; j < RING - 1; ++j) copy_step(j, min(j, last));
-  // step s: its copies landed (steps s+1, s+2 may still be in flight) ->
-  // barrier -> refill the slot of step s-1 with step s+3 -> read step s's
-  // fragments -> its MFMAs.  Two waves share each SIMD, so one's MFMAs cover
-  // the other's wait, barrier and reads.
   // A ragged tile whose rows all lie in the first half: the waves of the
   // second half copy and meet every barrier but skip their reads and MFMAs,
   // which leaves the matrix units of each SIMD to the other wave.
   const bool live =
       !MOE_GEMM_HALF_SKIP || __builtin_amdgcn_readfirstlane((int)(wm == 0 || rows > BM / 2)) != 0;
+  // step s: its copies landed (later steps may still be in flight) ->
+  // barrier -> refill the slot of step s-1 with step s+RING-1 -> read step
+  // s's fragments -> its MFMAs.  Two waves share each SIMD, so one's MFMAs
+  // cover the other's wait, barrier and reads.
   for (int s = 0; s < nk; ++s) {
     __builtin_amdgcn_s_waitcnt(vmcnt_imm((RING - 2) * OPS));
     wg_barrier();
     copy_step((s + RING - 1) % RING, min(s + RING - 1, last));
     if (!live) continue;
     const char* sl = smem + (s % RING) * SLOT;
-    u32x4 af[MT], bf[NT];
+    u32x4 af[KH][MT], bf[KH][NT];
 #pragma unroll
-    for (int t = 0; t < MT; ++t) af[t] = *reinterpret_cast<const u32x4*>(sl + aoff + t * 1024);
+    for (int h = 0; h < KH; ++h) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t) bf[t] = *reinterpret_cast<const u32x4*>(sl + boff + t * 1024);
+      for (int t = 0; t < MT; ++t)
+        af[h][t] = *reinterpret_cast<const u32x4*>(sl + aoff[h] + t * 16 * RB);
 #pragma unroll
-    for (int mi = 0; mi < MT; ++mi)
+      for (int t = 0; t < NT; ++t)
+        bf[h][t] = *reinterpret_cast<const u32x4*>(sl + boff[h] + t * 16 * RB);
+    }
 #pragma unroll
-      for (int ni = 0; ni < NT; ++ni)
-        acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(af[mi]), as_bf16x8(bf[ni]),
-                                                              acc[mi][ni], 0, 0, 0);
+    for (int h = 0; h < KH; ++h)
+#pragma unroll
+      for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NT; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              as_bf16x8(af[h][mi]), as_bf16x8(bf[h][ni]), acc[mi][ni], 0, 0, 0);
+    if constexpr (KH == 2) {
+      // the first half's reads, then each of the second half's reads after
+      // one of the first half's MFMAs, then the remaining MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x100, MT + NT, 0);  // LDS reads
+#pragma unroll
+      for (int t = 0; t < MT + NT; ++t) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // one LDS read
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * MT * NT - (MT + NT), 0);
+    }
   }
   // no copy may still be landing in LDS when the workgroup ends
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -496,6 +533,9 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(const float* __re
 #ifndef MOE_GEMM_RING
 #define MOE_GEMM_RING 1     // the 4-slot LDS ring kernel for 256 x 256 tiles (H % 32 == 0)
 #endif
+#ifndef MOE_GEMM_RK64
+#define MOE_GEMM_RK64 1     // 256-row ring tiles with 64-wide K steps when H % 64 == 0
+#endif
 #ifndef MOE_GEMM_RING_BM
 #define MOE_GEMM_RING_BM 256  // rows per tile of the ring kernel (256 or 128)
 #endif
@@ -520,14 +560,14 @@ hipError_t launch_gg(const void* x_perm, const void* weight, const int32_t* offs
   return hipGetLastError();
 }
 
-template <int RBM>
+template <int RBM, int RK>
 hipError_t launch_ring(const void* x_perm, const void* weight, const int32_t* offsets, int64_t T,
                        int H, int E, int F, void* y, hipStream_t s) {
   const int64_t mtiles = (T + RBM - 1) / RBM + E;
   const int ntn = (F + 255) / 256;
   const int64_t groups = (mtiles + kGroupM - 1) / kGroupM;
   const int64_t blocks = ((groups + 7) / 8) * 8 * kGroupM * ntn;
-  hipLaunchKernelGGL(grouped_gemm_ring_kernel<RBM>, dim3((unsigned)blocks), dim3(512), 0, s,
+  hipLaunchKernelGGL((grouped_gemm_ring_kernel<RBM, RK>), dim3((unsigned)blocks), dim3(512), 0, s,
                      reinterpret_cast<const uint16_t*>(x_perm),
                      reinterpret_cast<const uint16_t*>(weight), offsets, E, T, H, F, ntn,
                      reinterpret_cast<uint16_t*>(y));
@@ -544,11 +584,13 @@ hipError_t launch_grouped_linear(const void* x_perm, const void* weight, const i
     const int64_t big = ((T + 255) / 256) * ((F + 255) / 256);
     const bool ring = MOE_GEMM_RING && H % 32 == 0;
     if (MOE_GEMM_TILE == 256 && big >= 1024) {
-      if (ring) return launch_ring<MOE_GEMM_RING_BM>(x_perm, weight, offsets, T, H, E, F, y, s);
+      if (ring && MOE_GEMM_RK64 && H % 64 == 0)
+        return launch_ring<MOE_GEMM_RING_BM, 64>(x_perm, weight, offsets, T, H, E, F, y, s);
+      if (ring) return launch_ring<MOE_GEMM_RING_BM, 32>(x_perm, weight, offsets, T, H, E, F, y, s);
       return launch_gg<256, 256>(x_perm, weight, offsets, T, H, E, F, y, s);
     }
     if (ring && MOE_GEMM_SMALL_RING)
-      return launch_ring<128>(x_perm, weight, offsets, T, H, E, F, y, s);
+      return launch_ring<128, 32>(x_perm, weight, offsets, T, H, E, F, y, s);
     return launch_gg<128, 128>(x_perm, weight, offsets, T, H, E, F, y, s);
   } else {
     hipLaunchKernelGGL(grouped_gemm_f32_kernel, dim3((unsigned)((T * F + 255) / 256)), dim3(256),

@@ -97,11 +97,12 @@ def test_grouped_linear_headline_shape_sampled_rows():
     _check(got[rows], ref, x, W, off, rows, "bf16")
 
 
-@pytest.mark.parametrize("H,F", [(96, 1000), (32, 1024)])
+@pytest.mark.parametrize("H,F", [(96, 1000), (32, 1024), (64, 1000), (192, 1024)])
 def test_grouped_linear_large_tiles_ragged_sampled_rows(H, F):
-    # enough tiles for the 256 x 256 path (its 32-wide K ring: H = 96 takes
-    # three steps, H = 32 one), a ragged last n-tile (F = 1000) and experts
-    # of every size including empty ones; sampled rows against the oracle
+    # enough tiles for the 256 x 256 path, with 32-wide K steps (H = 96:
+    # three steps, H = 32: one) and 64-wide ones (H = 64: one, H = 192:
+    # three), a ragged last n-tile (F = 1000) and experts of every size
+    # including empty ones; sampled rows against the oracle
     N, E, K = 33000, 40, 2
     print(f"[grouped] large tiles H={H} F={F}", flush=True)
     ids = I.random_ids(H + F, N, E, K, skew=0.8)
