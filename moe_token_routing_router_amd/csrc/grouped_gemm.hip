@@ -27,8 +27,7 @@
 //    v_mfma_f32_16x16x32_bf16 tiles, fp32 accumulation, one rounding to bf16
 //    at the end.
 // When H % 32 != 0: 256 x 256 or 128 x 128 tiles of 4 waves with 64-wide K
-// steps double-buffered through registers (or, with MOE_GEMM_DMA, straight
-// into LDS -- measured equal), chunk c of row r at c ^ (r & 7).
+// steps double-buffered through registers, chunk c of row r at c ^ (r & 7).
 // fp32 inputs use a plain fp32 FMA kernel (one output per thread).
 #include "moe_internal.h"
 
@@ -52,22 +51,12 @@ constexpr int GBK = 64;   // K step (h)
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4 u) { return __builtin_bit_cast(bf16x8_t, u); }
 
-#ifndef MOE_GEMM_SWZ
-#define MOE_GEMM_SWZ 0
-#endif
 // LDS swizzle of a 128-byte tile row: 16-byte chunk c of row r is stored in
 // slot c ^ swz(r)
-__device__ __forceinline__ int swz(int r) { return MOE_GEMM_SWZ ? (r >> 1) & 7 : r & 7; }
+__device__ __forceinline__ int swz(int r) { return r & 7; }
 
 // s_waitcnt immediate for vmcnt(v) alone (expcnt and lgkmcnt left at their maxima)
 constexpr int vmcnt_imm(int v) { return (v & 15) | 0x70 | 0xF00 | (((v >> 4) & 3) << 14); }
-
-// 16 bytes per lane from global memory straight into LDS: lane l's bytes land
-// at lds_base + 16*l (lds_base must be the same in every lane of the wave).
-__device__ __forceinline__ void lds_dma16(const void* src, char* lds_base) {
-  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_base, 16, 0,
-                                   0);
-}
 
 // This workgroup's expert and rows: tiles of BM rows are numbered expert by
 // expert.  Offsets are clamped to [0, T] (inconsistent ones give wrong rows,
@@ -126,14 +115,7 @@ __device__ __forceinline__ bool tile_coords(int ntn, int* mt, int* nt) {
 
 // BM x BN output tile of one expert, 4 waves in a 2 x 2 grid, each wave a
 // (BM/2) x (BN/2) block of 16 x 16 MFMA tiles.
-// DMA: full K steps go global -> LDS directly (global_load_lds_dwordx4, no
-// register staging): load i of wave w fills rows 32*i + 8*w .. +8 of the
-// tile, lane l writing 16 bytes at (LDS base) + 16*l, i.e. row +l/8, slot
-// l%8; the lane loads global chunk (l%8) ^ (l/8) so slot s of row r holds
-// chunk s ^ (r%8), the same swizzle as the register path.  These writes are
-// not tracked by the compiler's LDS wait counts: each wave waits for its own
-// loads (vmcnt) before the workgroup barrier that precedes the reads.
-template <int BM, int BN, bool DMA>
+template <int BM, int BN>
 __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
     const int32_t* __restrict__ offsets, int E, int64_t T, int H, int F, int ntn,
@@ -178,24 +160,6 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(
   for (int i = 0; i < LA; ++i) aof[i] = min(rr0 + 32 * i, rows - 1) * H + 8 * lch;
 #pragma unroll
   for (int i = 0; i < LB; ++i) bof[i] = min(n0 + rr0 + 32 * i, F - 1) * H + 8 * lch;
-  int daof[DMA ? LA : 1], dbof[DMA ? LB : 1];
-  if constexpr (DMA) {
-    const int dr = lane >> 3;
-    const int dch = (lane & 7) ^ swz(8 * wid + dr);  // rows 32*i + 8*w + dr: swz ignores 32*i
-#pragma unroll
-    for (int i = 0; i < LA; ++i) daof[i] = min(32 * i + 8 * wid + dr, rows - 1) * H + 8 * dch;
-#pragma unroll
-    for (int i = 0; i < LB; ++i) dbof[i] = min(n0 + 32 * i + 8 * wid + dr, F - 1) * H + 8 * dch;
-  }
-  auto gload_dma = [&](int buf, int kt) {
-#pragma unroll
-    for (int i = 0; i < LA; ++i)
-      lds_dma16(xa + daof[i] + kt * GBK, sA[buf] + (32 * i + 8 * wid) * 128);
-#pragma unroll
-    for (int i = 0; i < LB; ++i)
-      lds_dma16(wb + dbof[i] + kt * GBK, sB[buf] + (32 * i + 8 * wid) * 128);
-  };
-  auto wait_vm = [] { __builtin_amdgcn_s_waitcnt(0x0F70); };  // vmcnt(0) only
   // fragment rows: A (BM/2)*wm + 16*t + r, B (BN/2)*wn + 16*t + r; chunk 4*kh + g
   auto frag_off = [&](int row, int kh) { return row * 128 + (((4 * kh + g) ^ swz(row)) << 4); };
 
@@ -261,22 +225,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(
   // last step.  The loads stay in flight under the MFMAs of the current step.
   const int nfull = H / GBK;
   u32x4 ra[LA], rb[LB];
-  if constexpr (DMA) {
-    if (nfull > 0) {
-      gload_dma(0, 0);
-      wait_vm();
-      __syncthreads();
-      for (int kt = 0; kt < nfull; ++kt) {
-        const int cur = kt & 1;
-        gload_dma(cur ^ 1, min(kt + 1, nfull - 1));
-        __builtin_amdgcn_sched_barrier(0);
-        compute(cur);
-        __builtin_amdgcn_sched_barrier(0);
-        wait_vm();
-        __syncthreads();
-      }
-    }
-  } else if (nfull > 0) {
+  if (nfull > 0) {
     gload(ra, rb, 0);
     lstore(0, ra, rb);
     __syncthreads();
@@ -539,9 +488,6 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(const float* __re
 #ifndef MOE_GEMM_RING_BM
 #define MOE_GEMM_RING_BM 256  // rows per tile of the ring kernel (256 or 128)
 #endif
-#ifndef MOE_GEMM_DMA
-#define MOE_GEMM_DMA 0      // 1: global -> LDS without register staging (measured equal)
-#endif
 
 template <int BM, int BN>
 hipError_t launch_gg(const void* x_perm, const void* weight, const int32_t* offsets, int64_t T,
@@ -552,7 +498,7 @@ hipError_t launch_gg(const void* x_perm, const void* weight, const int32_t* offs
   const int ntn = (F + BN - 1) / BN;
   const int64_t groups = (mtiles + kGroupM - 1) / kGroupM;
   const int64_t blocks = ((groups + 7) / 8) * 8 * kGroupM * ntn;
-  hipLaunchKernelGGL((grouped_gemm_bf16_kernel<BM, BN, MOE_GEMM_DMA != 0>),
+  hipLaunchKernelGGL((grouped_gemm_bf16_kernel<BM, BN>),
                      dim3((unsigned)blocks), dim3(256), 0, s,
                      reinterpret_cast<const uint16_t*>(x_perm),
                      reinterpret_cast<const uint16_t*>(weight), offsets, E, T, H, F, ntn,
