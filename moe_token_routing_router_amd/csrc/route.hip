@@ -45,6 +45,15 @@
 #ifndef MOE_ROUTE_DEPTH
 #define MOE_ROUTE_DEPTH 1    // steps of register prefetch (1 or 2) for E <= 64
 #endif
+#ifndef MOE_ROUTE_ESPLIT64
+#define MOE_ROUTE_ESPLIT64 0   // 33..64 experts: waves split the experts instead of H
+#endif
+#ifndef MOE_ROUTE_ESPLIT128
+#define MOE_ROUTE_ESPLIT128 1  // 65..128 experts: the same
+#endif
+#ifndef MOE_ROUTE_ESPLIT256
+#define MOE_ROUTE_ESPLIT256 1  // 129..256 experts: the same (from 8192 tokens on)
+#endif
 
 namespace moe {
 
@@ -438,6 +447,216 @@ __global__ __launch_bounds__(NW * 64) void route_bf16_kernel(
   }
 }
 
+// ------------------------------------------------- bf16 MFMA, experts split
+// The NW waves of a workgroup split the experts instead of H: wave w owns the
+// 16-expert tiles [w*NTW, (w+1)*NTW) over all of H, so its accumulators hold
+// complete logits (MT*NTW*4 registers) and no partial sums are exchanged.
+// Each 64-wide step's token tile is loaded once per workgroup (every wave a
+// share of its rows), double-buffered in LDS with the XOR swizzle above, and
+// read by every wave: one barrier per step.  The small register and LDS
+// footprint lets several workgroups share a CU, so one's selection overlaps
+// the others' streaming.  Same MFMA operand layout as route_bf16_kernel.
+template <int NT, int MT, int NW>
+__global__ __launch_bounds__(NW * 64) void route_bf16_esplit_kernel(
+    const uint16_t* __restrict__ x, const u32x4* __restrict__ gfrag,
+    const float* __restrict__ bias, int64_t N, int H, int E, int K, int32_t* __restrict__ ids,
+    float* __restrict__ topw, int32_t* __restrict__ counts, int32_t* __restrict__ lrank,
+    int32_t* __restrict__ bhist, int nb) {
+  constexpr int BM = 16 * MT;
+  constexpr int EP = 16 * NT;
+  constexpr int NTW = NT / NW;   // expert tiles per wave
+  constexpr int ROWP = EP + 4;
+  constexpr int TILE = BM * 128;  // one step's token tile
+  constexpr int ALD = BM / (8 * NW);  // token-tile loads per wave and step (8 rows each)
+  static_assert(NT % NW == 0 && BM % (8 * NW) == 0, "whole expert tiles and row blocks per wave");
+  static_assert(BM % (4 * NW) == 0, "epilogue maps 4 tokens per wave per pass");
+  constexpr int SMEM_A = 2 * TILE;
+  constexpr int SMEM_L = BM * ROWP * 4;
+  constexpr int SMEM = SMEM_A > SMEM_L ? SMEM_A : SMEM_L;
+  static_assert((BM * kMaxRouteK + (NW + 1) * kMaxExperts) * 4 <= SMEM,
+                "dispatch ranking reuses the tile / logit area");
+  __shared__ __align__(16) char smem[SMEM];
+  __shared__ int hist[EP];
+
+  const int tid = threadIdx.x;
+  const int wid = tid >> 6;
+  const int lane = tid & 63;
+  const int r = lane & 15;
+  const int g = lane >> 4;
+  const int64_t t0 = (int64_t)blockIdx.x * BM;
+  const int q0 = wid * NTW;
+
+  if (counts) {
+    for (int e = tid; e < EP; e += NW * 64) hist[e] = 0;
+  }
+
+  // token-tile loads: wave w, load j -> row 8*(w*ALD + j) + lane/8, chunk lane%8
+  const int lrow = lane >> 3;
+  const int lch = lane & 7;
+  const uint16_t* aptr[ALD];
+  int wofs[ALD];
+#pragma unroll
+  for (int j = 0; j < ALD; ++j) {
+    const int row = 8 * (wid * ALD + j) + lrow;
+    int64_t t = t0 + row;
+    if (t > N - 1) t = N - 1;  // tail rows recompute the last token; never stored
+    aptr[j] = x + t * H + 8 * lch;
+    wofs[j] = row * 128 + ((lch ^ (row & 7)) << 4);
+  }
+  int rofs[MT][2];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const int row = 16 * m + r;
+      rofs[m][hf] = row * 128 + (((2 * g + hf) ^ (row & 7)) << 4);
+    }
+
+  f32x4_t acc[MT][NTW];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int q = 0; q < NTW; ++q) acc[m][q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  struct Buf {
+    u32x4 a[ALD];
+    u32x4 b[NTW][2];
+  };
+  auto load_gate = [&](Buf& bf, int s) {
+    const u32x4* gb = gfrag + (size_t)s * NT * 128 + lane;
+#pragma unroll
+    for (int q = 0; q < NTW; ++q) {
+      bf.b[q][0] = gb[(2 * (q0 + q)) * 64];
+      bf.b[q][1] = gb[(2 * (q0 + q) + 1) * 64];
+    }
+  };
+  auto load = [&](Buf& bf, int s) {
+#pragma unroll
+    for (int j = 0; j < ALD; ++j) bf.a[j] = *reinterpret_cast<const u32x4*>(aptr[j] + s * 64);
+    load_gate(bf, s);
+  };
+  // the ragged last step (H % 64 != 0): chunks beyond H read column 0 of
+  // their row and are replaced by zeros (the packed gate is zero there)
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  auto load_masked = [&](Buf& bf, int s) {
+    const bool ok = s * 64 + 8 * lch < H;
+    const int o = ok ? s * 64 : -8 * lch;
+#pragma unroll
+    for (int j = 0; j < ALD; ++j) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(aptr[j] + o);
+      bf.a[j] = ok ? v : zero;
+    }
+    load_gate(bf, s);
+  };
+  // Step i uses LDS tile i % 2.  Its rows are written, then every wave's LDS
+  // operations are waited for and the workgroup meets at a bare barrier (the
+  // register prefetch of the next step stays in flight), then every wave reads
+  // its fragments.  The tile written at step i was last read at step i - 2,
+  // whose reads fed MFMAs issued before the barrier of step i - 1.
+  auto mma = [&](const Buf& bf, int buf) {
+    char* tile = smem + buf * TILE;
+#pragma unroll
+    for (int j = 0; j < ALD; ++j) *reinterpret_cast<u32x4*>(tile + wofs[j]) = bf.a[j];
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes are done
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    u32x4 af[MT][2];
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+        af[m][hf] = *reinterpret_cast<const u32x4*>(tile + rofs[m][hf]);
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int q = 0; q < NTW; ++q)
+          acc[m][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              as_bf16x8(af[m][hf]), as_bf16x8(bf.b[q][hf]), acc[m][q], 0, 0, 0);
+  };
+
+  const int nfull = H >> 6;
+  if (nfull > 0) {
+    const int last = nfull - 1;
+    Buf p, q;
+    load(p, 0);
+    int i = 0;
+    for (; i + 2 <= nfull; i += 2) {
+      load(q, i + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(p, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      load(p, min(i + 2, last));
+      __builtin_amdgcn_sched_barrier(0);
+      mma(q, 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (i < nfull) mma(p, 0);
+  }
+  if (H & 63) {
+    Buf t;
+    load_masked(t, nfull);
+    mma(t, nfull & 1);
+  }
+
+  // complete logits -> LDS (reusing the token tiles)
+  __syncthreads();
+  float(*lg)[ROWP] = reinterpret_cast<float(*)[ROWP]>(smem);
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int q = 0; q < NTW; ++q)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lg[16 * m + 4 * g + i][16 * (q0 + q) + r] = acc[m][q][i];
+  __syncthreads();
+
+  // each 16-lane group selects for the U tokens tl = wid*4 + g + u*NW*4
+  constexpr int U = BM / (4 * NW);
+  float v[U][NT];
+  int64_t tt[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int tl = wid * 4 + g + u * NW * 4;
+    tt[u] = t0 + tl;
+#pragma unroll
+    for (int q = 0; q < NT; ++q) {
+      const int e = 16 * q + r;
+      float sum = lg[tl][e];
+      if (bias) sum += bias[e < E ? e : 0];  // e >= E is never a candidate
+      v[u][q] = sum;
+    }
+  }
+  int pick[U];
+  select_topk_store<NT, U>(v, r, E, K, tt, N, ids, topw, (counts && !lrank) ? hist : nullptr,
+                           pick);
+
+  int* sids = reinterpret_cast<int*>(smem);
+  int* rhist = sids + BM * kMaxRouteK;
+  if (lrank) {
+    __syncthreads();  // every wave is done reading the logits
+    int* wcnt = rhist + kMaxExperts;
+    if (r < K) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int tl = wid * 4 + g + u * NW * 4;
+        sids[tl * K + r] = pick[u];
+      }
+    }
+    const int ntok = (int)min((int64_t)BM, N - t0);
+    block_stable_rank<NW>(sids, ntok * K, E, lrank + t0 * K, rhist, wcnt);
+    for (int e = tid; e < E; e += NW * 64) bhist[(int64_t)e * nb + blockIdx.x] = rhist[e];
+  }
+
+  if (counts) {
+    __syncthreads();
+    const int* h = lrank ? rhist : hist;
+    for (int e = tid; e < E; e += NW * 64)
+      if (h[e]) atomicAdd(&counts[e], h[e]);
+  }
+}
+
 // ---------------------------------------------------------------- fp32 VALU
 // 16 tokens per 256-thread workgroup: wave w, lane group g owns token
 // 16*blockIdx + 4w + g; lane r accumulates experts r, r+16, ... with one fp32
@@ -542,6 +761,18 @@ __global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
   if (i < n) p[i] = v;
 }
 
+// the experts-split router: NW waves of NT / NW expert tiles each
+template <int NT, int MT, int NW>
+hipError_t launch_bf16_esplit(const uint16_t* x, const uint16_t* wgt, const float* bias, int64_t N,
+                              int H, int E, int K, int32_t* ids, float* w, int32_t* counts,
+                              int32_t* lrank, int32_t* bhist, hipStream_t s) {
+  const int64_t blocks = (N + 16 * MT - 1) / (16 * MT);
+  hipLaunchKernelGGL((route_bf16_esplit_kernel<NT, MT, NW>), dim3((unsigned)blocks),
+                     dim3(NW * 64), 0, s, x, reinterpret_cast<const u32x4*>(wgt), bias, N, H, E,
+                     K, ids, w, counts, lrank, bhist, (int)blocks);
+  return hipGetLastError();
+}
+
 template <int NT, int MT, int NW = (NT <= 4 ? MOE_ROUTE_NW : NT == 8 ? MOE_ROUTE_NW128 : 4),
           int D = (NT <= 4 ? MOE_ROUTE_DEPTH : 1)>
 hipError_t launch_bf16_nt(const uint16_t* x, const uint16_t* wgt, const float* bias, int64_t N,
@@ -600,11 +831,17 @@ hipError_t launch_gate_transpose(const uint16_t* gate_w, int H, int E, uint16_t*
 // For 32 < E <= 128 the workgroup takes 64 tokens only when that still gives
 // every CU a workgroup (N >= 256 * 64); smaller N use 32-token workgroups,
 // twice as many, so more CUs stream x (the gate is read once per workgroup).
+// For 128 < E <= 256 the experts-split kernel takes 64 or 32 tokens the same
+// way from 8192 tokens on; below that the H-split kernel with 16 tokens per
+// workgroup is faster (more workgroups).
 constexpr int64_t kRouteSmallN = 256 * 64;
+constexpr int64_t kRoute256SplitN = 8192;
 static bool route_small(int EP, int64_t N) { return (EP == 64 || EP == 128) && N < kRouteSmallN; }
+static bool route_esplit256(int64_t N) { return MOE_ROUTE_ESPLIT256 && N >= kRoute256SplitN; }
 
 int route_tokens_per_block(int E, int64_t N) {
   const int EP = route_padded_experts(E);
+  if (EP == 256 && route_esplit256(N)) return N < kRouteSmallN ? 32 : 64;
   return route_small(EP, N) ? 32 : 16 * route_mt(EP);
 }
 
@@ -619,16 +856,37 @@ hipError_t launch_route_bf16(const uint16_t* x, const uint16_t* wgt, const float
       return launch_bf16_nt<2, route_mt(32)>(x, wgt, bias, N, H, E, K, ids, w, counts, lrank,
                                              bhist, s);
     case 64:
+      if (MOE_ROUTE_ESPLIT64) {
+        if (route_small(64, N))
+          return launch_bf16_esplit<4, 2, 4>(x, wgt, bias, N, H, E, K, ids, w, counts, lrank,
+                                             bhist, s);
+        return launch_bf16_esplit<4, route_mt(64), 4>(x, wgt, bias, N, H, E, K, ids, w, counts,
+                                                      lrank, bhist, s);
+      }
       if (route_small(64, N))
         return launch_bf16_nt<4, 2>(x, wgt, bias, N, H, E, K, ids, w, counts, lrank, bhist, s);
       return launch_bf16_nt<4, route_mt(64)>(x, wgt, bias, N, H, E, K, ids, w, counts, lrank,
                                              bhist, s);
     case 128:
+      if (MOE_ROUTE_ESPLIT128) {
+        if (route_small(128, N))
+          return launch_bf16_esplit<8, 2, 4>(x, wgt, bias, N, H, E, K, ids, w, counts, lrank,
+                                             bhist, s);
+        return launch_bf16_esplit<8, route_mt(128), 4>(x, wgt, bias, N, H, E, K, ids, w, counts,
+                                                       lrank, bhist, s);
+      }
       if (route_small(128, N))
         return launch_bf16_nt<8, 2>(x, wgt, bias, N, H, E, K, ids, w, counts, lrank, bhist, s);
       return launch_bf16_nt<8, route_mt(128)>(x, wgt, bias, N, H, E, K, ids, w, counts, lrank,
                                               bhist, s);
     case 256:
+      if (route_esplit256(N)) {
+        if (N < kRouteSmallN)
+          return launch_bf16_esplit<16, 2, 4>(x, wgt, bias, N, H, E, K, ids, w, counts, lrank,
+                                              bhist, s);
+        return launch_bf16_esplit<16, 4, 4>(x, wgt, bias, N, H, E, K, ids, w, counts, lrank,
+                                            bhist, s);
+      }
       return launch_bf16_nt<16, route_mt(256), 4>(x, wgt, bias, N, H, E, K, ids, w, counts,
                                                   lrank, bhist, s);
   }
