@@ -15,8 +15,11 @@
 //    reads it from L2 with one 16-byte load per lane and fragment;
 //  * token rows are read from HBM exactly once with coalesced 16-byte loads
 //    and pass through the wave's own XOR-swizzled LDS tile into MFMA layout;
-//  * a workgroup owns BM = 16*MT tokens; its NW waves split H and their fp32
-//    partial logits are summed through LDS in a fixed order (deterministic);
+//  * a workgroup owns BM = 16*MT tokens; up to 64 experts its NW waves split H
+//    and their fp32 partial logits are summed through LDS in a fixed order
+//    (deterministic); for 65..128 experts, and 129..256 from 8192 tokens on,
+//    the waves split the experts instead, share each step's token tile
+//    through LDS and keep complete logits (route_bf16_esplit_kernel);
 //  * softmax/top-K/renorm happen in registers: a token's logits live in one
 //    16-lane row of the wave (lane r holds experts r, r+16, ...), and each of
 //    the K rounds is a 16-lane arg-max butterfly.
@@ -45,11 +48,8 @@
 #ifndef MOE_ROUTE_DEPTH
 #define MOE_ROUTE_DEPTH 1    // steps of register prefetch (1 or 2) for E <= 64
 #endif
-#ifndef MOE_ROUTE_ESPLIT64
-#define MOE_ROUTE_ESPLIT64 0   // 33..64 experts: waves split the experts instead of H
-#endif
 #ifndef MOE_ROUTE_ESPLIT128
-#define MOE_ROUTE_ESPLIT128 1  // 65..128 experts: the same
+#define MOE_ROUTE_ESPLIT128 1  // 65..128 experts: waves split the experts instead of H
 #endif
 #ifndef MOE_ROUTE_ESPLIT256
 #define MOE_ROUTE_ESPLIT256 1  // 129..256 experts: the same (from 8192 tokens on)
@@ -856,13 +856,6 @@ hipError_t launch_route_bf16(const uint16_t* x, const uint16_t* wgt, const float
       return launch_bf16_nt<2, route_mt(32)>(x, wgt, bias, N, H, E, K, ids, w, counts, lrank,
                                              bhist, s);
     case 64:
-      if (MOE_ROUTE_ESPLIT64) {
-        if (route_small(64, N))
-          return launch_bf16_esplit<4, 2, 4>(x, wgt, bias, N, H, E, K, ids, w, counts, lrank,
-                                             bhist, s);
-        return launch_bf16_esplit<4, route_mt(64), 4>(x, wgt, bias, N, H, E, K, ids, w, counts,
-                                                      lrank, bhist, s);
-      }
       if (route_small(64, N))
         return launch_bf16_nt<4, 2>(x, wgt, bias, N, H, E, K, ids, w, counts, lrank, bhist, s);
       return launch_bf16_nt<4, route_mt(64)>(x, wgt, bias, N, H, E, K, ids, w, counts, lrank,
