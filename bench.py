@@ -470,8 +470,10 @@ def main():
 
     # Context: plain PyTorch kernels with the stages' read:write mixes on
     # buffers of the same size (rotating three sets, like the path): a 1:1
-    # copy, dispatch's 1:2 fan-out (index_select repeating each row twice) and
-    # combine's 2:1 (the sum of row pairs).  Algorithmic GB/s.
+    # copy, dispatch's 1:2 fan-out (index_select repeating each row twice),
+    # combine's 2:1 as the sum of row pairs and, for K >= 2, as an elementwise
+    # add of two contiguous halves of y (a plain streaming kernel).
+    # Algorithmic GB/s.
     def plain_gbs(fn, nbytes, n=20):
         for i in range(3):
             fn(i)
@@ -489,6 +491,10 @@ def main():
                                 out=sets[i % N_SETS]["out"]), T * H * b + N * H * b),
         "note": "plain PyTorch kernels, same sizes, read:write mixes of copy, dispatch, combine",
     }
+    if K >= 2:
+        ceilings["add_2to1"] = plain_gbs(
+            lambda i: torch.add(sets[i % N_SETS]["y"][:N], sets[i % N_SETS]["y"][N:2 * N],
+                                out=sets[i % N_SETS]["out"]), 3 * N * H * b)
     # leave the outputs of the path consistent for the check below
     for i in range(N_SETS):
         step(i)
