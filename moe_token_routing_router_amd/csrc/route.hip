@@ -48,9 +48,6 @@
 #ifndef MOE_ROUTE_DEPTH
 #define MOE_ROUTE_DEPTH 1    // steps of register prefetch (1 or 2) for E <= 64
 #endif
-#ifndef MOE_GATE_PACK8
-#define MOE_GATE_PACK8 1       // E % 8 == 0: the gate packed 8 x 8 blocks per thread
-#endif
 #ifndef MOE_ROUTE_ESPLIT128
 #define MOE_ROUTE_ESPLIT128 1  // 65..128 experts: waves split the experts instead of H
 #endif
@@ -759,44 +756,6 @@ __global__ __launch_bounds__(64) void gate_pack_kernel(const uint16_t* __restric
   gfrag[((int64_t)(s * NTL + (e >> 4)) * 2 + hf) * 64 + 16 * g + (e & 15)] = o;
 }
 
-// The same layout when E % 8 == 0: one thread per 8 rows x 8 experts block
-// (eight 16-byte loads, an 8 x 8 transpose of 16-bit values in registers,
-// eight 16-byte stores that land side by side).
-__global__ __launch_bounds__(64) void gate_pack8_kernel(const uint16_t* __restrict__ gate_w, int H,
-                                                        int E, int EP, int HP,
-                                                        u32x4* __restrict__ gfrag,
-                                                        int32_t* __restrict__ counts) {
-  const int64_t idx = (int64_t)blockIdx.x * 64 + threadIdx.x;
-  if (counts && idx < E) counts[idx] = 0;
-  const int ng = EP / 8;  // 8-expert groups, including the zero padding up to EP
-  if (idx >= (int64_t)(HP / 8) * ng) return;
-  const int hb = (int)(idx / ng);
-  const int e0 = 8 * (int)(idx - (int64_t)hb * ng);
-  const int h0 = hb * 8;
-  const u32x4 zero = {0u, 0u, 0u, 0u};
-  u32x4 in[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-    in[i] = (e0 < E && h0 + i < H)
-                ? *reinterpret_cast<const u32x4*>(gate_w + (int64_t)(h0 + i) * E + e0)
-                : zero;
-  const int s = h0 >> 6;
-  const int g = (h0 >> 4) & 3;
-  const int hf = (h0 >> 3) & 1;
-  const int NTL = EP / 16;
-  u32x4* dst = gfrag + ((int64_t)(s * NTL + (e0 >> 4)) * 2 + hf) * 64 + 16 * g + (e0 & 15);
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    // expert e0 + j: its value in rows h0 .. h0+7, two per word (row 2p low)
-    const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
-    u32x4 o;
-#pragma unroll
-    for (int p = 0; p < 4; ++p)
-      o[p] = __builtin_amdgcn_perm(in[2 * p + 1][j >> 1], in[2 * p][j >> 1], sel);
-    dst[j] = o;
-  }
-}
-
 __global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = v;
@@ -862,13 +821,6 @@ hipError_t launch_gate_transpose(const uint16_t* gate_w, int H, int E, uint16_t*
                                  int32_t* counts, hipStream_t s) {
   const int EP = route_padded_experts(E);
   const int HP = route_gate_rows(H);
-  if (MOE_GATE_PACK8 && E % 8 == 0) {
-    int64_t threads = (int64_t)(HP / 8) * (EP / 8);
-    if (threads < E) threads = E;
-    hipLaunchKernelGGL(gate_pack8_kernel, dim3((unsigned)((threads + 63) / 64)), dim3(64), 0, s,
-                       gate_w, H, E, EP, HP, reinterpret_cast<u32x4*>(wgt), counts);
-    return hipGetLastError();
-  }
   int64_t threads = (int64_t)(HP / 8) * EP;
   if (threads < E) threads = E;
   hipLaunchKernelGGL(gate_pack_kernel, dim3((unsigned)((threads + 63) / 64)), dim3(64), 0, s,
