@@ -75,7 +75,7 @@ moe_status_t moe_route(const void* x, const void* gate_w, const float* bias, int
   }
   return from_hip(moe::launch_route_f32(reinterpret_cast<const float*>(x),
                                         reinterpret_cast<const float*>(gate_w), bias, N, H, E, K,
-                                        topk_ids, topk_w, counts, s));
+                                        topk_ids, topk_w, counts, nullptr, nullptr, s));
 }
 
 namespace {
@@ -156,7 +156,7 @@ size_t moe_route_dispatch_workspace_size(int64_t N, int32_t H, int32_t E, int32_
                                          moe_dtype_t dtype) {
   if (N < 0 || H <= 0 || E <= 0 || E > moe::kMaxExperts || K < 1 || !valid_dtype(dtype)) return 0;
   const int bt =
-      dtype == MOE_BF16 ? moe::route_tokens_per_block(E, N) : moe::dispatch_count_tokens(K);
+      dtype == MOE_BF16 ? moe::route_tokens_per_block(E, N) : moe::kRouteF32Tokens;
   return moe_route_workspace_size(H, E, dtype) + dispatch_scratch_bytes(N, E, K, bt);
 }
 
@@ -181,7 +181,7 @@ moe_status_t moe_route_dispatch(const void* x, const void* gate_w, const float* 
     return MOE_ERR_WORKSPACE_TOO_SMALL;
   const size_t rws = moe_route_workspace_size(H, E, dtype);
   const int bt =
-      dtype == MOE_BF16 ? moe::route_tokens_per_block(E, N) : moe::dispatch_count_tokens(K);
+      dtype == MOE_BF16 ? moe::route_tokens_per_block(E, N) : moe::kRouteF32Tokens;
   char* base = reinterpret_cast<char*>(workspace);
   int32_t* bhist = reinterpret_cast<int32_t*>(base + rws);
   int32_t* lrank = reinterpret_cast<int32_t*>(
@@ -204,11 +204,10 @@ moe_status_t moe_route_dispatch(const void* x, const void* gate_w, const float* 
           topk_ids, x, N, (int64_t)H * elem_bytes(dtype), E, K, bt, counts, offsets, perm, inv,
           x_perm, lrank, bhist, s));
   } else {
+    // the fp32 router ranks its own 16-token blocks: no count kernel
     e = moe::launch_route_f32(reinterpret_cast<const float*>(x),
                               reinterpret_cast<const float*>(gate_w), bias, N, H, E, K, topk_ids,
-                              topk_w, nullptr, s);
-    if (e != hipSuccess) return MOE_ERR_HIP;
-    e = moe::launch_dispatch_count(topk_ids, N, E, K, lrank, bhist, s);
+                              topk_w, nullptr, lrank, bhist, s);
   }
   if (e != hipSuccess) return MOE_ERR_HIP;
   return from_hip(moe::launch_dispatch_finish(topk_ids, x, N, (int64_t)H * elem_bytes(dtype), E, K,

@@ -178,9 +178,12 @@ hipError_t launch_gate_transpose(const uint16_t* gate_w, int H, int E, uint16_t*
 hipError_t launch_route_bf16(const uint16_t* x, const uint16_t* wgt, const float* bias,
                              int64_t N, int H, int E, int K, int32_t* ids, float* w,
                              int32_t* counts, int32_t* lrank, int32_t* bhist, hipStream_t s);
+// The fp32 router works on blocks of kRouteF32Tokens tokens; with lrank it
+// ranks its own picks per block like the bf16 router.
+constexpr int kRouteF32Tokens = 16;
 hipError_t launch_route_f32(const float* x, const float* gate_w, const float* bias, int64_t N,
                             int H, int E, int K, int32_t* ids, float* w, int32_t* counts,
-                            hipStream_t s);
+                            int32_t* lrank, int32_t* bhist, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
 
 // Dispatch.  lrank [N*K] and bhist [E][dispatch_num_blocks(N, bt)] live in

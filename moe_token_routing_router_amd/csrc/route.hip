@@ -48,6 +48,9 @@
 #ifndef MOE_ROUTE_DEPTH
 #define MOE_ROUTE_DEPTH 1    // steps of register prefetch (1 or 2) for E <= 64
 #endif
+#ifndef MOE_ROUTE_F32_UNROLL
+#define MOE_ROUTE_F32_UNROLL 8  // fp32 router: h steps of 4 unrolled together
+#endif
 #ifndef MOE_ROUTE_ESPLIT128
 #define MOE_ROUTE_ESPLIT128 1  // 65..128 experts: waves split the experts instead of H
 #endif
@@ -658,9 +661,10 @@ __global__ __launch_bounds__(NW * 64) void route_bf16_esplit_kernel(
 }
 
 // ---------------------------------------------------------------- fp32 VALU
-// 16 tokens per 256-thread workgroup: wave w, lane group g owns token
-// 16*blockIdx + 4w + g; lane r accumulates experts r, r+16, ... with one fp32
-// FMA chain per expert in ascending h.
+// kRouteF32Tokens = 16 tokens per 256-thread workgroup: wave w, lane group g
+// owns token 16*blockIdx + 4w + g; lane r accumulates experts r, r+16, ...
+// with one fp32 FMA chain per expert in ascending h.  With lrank (the fused
+// call) the workgroup ranks its picks for the dispatch like the bf16 kernels.
 template <int NT>
 __global__ __launch_bounds__(256) void route_f32_kernel(const float* __restrict__ x,
                                                         const float* __restrict__ gate_w,
@@ -668,9 +672,15 @@ __global__ __launch_bounds__(256) void route_f32_kernel(const float* __restrict_
                                                         int H, int E, int K,
                                                         int32_t* __restrict__ ids,
                                                         float* __restrict__ topw,
-                                                        int32_t* __restrict__ counts) {
+                                                        int32_t* __restrict__ counts,
+                                                        int32_t* __restrict__ lrank,
+                                                        int32_t* __restrict__ bhist, int nb) {
+  static_assert(kRouteF32Tokens == 16, "four tokens per wave, four waves");
   constexpr int EP = 16 * NT;
   __shared__ int hist[EP];
+  __shared__ int sids[kRouteF32Tokens * kMaxRouteK];
+  __shared__ int rhist[kMaxExperts];
+  __shared__ int wcnt[4 * kMaxExperts];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int r = lane & 15;
@@ -685,6 +695,9 @@ __global__ __launch_bounds__(256) void route_f32_kernel(const float* __restrict_
   float acc[NT];
 #pragma unroll
   for (int q = 0; q < NT; ++q) acc[q] = 0.f;
+  // (unrolled so that several steps' loads are in flight; the FMA order per
+  // expert stays h ascending)
+#pragma unroll MOE_ROUTE_F32_UNROLL
   for (int h = 0; h < H; h += 4) {
     const float4 xv = *reinterpret_cast<const float4*>(xr + h);
     const float* wr = gate_w + (int64_t)h * E;
@@ -711,11 +724,21 @@ __global__ __launch_bounds__(256) void route_f32_kernel(const float* __restrict_
   for (int q = 0; q < NT; ++q) v1[0][q] = acc[q];
   const int64_t t1[1] = {t};
   int pick[1];
-  select_topk_store<NT, 1>(v1, r, E, K, t1, N, ids, topw, counts ? hist : nullptr, pick);
+  select_topk_store<NT, 1>(v1, r, E, K, t1, N, ids, topw, (counts && !lrank) ? hist : nullptr,
+                           pick);
+  if (lrank) {
+    const int64_t t0 = (int64_t)blockIdx.x * kRouteF32Tokens;
+    if (r < K) sids[((tid >> 6) * 4 + g) * K + r] = pick[0];
+    const int ntok = (int)min((int64_t)kRouteF32Tokens, N - t0);
+    // (the ranking's first barrier publishes sids)
+    block_stable_rank<4>(sids, ntok * K, E, lrank + t0 * K, rhist, wcnt);
+    for (int e = tid; e < E; e += 256) bhist[(int64_t)e * nb + blockIdx.x] = rhist[e];
+  }
   if (counts) {
     __syncthreads();
+    const int* h = lrank ? rhist : hist;
     for (int e = tid; e < E; e += 256)
-      if (hist[e]) atomicAdd(&counts[e], hist[e]);
+      if (h[e]) atomicAdd(&counts[e], h[e]);
   }
 }
 
@@ -793,10 +816,11 @@ constexpr int route_mt(int EP) {
 
 template <int NT>
 hipError_t launch_f32_nt(const float* x, const float* gw, const float* bias, int64_t N, int H,
-                         int E, int K, int32_t* ids, float* w, int32_t* counts, hipStream_t s) {
-  const int64_t blocks = (N + 15) / 16;
+                         int E, int K, int32_t* ids, float* w, int32_t* counts, int32_t* lrank,
+                         int32_t* bhist, hipStream_t s) {
+  const int64_t blocks = (N + kRouteF32Tokens - 1) / kRouteF32Tokens;
   hipLaunchKernelGGL((route_f32_kernel<NT>), dim3((unsigned)blocks), dim3(256), 0, s, x, gw,
-                     bias, N, H, E, K, ids, w, counts);
+                     bias, N, H, E, K, ids, w, counts, lrank, bhist, (int)blocks);
   return hipGetLastError();
 }
 
@@ -888,13 +912,13 @@ hipError_t launch_route_bf16(const uint16_t* x, const uint16_t* wgt, const float
 
 hipError_t launch_route_f32(const float* x, const float* gate_w, const float* bias, int64_t N,
                             int H, int E, int K, int32_t* ids, float* w, int32_t* counts,
-                            hipStream_t s) {
+                            int32_t* lrank, int32_t* bhist, hipStream_t s) {
   switch (route_padded_experts(E)) {
-    case 16: return launch_f32_nt<1>(x, gate_w, bias, N, H, E, K, ids, w, counts, s);
-    case 32: return launch_f32_nt<2>(x, gate_w, bias, N, H, E, K, ids, w, counts, s);
-    case 64: return launch_f32_nt<4>(x, gate_w, bias, N, H, E, K, ids, w, counts, s);
-    case 128: return launch_f32_nt<8>(x, gate_w, bias, N, H, E, K, ids, w, counts, s);
-    case 256: return launch_f32_nt<16>(x, gate_w, bias, N, H, E, K, ids, w, counts, s);
+    case 16: return launch_f32_nt<1>(x, gate_w, bias, N, H, E, K, ids, w, counts, lrank, bhist, s);
+    case 32: return launch_f32_nt<2>(x, gate_w, bias, N, H, E, K, ids, w, counts, lrank, bhist, s);
+    case 64: return launch_f32_nt<4>(x, gate_w, bias, N, H, E, K, ids, w, counts, lrank, bhist, s);
+    case 128: return launch_f32_nt<8>(x, gate_w, bias, N, H, E, K, ids, w, counts, lrank, bhist, s);
+    case 256: return launch_f32_nt<16>(x, gate_w, bias, N, H, E, K, ids, w, counts, lrank, bhist, s);
   }
   return hipErrorInvalidValue;
 }
