@@ -7,7 +7,7 @@
 // bincount over per-block private histograms, a reduction + prefix sum, and a
 // counting-sort scatter producing the expand index -- replacing a chain of
 // argsort / nonzero / searchsorted / repeat_interleave launches with fixed-size
-// outputs.  This build keeps that three-kernel shape, on CDNA4:
+// outputs.  The kernels here keep that three-kernel shape, on CDNA4:
 //
 //  count   (one workgroup per block of bt tokens)  stable rank of every slot
 //          among the equal ids of its block (wave ballots on the id bits, then
@@ -24,9 +24,11 @@
 // The fused router (route.hip) produces lrank and bhist in its own epilogue,
 // so moe_route_dispatch skips the count kernel; for K <= 2 the router also
 // adds its block histograms into counts and the scatter sums the earlier
-// blocks' counts itself, so the scan kernel is skipped too.  Right after the
-// router, the scatter takes its tokens in the router's XCD order (see
-// scatter_token) so part of its read of x hits L2.
+// blocks' counts itself, so the scan kernel is skipped too.  With a bhist of
+// at most kSumAllMaxInts entries (small N and E) every scatter workgroup also
+// sums whole histogram rows for the totals, so no scan kernel runs either.
+// Right after the router, the scatter takes its tokens in the router's XCD
+// order (see scatter_token) so part of its read of x hits L2.
 //
 // Atomics only ever produce counts; every position comes from a deterministic
 // rank, so the output is bitwise reproducible and equal to a stable argsort.
@@ -58,6 +60,10 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kScatterTokens = MOE_SCATTER_TOKENS;
+#ifndef MOE_SCATTER_SUMALL_INTS
+#define MOE_SCATTER_SUMALL_INTS 1024  // bhist up to this size: the scatter sums it itself
+#endif
+constexpr int kSumAllMaxInts = MOE_SCATTER_SUMALL_INTS;
 
 __device__ __forceinline__ u32x4 ld_row(const u32x4* p) {
 #if MOE_SCATTER_NT_LOAD
@@ -136,17 +142,21 @@ __device__ __forceinline__ int64_t scatter_token(int64_t g, int64_t N, int xbt) 
 // One workgroup per kScatterTokens tokens.  The rows' first loads are issued
 // before the index work (they do not depend on it), so the E-wide offset
 // scan and the index arithmetic overlap them.
-// PREFIX: bhist holds the raw per-block counts (no scan kernel ran) and
-// counts their totals; each workgroup sums the blocks before its own for the
-// experts of its slots (at most nb entries of one bhist row per slot).
-template <bool PREFIX>
+// MODE 0: bhist holds the scanned block bases and counts the totals (the
+// scan kernel ran).  MODE 1: bhist holds the raw per-block counts and counts
+// their totals (the fused router added them); each workgroup sums the blocks
+// before its own for the experts of its slots (at most nb entries of one
+// bhist row per slot).  MODE 2: as MODE 1, and every workgroup also sums
+// whole bhist rows for the totals (small bhist only), workgroup 0 storing
+// them to counts.
+template <int MODE>
 __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
-    const int32_t* __restrict__ ids, const int32_t* __restrict__ counts,
+    const int32_t* __restrict__ ids, int32_t* __restrict__ counts,
     const int32_t* __restrict__ bhist, const int32_t* __restrict__ lrank, int64_t N, int K,
     int E, int nb, int bt, int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
     int32_t* __restrict__ inv, const u32x4* __restrict__ x, u32x4* __restrict__ x_perm,
     int row_vecs, int64_t dlim, int xbt) {
-  extern __shared__ int dst[];  // [kScatterTokens*K], then (PREFIX) red[4][kScatterTokens*K]
+  extern __shared__ int dst[];  // [kScatterTokens*K], then (MODE >= 1) red[4][kScatterTokens*K]
   __shared__ int off[kMaxExperts];
   __shared__ int scan_lds[4];
   const int tid = threadIdx.x;
@@ -168,7 +178,7 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
 
   const int S = ntok * K;
   const int64_t s0 = n0 * K;
-  if constexpr (PREFIX) {
+  if constexpr (MODE >= 1) {
     // per slot: the counts of its expert in the blocks before its own (the
     // barriers of the offset scan below publish red)
     for (int j = 0; j < S; ++j) {
@@ -185,7 +195,17 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
 
   // offsets = exclusive scan of counts (E <= 256: one expert per thread)
   {
-    const int c = tid < E ? counts[tid] : 0;
+    int c = 0;
+    if constexpr (MODE == 2) {
+      if (tid < E) {
+        const int32_t* row = bhist + (int64_t)tid * nb;
+#pragma unroll 8
+        for (int bb = 0; bb < nb; ++bb) c += row[bb];
+        if (blockIdx.x == 0) counts[tid] = c;
+      }
+    } else {
+      c = tid < E ? counts[tid] : 0;
+    }
     int tot;
     const int ex = block_exclusive_scan_256(c, scan_lds, &tot);
     if (tid < E) off[tid] = ex;
@@ -202,8 +222,9 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
     int d = -1;
     if ((unsigned)e < (unsigned)E) {
       const int64_t b = (slot / K) / bt;
-      const int64_t base = PREFIX ? (int64_t)((red[j] + red[S + j]) + red[2 * S + j]) + red[3 * S + j]
-                                  : (int64_t)bhist[(int64_t)e * nb + b];
+      const int64_t base = MODE >= 1
+                               ? (int64_t)((red[j] + red[S + j]) + red[2 * S + j]) + red[3 * S + j]
+                               : (int64_t)bhist[(int64_t)e * nb + b];
       const int64_t dd = (int64_t)off[e] + base + lrank[slot];
       if (dd >= 0 && dd < dlim) {  // always true for consistent inputs
         d = (int)dd;
@@ -278,8 +299,8 @@ hipError_t launch_dispatch_scatter_prefix(const int32_t* ids, const void* x, int
   const int nb = (int)dispatch_num_blocks(N, bt);
   const int64_t blocks = (N + kScatterTokens - 1) / kScatterTokens;
   const size_t dyn = sizeof(int) * 5 * (size_t)kScatterTokens * K;
-  hipLaunchKernelGGL(dispatch_scatter_kernel<true>, dim3((unsigned)blocks), dim3(256), dyn, s, ids,
-                     counts, bhist, lrank, N, K, E, nb, bt, offsets, perm, inv,
+  hipLaunchKernelGGL(dispatch_scatter_kernel<1>, dim3((unsigned)blocks), dim3(256), dyn, s, ids,
+                     const_cast<int32_t*>(counts), bhist, lrank, N, K, E, nb, bt, offsets, perm, inv,
                      reinterpret_cast<const u32x4*>(x), reinterpret_cast<u32x4*>(x_perm),
                      (int)(row_bytes / 16), N * K, scatter_xbt(N, bt));
   return hipGetLastError();
@@ -291,13 +312,23 @@ hipError_t launch_dispatch_finish(const int32_t* ids, const void* x, int64_t N, 
                                   const int32_t* lrank, int32_t* bhist, int64_t dlim,
                                   hipStream_t s, int router_bt) {
   const int nb = (int)dispatch_num_blocks(N, bt);
+  const int64_t blocks = (N + kScatterTokens - 1) / kScatterTokens;
+  if ((int64_t)nb * E <= kSumAllMaxInts) {
+    // a small bhist: every scatter workgroup sums it itself (no scan kernel;
+    // measured slower from about 2048 entries on)
+    const size_t dyn = sizeof(int) * 5 * (size_t)kScatterTokens * K;
+    hipLaunchKernelGGL(dispatch_scatter_kernel<2>, dim3((unsigned)blocks), dim3(256), dyn, s, ids,
+                       counts, bhist, lrank, N, K, E, nb, bt, offsets, perm, inv,
+                       reinterpret_cast<const u32x4*>(x), reinterpret_cast<u32x4*>(x_perm),
+                       (int)(row_bytes / 16), dlim, scatter_xbt(N, router_bt));
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(dispatch_scan_kernel, dim3(E), dim3(256), 0, s, bhist, nb, counts, E,
                      (int32_t*)nullptr);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const int64_t blocks = (N + kScatterTokens - 1) / kScatterTokens;
   const size_t dyn = sizeof(int) * (size_t)kScatterTokens * K;
-  hipLaunchKernelGGL(dispatch_scatter_kernel<false>, dim3((unsigned)blocks), dim3(256), dyn, s, ids,
+  hipLaunchKernelGGL(dispatch_scatter_kernel<0>, dim3((unsigned)blocks), dim3(256), dyn, s, ids,
                      counts, bhist, lrank, N, K, E, nb, bt, offsets, perm, inv,
                      reinterpret_cast<const u32x4*>(x), reinterpret_cast<u32x4*>(x_perm),
                      (int)(row_bytes / 16), dlim, scatter_xbt(N, router_bt));
