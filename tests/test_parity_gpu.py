@@ -314,25 +314,27 @@ def test_route_dispatch_block_counts(N, K, bias):
 # to 64 experts, and 129..256 experts below 8192 tokens); ragged token tails
 # and H not a multiple of 64.  Both the router alone and the fused call.
 ROUTER_PATHS = [
-    # (N, H, E, K, bias)
-    (8192 + 37, 200, 256, 8, True),     # experts split, 32-token workgroups
-    (16384 + 5, 136, 200, 16, False),   # experts split, 64-token workgroups, E padded to 256
-    (8191, 72, 256, 4, True),           # just below the split: the H-split kernel
-    (16384 + 40, 128, 100, 6, True),    # 65..128 experts, 64-token workgroups
-    (3000, 96, 128, 8, False),          # 65..128 experts, 32-token workgroups
+    # (N, H, E, K, bias, dtype)
+    (8192 + 37, 200, 256, 8, True, "bf16"),     # experts split, 32-token workgroups
+    (16384 + 5, 136, 200, 16, False, "bf16"),   # experts split, 64-token workgroups, E padded
+    (8191, 72, 256, 4, True, "bf16"),           # just below the split: the H-split kernel
+    (16384 + 40, 128, 100, 6, True, "bf16"),    # 65..128 experts, 64-token workgroups
+    (3000, 96, 128, 8, False, "bf16"),          # 65..128 experts, 32-token workgroups
+    (700, 72, 256, 16, True, "f32"),            # fp32 router ranking 16-token blocks, E, K at limits
+    (3001, 40, 128, 8, False, "f32"),           # fp32, block histogram above the scatter's own sum
 ]
 
 
-@pytest.mark.parametrize("N,H,E,K,bias", ROUTER_PATHS)
-def test_router_kernel_paths(N, H, E, K, bias):
-    print(f"[router paths] N={N} H={H} E={E} K={K} bias={bias}", flush=True)
-    d = I.random_case(N + E, N, H, E, K, "bf16", bias=bias)
-    ids_o, w_o, logits_o, _ = O.route(d["x"], d["gate_w"], d["bias"], K, "bf16")
+@pytest.mark.parametrize("N,H,E,K,bias,dtype", ROUTER_PATHS)
+def test_router_kernel_paths(N, H, E, K, bias, dtype):
+    print(f"[router paths] N={N} H={H} E={E} K={K} bias={bias} {dtype}", flush=True)
+    d = I.random_case(N + E, N, H, E, K, dtype, bias=bias)
+    ids_o, w_o, logits_o, _ = O.route(d["x"], d["gate_w"], d["bias"], K, dtype)
     ids, w, counts = gpu_route(d)
-    check_route(ids, w, ids_o, w_o, logits_o, K, "bf16")
+    check_route(ids, w, ids_o, w_o, logits_o, K, dtype)
     np.testing.assert_array_equal(counts, np.bincount(ids.ravel(), minlength=E))
-    gids, gw_ = _fused_and_check(d, K, E, "bf16")
-    check_route(gids, gw_, ids_o, w_o, logits_o, K, "bf16")
+    gids, gw_ = _fused_and_check(d, K, E, dtype)
+    check_route(gids, gw_, ids_o, w_o, logits_o, K, dtype)
 
 
 def test_route_dispatch_metadata_only():
