@@ -438,6 +438,17 @@ def main():
             call(name, i)
         _, ms = timed(lambda i, n=name: call(n, i), args.steps)
         stage_ms[name] = ms / args.steps
+    # context for the grouped GEMM: the platform library's dense GEMM of the
+    # same total shape (all T rows through one expert's F x H weights), i.e.
+    # what a tuned library GEMM reaches without per-expert segments
+    dense_ms = None
+    if tdt == torch.bfloat16:
+        w0 = wexp[0]
+        dense = lambda i: torch.mm(sets[i % N_SETS]["x_perm"], w0.t(), out=sets[i % N_SETS]["yexp"])
+        for i in range(3):
+            dense(i)
+        _, ms = timed(dense, args.steps)
+        dense_ms = ms / args.steps
     # leave every set's outputs consistent for the check below
     for i in range(N_SETS):
         step(i)
@@ -487,6 +498,9 @@ def main():
         F=F, tflops=round(g_flops / (stage_ms["grouped_linear"] * 1e-3) / 1e12, 1),
         mfma_frac=round(g_flops / (stage_ms["grouped_linear"] * 1e-3)
                         / (BF16_MFMA_PEAK_TFLOPS * 1e12), 4))
+    if dense_ms is not None:
+        stages["grouped_linear"]["dense_library_gemm_tflops"] = round(
+            g_flops / (dense_ms * 1e-3) / 1e12, 1)
     r_flops = 2.0 * N * H * E
     stages["route"]["mfma_util"] = round(
         r_flops / (stage_ms["route"] * 1e-3) / (BF16_MFMA_PEAK_TFLOPS * 1e12), 4)
