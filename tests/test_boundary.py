@@ -265,3 +265,12 @@ def test_binding_rejects_host_tensors():
     x = torch.zeros((4, 16), dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         _lib.route(x, torch.zeros((16, 8), dtype=torch.bfloat16), 2)
+
+
+def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
+    # no fallback of any kind: a missing libmoe.so is an ImportError at the
+    # first call, not a silent switch to another implementation
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "libmoe.so"))
+    with pytest.raises(ImportError):
+        _lib.library()
