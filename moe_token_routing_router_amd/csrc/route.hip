@@ -42,6 +42,10 @@
 #ifndef MOE_ROUTE_MT128
 #define MOE_ROUTE_MT128 4    // ... for 64 < E <= 128 (4 waves per workgroup)
 #endif
+#ifndef MOE_ROUTE_ESPLIT_DEPTH
+#define MOE_ROUTE_ESPLIT_DEPTH 2  // steps of register prefetch (1 or 2) in the experts-split
+                                  // kernel at 65..128 experts (256 experts: always 1)
+#endif
 #ifndef MOE_ROUTE_ROTATE
 #define MOE_ROUTE_ROTATE 1   // stagger each workgroup's first H step
 #endif
@@ -456,9 +460,10 @@ __global__ __launch_bounds__(NW * 64) void route_bf16_kernel(
 // complete logits (MT*NTW*4 registers) and no partial sums are exchanged.
 // Each 64-wide step's token tile is loaded once per workgroup (every wave a
 // share of its rows), double-buffered in LDS with the XOR swizzle above, and
-// read by every wave: one barrier per step.  The small register and LDS
-// footprint lets several workgroups share a CU, so one's selection overlaps
-// the others' streaming.  Same MFMA operand layout as route_bf16_kernel.
+// read by every wave: one barrier per step.  Up to 128 experts the registers
+// hold two steps of prefetch (three buffers in rotation), 256 experts one.
+// The small register and LDS footprint lets several workgroups share a CU,
+// so one's selection overlaps the others' streaming.  Same MFMA operand layout as route_bf16_kernel.
 template <int NT, int MT, int NW>
 __global__ __launch_bounds__(NW * 64) void route_bf16_esplit_kernel(
     const uint16_t* __restrict__ x, const u32x4* __restrict__ gfrag,
@@ -581,7 +586,32 @@ __global__ __launch_bounds__(NW * 64) void route_bf16_esplit_kernel(
   };
 
   const int nfull = H >> 6;
-  if (nfull > 0) {
+  if (MOE_ROUTE_ESPLIT_DEPTH == 2 && NT <= 8 && nfull > 0) {
+    // two steps of register prefetch: three buffers in rotation, the LDS
+    // tile still alternating with the step (at 256 experts the extra 48
+    // registers cost more than the deeper prefetch gains)
+    const int last = nfull - 1;
+    Buf p, q, o;
+    load(p, 0);
+    load(q, min(1, last));
+    int i = 0;
+    for (; i + 3 <= nfull; i += 3) {
+      load(o, min(i + 2, last));
+      __builtin_amdgcn_sched_barrier(0);
+      mma(p, i & 1);
+      __builtin_amdgcn_sched_barrier(0);
+      load(p, min(i + 3, last));
+      __builtin_amdgcn_sched_barrier(0);
+      mma(q, (i + 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);
+      load(q, min(i + 4, last));
+      __builtin_amdgcn_sched_barrier(0);
+      mma(o, (i + 2) & 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (i < nfull) mma(p, i & 1);
+    if (i + 1 < nfull) mma(q, (i + 1) & 1);
+  } else if (nfull > 0) {
     const int last = nfull - 1;
     Buf p, q;
     load(p, 0);

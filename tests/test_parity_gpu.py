@@ -320,6 +320,13 @@ ROUTER_PATHS = [
     (8191, 72, 256, 4, True, "bf16"),           # just below the split: the H-split kernel
     (16384 + 40, 128, 100, 6, True, "bf16"),    # 65..128 experts, 64-token workgroups
     (3000, 96, 128, 8, False, "bf16"),          # 65..128 experts, 32-token workgroups
+    # 65..128 experts by the number of 64-wide H steps (the prefetch loop
+    # takes three steps per pass): 3 (one pass), 4 (a pass and one more),
+    # 5 and a ragged one, none but the ragged one
+    (16384 + 3, 192, 128, 8, True, "bf16"),
+    (5000, 256, 96, 4, False, "bf16"),
+    (4100, 344, 128, 2, True, "bf16"),
+    (2000, 40, 80, 3, False, "bf16"),
     (700, 72, 256, 16, True, "f32"),            # fp32 router ranking 16-token blocks, E, K at limits
     (3001, 40, 128, 8, False, "f32"),           # fp32, block histogram above the scatter's own sum
 ]
