@@ -891,10 +891,16 @@ hipError_t launch_gate_transpose(const uint16_t* gate_w, int H, int E, uint16_t*
 constexpr int64_t kRouteSmallN = 256 * 64;
 constexpr int64_t kRoute256SplitN = 8192;
 static bool route_small(int EP, int64_t N) { return (EP == 64 || EP == 128) && N < kRouteSmallN; }
+// Up to 256 * 16 tokens, 33..64 experts take 16-token workgroups of 4 waves
+// (one workgroup per CU at most, where 32-token workgroups of 8 waves would
+// leave half the CUs idle); above that the 32-token ones are faster.
+constexpr int64_t kRouteTinyN = 256 * 16;
+static bool route_tiny64(int64_t N) { return N <= kRouteTinyN; }
 static bool route_esplit256(int64_t N) { return MOE_ROUTE_ESPLIT256 && N >= kRoute256SplitN; }
 
 int route_tokens_per_block(int E, int64_t N) {
   const int EP = route_padded_experts(E);
+  if (EP == 64 && route_tiny64(N)) return 16;
   if (EP == 256 && route_esplit256(N)) return N < kRouteSmallN ? 32 : 64;
   return route_small(EP, N) ? 32 : 16 * route_mt(EP);
 }
@@ -910,6 +916,8 @@ hipError_t launch_route_bf16(const uint16_t* x, const uint16_t* wgt, const float
       return launch_bf16_nt<2, route_mt(32)>(x, wgt, bias, N, H, E, K, ids, w, counts, lrank,
                                              bhist, s);
     case 64:
+      if (route_tiny64(N))
+        return launch_bf16_nt<4, 1, 4, 1>(x, wgt, bias, N, H, E, K, ids, w, counts, lrank, bhist, s);
       if (route_small(64, N))
         return launch_bf16_nt<4, 2>(x, wgt, bias, N, H, E, K, ids, w, counts, lrank, bhist, s);
       return launch_bf16_nt<4, route_mt(64)>(x, wgt, bias, N, H, E, K, ids, w, counts, lrank,

@@ -311,8 +311,8 @@ def test_route_dispatch_block_counts(N, K, bias):
 # The router's kernels by expert and token count: the experts-split kernel
 # (65..128 experts at any N; 129..256 experts from 8192 tokens on, with 32
 # tokens per workgroup below 16384 and 64 above) and the H-split kernel (up
-# to 64 experts, and 129..256 experts below 8192 tokens); ragged token tails
-# and H not a multiple of 64.  Both the router alone and the fused call.
+# to 64 experts, with 16, 32 or 64 tokens per workgroup by N, and 129..256
+# experts below 8192 tokens); ragged token tails and H not a multiple of 64.  Both the router alone and the fused call.
 ROUTER_PATHS = [
     # (N, H, E, K, bias, dtype)
     (8192 + 37, 200, 256, 8, True, "bf16"),     # experts split, 32-token workgroups
@@ -327,6 +327,11 @@ ROUTER_PATHS = [
     (5000, 256, 96, 4, False, "bf16"),
     (4100, 344, 128, 2, True, "bf16"),
     (2000, 40, 80, 3, False, "bf16"),
+    # 33..64 experts: 16-token workgroups of 4 waves up to 4096 tokens,
+    # 32-token ones of 8 waves just above
+    (4096, 200, 64, 4, True, "bf16"),
+    (1000, 72, 40, 3, False, "bf16"),
+    (4097, 128, 64, 2, False, "bf16"),
     (700, 72, 256, 16, True, "f32"),            # fp32 router ranking 16-token blocks, E, K at limits
     (3001, 40, 128, 8, False, "f32"),           # fp32, block histogram above the scatter's own sum
 ]
