@@ -21,6 +21,9 @@
 #ifndef MOE_COMBINE_U2
 #define MOE_COMBINE_U2 4        // output vectors per lane in flight for K = 2
 #endif
+#ifndef MOE_COMBINE_U8
+#define MOE_COMBINE_U8 4        // ... for K = 8
+#endif
 #ifndef MOE_COMBINE_NT_LOAD
 #define MOE_COMBINE_NT_LOAD 1   // non-temporal loads of y (each row is read once)
 #endif
@@ -204,7 +207,7 @@ hipError_t launch_dtype(const void* y, const int32_t* inv, const float* w, int64
     case 1: return launch_k<BF16, 1, 8>(y, inv, w, N, H, K, res, out, s);
     case 2: return launch_k<BF16, 2, MOE_COMBINE_U2>(y, inv, w, N, H, K, res, out, s);
     case 4: return launch_k<BF16, 4, 2>(y, inv, w, N, H, K, res, out, s);
-    case 8: return launch_k<BF16, 8, 2>(y, inv, w, N, H, K, res, out, s);
+    case 8: return launch_k<BF16, 8, MOE_COMBINE_U8>(y, inv, w, N, H, K, res, out, s);
     default: return launch_k<BF16, 0, 1>(y, inv, w, N, H, K, res, out, s);
   }
 }
