@@ -155,6 +155,39 @@ moe_status_t moe_route_dispatch(const void *x, const void *gate_w, const float *
                                 size_t workspace_bytes, void *stream);
 
 /*
+ * Bytes of the built-in workspace of moe_route_dispatch_noalloc (one copy per
+ * GPU, held by the library until the process ends).
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+
+/*
+ * moe_route_dispatch_noalloc -- for callers that cannot allocate device
+ * memory or pass a workspace (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): moe_route_dispatch with its
+ * workspace taken from a file-scope device array of MOE_NOALLOC_SCRATCH_BYTES
+ * instead of a caller buffer.  Arguments, outputs, limits and status codes
+ * are those of moe_route_dispatch without workspace/workspace_bytes; the
+ * outputs are bit for bit those of moe_route_dispatch.
+ *  - MOE_ERR_WORKSPACE_TOO_SMALL when moe_route_dispatch_workspace_size(N, H,
+ *    E, K, dtype) exceeds MOE_NOALLOC_SCRATCH_BYTES (e.g. N = 16384, H = 4096,
+ *    E = 64, K = 2 needs 0.7 MiB; N = 32768, H = 2048, E = 128, K = 8 needs
+ *    1.8 MiB).
+ *  - The device is the calling thread's current HIP device; `stream` must
+ *    belong to it.  The first call on a device looks up that device's copy of
+ *    the array (hipGetSymbolAddress, no allocation); MOE_ERR_HIP if that fails.
+ *  - No hipMalloc, hipFree or memset is made, here or in any later call.
+ *  - Every call on one GPU shares that GPU's array: calls that may overlap
+ *    on one GPU (different streams, or threads without ordering) RACE and
+ *    must be serialised by the caller.  Nothing in the array needs clearing
+ *    between calls (each call writes every byte it reads first).
+ */
+moe_status_t moe_route_dispatch_noalloc(const void *x, const void *gate_w, const float *bias,
+                                        int64_t N, int32_t H, int32_t E, int32_t K,
+                                        moe_dtype_t dtype, int32_t *topk_ids, float *topk_w,
+                                        int32_t *counts, int32_t *offsets, int32_t *perm,
+                                        int32_t *inv, void *x_perm, void *stream);
+
+/*
  * Bytes of device workspace moe_ep_dispatch needs (0 for invalid sizes).
  */
 size_t moe_ep_dispatch_workspace_size(int64_t N, int32_t E, int32_t K, int32_t ep_size);

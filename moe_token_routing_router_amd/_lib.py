@@ -27,7 +27,7 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARGUMENT", 2: "MOE_ERR_UNSUPPORTED",
 
 EXPORTS = ("moe_status_string", "moe_route_workspace_size", "moe_route",
            "moe_dispatch_workspace_size", "moe_dispatch", "moe_route_dispatch_workspace_size",
-           "moe_route_dispatch", "moe_ep_dispatch_workspace_size", "moe_ep_dispatch",
+           "moe_route_dispatch", "moe_route_dispatch_noalloc", "moe_ep_dispatch_workspace_size", "moe_ep_dispatch",
            "moe_combine", "moe_aggregate", "moe_grouped_linear", "moe_combine_backward",
            "moe_dispatch_backward",
            "moe_route_backward_workspace_size", "moe_route_backward")
@@ -68,6 +68,9 @@ def library() -> ctypes.CDLL:
         lib.moe_route_dispatch.argtypes = [P, P, P, i64, i32, i32, i32, ctypes.c_int, P, P, P, P,
                                            P, P, P, P, sz, P]
         lib.moe_route_dispatch.restype = ctypes.c_int
+        lib.moe_route_dispatch_noalloc.argtypes = [P, P, P, i64, i32, i32, i32, ctypes.c_int, P,
+                                                   P, P, P, P, P, P, P]
+        lib.moe_route_dispatch_noalloc.restype = ctypes.c_int
         lib.moe_ep_dispatch_workspace_size.argtypes = [i64, i32, i32, i32]
         lib.moe_ep_dispatch_workspace_size.restype = sz
         lib.moe_ep_dispatch.argtypes = [P, P, i64, i32, i32, i32, i32, ctypes.c_int, P, P, P, P,
@@ -229,6 +232,32 @@ def moe_route_dispatch(x: torch.Tensor, gate_w: torch.Tensor, bias: Optional[tor
         _dev(x_perm, "x_perm", x.dtype, N * K * H, dev),
         _dev(workspace, "workspace", torch.uint8, workspace.numel(), dev), workspace.numel(),
         _stream(dev)))
+
+
+def moe_route_dispatch_noalloc(x: torch.Tensor, gate_w: torch.Tensor,
+                               bias: Optional[torch.Tensor], K: int, topk_ids: torch.Tensor,
+                               topk_w: torch.Tensor, counts: torch.Tensor, offsets: torch.Tensor,
+                               perm: torch.Tensor, inv: torch.Tensor,
+                               x_perm: Optional[torch.Tensor]) -> None:
+    """moe_route_dispatch with the library's built-in per-GPU workspace
+    (no workspace argument, no allocation; see include/moe.h).  Calls that
+    may overlap on one GPU race on that workspace."""
+    N, H = x.shape
+    E = gate_w.shape[1]
+    if gate_w.shape[0] != H:
+        raise ValueError("gate_w must be [H, E]")
+    dev = x.device
+    if torch.cuda.current_device() != dev.index:
+        raise ValueError(f"the current device ({torch.cuda.current_device()}) is not {dev}")
+    _check("moe_route_dispatch_noalloc", library().moe_route_dispatch_noalloc(
+        _dev(x, "x", x.dtype, N * H, dev), _dev(gate_w, "gate_w", x.dtype, H * E, dev),
+        _dev(bias, "bias", torch.float32, E, dev), N, H, E, K, _dtype_code(x.dtype),
+        _dev(topk_ids, "topk_ids", torch.int32, N * K, dev),
+        _dev(topk_w, "topk_w", torch.float32, N * K, dev),
+        _dev(counts, "counts", torch.int32, E, dev),
+        _dev(offsets, "offsets", torch.int32, E + 1, dev),
+        _dev(perm, "perm", torch.int32, N * K, dev), _dev(inv, "inv", torch.int32, N * K, dev),
+        _dev(x_perm, "x_perm", x.dtype, N * K * H, dev), _stream(dev)))
 
 
 def moe_ep_dispatch(topk_ids: torch.Tensor, x: Optional[torch.Tensor], E: int, ep_size: int,

@@ -1,6 +1,8 @@
 // extern "C" entry points of libmoe.so (declared in include/moe.h).
 // Every argument is checked on the host before anything is enqueued; the
 // launchers in route.hip / dispatch.hip / combine.hip assume valid input.
+#include <mutex>
+
 #include "moe.h"
 #include "moe_internal.h"
 
@@ -22,6 +24,36 @@ inline bool row_ok(int32_t H, moe_dtype_t dt) {
 }
 
 inline moe_status_t from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+}  // namespace
+
+// Built-in workspace of moe_route_dispatch_noalloc.  Every GPU the library
+// runs on holds its own copy, at its own address, until the process ends.
+// In host code this name is only a stand-in for the symbol: the device
+// address comes from hipGetSymbolAddress (noalloc_scratch below), and only
+// that address is ever handed to a kernel.
+static __device__ __align__(256) char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device, once looked up
+
+// The device address of the current device's copy of `scratch`, looked up on
+// the first call on that device (with the device current) and kept.
+moe_status_t noalloc_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
 
 }  // namespace
 
@@ -160,25 +192,31 @@ size_t moe_route_dispatch_workspace_size(int64_t N, int32_t H, int32_t E, int32_
   return moe_route_workspace_size(H, E, dtype) + dispatch_scratch_bytes(N, E, K, bt);
 }
 
-moe_status_t moe_route_dispatch(const void* x, const void* gate_w, const float* bias, int64_t N,
-                                int32_t H, int32_t E, int32_t K, moe_dtype_t dtype,
-                                int32_t* topk_ids, float* topk_w, int32_t* counts,
-                                int32_t* offsets, int32_t* perm, int32_t* inv, void* x_perm,
-                                void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+
+// Argument checks of moe_route_dispatch other than the workspace's.
+moe_status_t check_route_dispatch(const void* x, const void* gate_w, const float* bias, int64_t N,
+                                  int32_t H, int32_t E, int32_t K, moe_dtype_t dtype,
+                                  const int32_t* topk_ids, const float* topk_w,
+                                  const int32_t* counts, const int32_t* offsets,
+                                  const int32_t* perm, const int32_t* inv, const void* x_perm) {
   if (!valid_dtype(dtype) || N < 0 || H <= 0 || E <= 0 || K < 1 || K > E)
     return MOE_ERR_INVALID_ARGUMENT;
-  if (N > 0 && (!x || !gate_w || !topk_ids || !topk_w || !workspace))
-    return MOE_ERR_INVALID_ARGUMENT;
+  if (N > 0 && (!x || !gate_w || !topk_ids || !topk_w)) return MOE_ERR_INVALID_ARGUMENT;
   moe_status_t st = check_dispatch_outputs(N, H, E, K, dtype, x, counts, offsets, perm, inv, x_perm);
   if (st != MOE_OK) return st;
   if (K > moe::kMaxRouteK) return MOE_ERR_UNSUPPORTED;
-  if (!aligned(gate_w, 16) || !aligned(bias, 4) || !aligned(topk_ids, 4) ||
-      !aligned(topk_w, 4) || !aligned(workspace, 16))
+  if (!aligned(gate_w, 16) || !aligned(bias, 4) || !aligned(topk_ids, 4) || !aligned(topk_w, 4))
     return MOE_ERR_MISALIGNED;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (N == 0) return zero_counts_offsets(counts, offsets, E, s);
-  if (workspace_bytes < moe_route_dispatch_workspace_size(N, H, E, K, dtype))
-    return MOE_ERR_WORKSPACE_TOO_SMALL;
+  return MOE_OK;
+}
+
+// The launches of moe_route_dispatch for N > 0 on a checked workspace.
+moe_status_t launch_route_dispatch(const void* x, const void* gate_w, const float* bias, int64_t N,
+                                   int32_t H, int32_t E, int32_t K, moe_dtype_t dtype,
+                                   int32_t* topk_ids, float* topk_w, int32_t* counts,
+                                   int32_t* offsets, int32_t* perm, int32_t* inv, void* x_perm,
+                                   void* workspace, hipStream_t s) {
   const size_t rws = moe_route_workspace_size(H, E, dtype);
   const int bt =
       dtype == MOE_BF16 ? moe::route_tokens_per_block(E, N) : moe::kRouteF32Tokens;
@@ -213,6 +251,48 @@ moe_status_t moe_route_dispatch(const void* x, const void* gate_w, const float* 
   return from_hip(moe::launch_dispatch_finish(topk_ids, x, N, (int64_t)H * elem_bytes(dtype), E, K,
                                               bt, counts, offsets, perm, inv, x_perm, lrank,
                                               bhist, s, dtype == MOE_BF16 ? bt : 0));
+}
+
+}  // namespace
+
+moe_status_t moe_route_dispatch(const void* x, const void* gate_w, const float* bias, int64_t N,
+                                int32_t H, int32_t E, int32_t K, moe_dtype_t dtype,
+                                int32_t* topk_ids, float* topk_w, int32_t* counts,
+                                int32_t* offsets, int32_t* perm, int32_t* inv, void* x_perm,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  moe_status_t st = check_route_dispatch(x, gate_w, bias, N, H, E, K, dtype, topk_ids, topk_w,
+                                         counts, offsets, perm, inv, x_perm);
+  if (st != MOE_OK) return st;
+  if (N > 0 && !workspace) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned(workspace, 16)) return MOE_ERR_MISALIGNED;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (N == 0) return zero_counts_offsets(counts, offsets, E, s);
+  if (workspace_bytes < moe_route_dispatch_workspace_size(N, H, E, K, dtype))
+    return MOE_ERR_WORKSPACE_TOO_SMALL;
+  return launch_route_dispatch(x, gate_w, bias, N, H, E, K, dtype, topk_ids, topk_w, counts,
+                               offsets, perm, inv, x_perm, workspace, s);
+}
+
+moe_status_t moe_route_dispatch_noalloc(const void* x, const void* gate_w, const float* bias,
+                                        int64_t N, int32_t H, int32_t E, int32_t K,
+                                        moe_dtype_t dtype, int32_t* topk_ids, float* topk_w,
+                                        int32_t* counts, int32_t* offsets, int32_t* perm,
+                                        int32_t* inv, void* x_perm, void* stream) {
+  moe_status_t st = check_route_dispatch(x, gate_w, bias, N, H, E, K, dtype, topk_ids, topk_w,
+                                         counts, offsets, perm, inv, x_perm);
+  if (st != MOE_OK) return st;
+  if (moe_route_dispatch_workspace_size(N, H, E, K, dtype) > MOE_NOALLOC_SCRATCH_BYTES)
+    return MOE_ERR_WORKSPACE_TOO_SMALL;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (N == 0) return zero_counts_offsets(counts, offsets, E, s);
+  void* ws = nullptr;
+  st = noalloc_scratch(&ws);
+  if (st != MOE_OK) return st;
+  // every byte of the workspace the kernels read is written earlier in the
+  // same call (packed gate, block histograms, in-block ranks), so nothing
+  // left by an earlier call needs clearing
+  return launch_route_dispatch(x, gate_w, bias, N, H, E, K, dtype, topk_ids, topk_w, counts,
+                               offsets, perm, inv, x_perm, ws, s);
 }
 
 size_t moe_ep_dispatch_workspace_size(int64_t N, int32_t E, int32_t K, int32_t ep_size) {

@@ -144,6 +144,28 @@ def test_route_dispatch_validation(lib):
     assert route_dispatch(lib, wsb=64) == WS_SMALL
 
 
+def route_dispatch_noalloc(lib, x=A, gw=A, bias=None, N=4, H=16, E=8, K=2, dt=BF16, ids=A2, w=A2,
+                           counts=A2, offsets=A2, perm=A2, inv=A2, xp=A):
+    return lib.moe_route_dispatch_noalloc(x, gw, bias, N, H, E, K, dt, ids, w, counts, offsets,
+                                          perm, inv, xp, None)
+
+
+def test_route_dispatch_noalloc_validation(lib):
+    # every check comes before the device is touched (no GPU here)
+    assert route_dispatch_noalloc(lib, K=9) == INVALID
+    assert route_dispatch_noalloc(lib, gw=None) == INVALID
+    assert route_dispatch_noalloc(lib, counts=None) == INVALID
+    assert route_dispatch_noalloc(lib, E=300, K=2) == UNSUPPORTED
+    assert route_dispatch_noalloc(lib, E=64, K=17) == UNSUPPORTED
+    assert route_dispatch_noalloc(lib, x=MIS8) == MISALIGNED
+    # beyond the built-in 8 MiB: rejected with the workspace status
+    big = dict(N=600000, H=8192, E=256, K=2)
+    assert lib.moe_route_dispatch_workspace_size(600000, 8192, 256, 2, BF16) > 8 << 20
+    assert route_dispatch_noalloc(lib, **big) == WS_SMALL
+    # the five workloads' largest need fits
+    assert lib.moe_route_dispatch_workspace_size(32768, 2048, 128, 8, BF16) <= 8 << 20
+
+
 def ep(lib, ids=A, x=A, N=4, H=16, E=8, K=2, R=2, dt=BF16, counts=A2, offsets=A2, perm=A2,
        inv=A2, sc=A2, so=A2, st=A2, sr=A2, ex=A2, xs=A, ws=A, wsb=1 << 20):
     return lib.moe_ep_dispatch(ids, x, N, H, E, K, R, dt, counts, offsets, perm, inv, sc, so, st,
