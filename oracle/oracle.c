@@ -89,6 +89,19 @@ static void store_elem(void *base, int64_t idx, int dtype, double v) {
     ((float *)base)[idx] = (float)v;
 }
 
+/* ---- threads (timing only) ------------------------------------------- */
+
+/* Threads for the token loops of oracle_route and oracle_combine: 1 unless
+ * a caller asks for more (the benchmark's CPU baseline does; the tests do
+ * not).  Each token is computed the same way whatever the count, so results
+ * are identical; without OpenMP the pragmas are ignored. */
+static int g_threads = 1;
+
+int oracle_set_threads(int32_t n) {
+  g_threads = n < 1 ? 1 : n;
+  return g_threads;
+}
+
 /* ---- [R] router -------------------------------------------------------- */
 
 /*
@@ -102,67 +115,84 @@ static void store_elem(void *base, int64_t idx, int dtype, double v) {
  * x [N,H] and gate_w [H,E] are row-major in `dtype`; bias [E] fp32 or NULL.
  * logits_out [N,E] (double) and margin [N] (double) may be NULL.
  */
+/* One token of oracle_route (logit, p and order are E-entry scratch). */
+static void route_token(const void *x, const void *gate_w, const float *bias, int64_t n,
+                        int32_t H, int32_t E, int32_t K, int32_t dtype, int32_t *ids,
+                        float *w, double *logits_out, double *margin, double *logit,
+                        double *p, int32_t *order) {
+  /* logits: a plain dot product per expert, h in ascending order */
+  for (int32_t e = 0; e < E; ++e) logit[e] = 0.0;
+  for (int32_t h = 0; h < H; ++h) {
+    double xv = load_elem(x, n * (int64_t)H + h, dtype);
+    for (int32_t e = 0; e < E; ++e)
+      logit[e] += xv * load_elem(gate_w, (int64_t)h * E + e, dtype);
+  }
+  if (bias)
+    for (int32_t e = 0; e < E; ++e) logit[e] += (double)bias[e];
+  if (logits_out)
+    for (int32_t e = 0; e < E; ++e) logits_out[n * (int64_t)E + e] = logit[e];
+
+  /* full ordering of the experts by (logit desc, index asc):
+   * insertion sort, which is stable, over indices 0..E-1 */
+  for (int32_t e = 0; e < E; ++e) order[e] = e;
+  for (int32_t i = 1; i < E; ++i) {
+    int32_t cur = order[i];
+    int32_t j = i - 1;
+    while (j >= 0 && logit[order[j]] < logit[cur]) {
+      order[j + 1] = order[j];
+      --j;
+    }
+    order[j + 1] = cur;
+  }
+  for (int32_t k = 0; k < K; ++k) ids[n * K + k] = order[k];
+  if (margin)
+    margin[n] = (K == E) ? INFINITY : logit[order[K - 1]] - logit[order[K]];
+
+  /* softmax over all E experts */
+  double mx = logit[0];
+  for (int32_t e = 1; e < E; ++e)
+    if (logit[e] > mx) mx = logit[e];
+  double z = 0.0;
+  for (int32_t e = 0; e < E; ++e) {
+    p[e] = exp(logit[e] - mx);
+    z += p[e];
+  }
+  for (int32_t e = 0; e < E; ++e) p[e] /= z;
+
+  /* renormalise the K kept probabilities */
+  double s = 0.0;
+  for (int32_t k = 0; k < K; ++k) s += p[order[k]];
+  for (int32_t k = 0; k < K; ++k) w[n * K + k] = (float)(p[order[k]] / s);
+}
+
 int oracle_route(const void *x, const void *gate_w, const float *bias, int64_t N,
                  int32_t H, int32_t E, int32_t K, int32_t dtype, int32_t *ids,
                  float *w, double *logits_out, double *margin) {
   if (N < 0 || H <= 0 || E <= 0 || K < 1 || K > E) return -1;
   if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return -1;
-  double *logit = (double *)malloc(sizeof(double) * (size_t)E);
-  double *p = (double *)malloc(sizeof(double) * (size_t)E);
-  int32_t *order = (int32_t *)malloc(sizeof(int32_t) * (size_t)E);
-  if (!logit || !p || !order) {
-    free(logit); free(p); free(order);
-    return -1;
+  int fail = 0;
+  /* tokens are independent: each thread takes whole tokens with its own
+   * scratch, so the result does not depend on the thread count */
+#pragma omp parallel num_threads(g_threads)
+  {
+    double *logit = (double *)malloc(sizeof(double) * (size_t)E);
+    double *p = (double *)malloc(sizeof(double) * (size_t)E);
+    int32_t *order = (int32_t *)malloc(sizeof(int32_t) * (size_t)E);
+    const int ok = logit && p && order;
+    if (!ok) {
+#pragma omp atomic write
+      fail = 1;
+    }
+#pragma omp for schedule(static)
+    for (int64_t n = 0; n < N; ++n)
+      if (ok)
+        route_token(x, gate_w, bias, n, H, E, K, dtype, ids, w, logits_out, margin, logit, p,
+                    order);
+    free(logit);
+    free(p);
+    free(order);
   }
-  for (int64_t n = 0; n < N; ++n) {
-    /* logits: a plain dot product per expert, h in ascending order */
-    for (int32_t e = 0; e < E; ++e) logit[e] = 0.0;
-    for (int32_t h = 0; h < H; ++h) {
-      double xv = load_elem(x, n * (int64_t)H + h, dtype);
-      for (int32_t e = 0; e < E; ++e)
-        logit[e] += xv * load_elem(gate_w, (int64_t)h * E + e, dtype);
-    }
-    if (bias)
-      for (int32_t e = 0; e < E; ++e) logit[e] += (double)bias[e];
-    if (logits_out)
-      for (int32_t e = 0; e < E; ++e) logits_out[n * (int64_t)E + e] = logit[e];
-
-    /* full ordering of the experts by (logit desc, index asc):
-     * insertion sort, which is stable, over indices 0..E-1 */
-    for (int32_t e = 0; e < E; ++e) order[e] = e;
-    for (int32_t i = 1; i < E; ++i) {
-      int32_t cur = order[i];
-      int32_t j = i - 1;
-      while (j >= 0 && logit[order[j]] < logit[cur]) {
-        order[j + 1] = order[j];
-        --j;
-      }
-      order[j + 1] = cur;
-    }
-    for (int32_t k = 0; k < K; ++k) ids[n * K + k] = order[k];
-    if (margin)
-      margin[n] = (K == E) ? INFINITY : logit[order[K - 1]] - logit[order[K]];
-
-    /* softmax over all E experts */
-    double mx = logit[0];
-    for (int32_t e = 1; e < E; ++e)
-      if (logit[e] > mx) mx = logit[e];
-    double z = 0.0;
-    for (int32_t e = 0; e < E; ++e) {
-      p[e] = exp(logit[e] - mx);
-      z += p[e];
-    }
-    for (int32_t e = 0; e < E; ++e) p[e] /= z;
-
-    /* renormalise the K kept probabilities */
-    double s = 0.0;
-    for (int32_t k = 0; k < K; ++k) s += p[order[k]];
-    for (int32_t k = 0; k < K; ++k) w[n * K + k] = (float)(p[order[k]] / s);
-  }
-  free(logit);
-  free(p);
-  free(order);
-  return 0;
+  return fail ? -1 : 0;
 }
 
 /* ---- [D] counting-sort dispatch --------------------------------------- */
@@ -334,12 +364,18 @@ int oracle_combine(const void *y, const int32_t *inv, const float *w, int64_t N,
   if (N < 0 || H <= 0 || K < 1) return -1;
   if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return -1;
   int64_t T = N * (int64_t)K;
+  int fail = 0;
+#pragma omp parallel for schedule(static) num_threads(g_threads)
   for (int64_t n = 0; n < N; ++n) {
     for (int32_t h = 0; h < H; ++h) {
       double acc = 0.0;
       for (int32_t k = 0; k < K; ++k) {
         int64_t row = inv[n * K + k];
-        if (row < 0 || row >= T) return -1;
+        if (row < 0 || row >= T) {
+#pragma omp atomic write
+          fail = 1;
+          continue;
+        }
         acc += (double)w[n * K + k] * load_elem(y, row * H + h, dtype);
       }
       if (dtype == ORACLE_BF16)
@@ -348,7 +384,7 @@ int oracle_combine(const void *y, const int32_t *inv, const float *w, int64_t N,
         ((float *)out)[n * (int64_t)H + h] = (float)acc;
     }
   }
-  return 0;
+  return fail ? -1 : 0;
 }
 
 /* ---- [A] forward_aggregate: weighted expert output + residual ------------ */

@@ -57,6 +57,8 @@ def _load():
         lib.oracle_aggregate.restype = ctypes.c_int
         lib.oracle_grouped_linear.argtypes = [P, P, P, i32, i32, i32, i32, P, i64, P]
         lib.oracle_grouped_linear.restype = ctypes.c_int
+        lib.oracle_set_threads.argtypes = [i32]
+        lib.oracle_set_threads.restype = ctypes.c_int
         lib.oracle_round_bf16.argtypes = [dbl]
         lib.oracle_round_bf16.restype = ctypes.c_uint16
         lib.oracle_decode_bf16.argtypes = [ctypes.c_uint16]
@@ -64,6 +66,13 @@ def _load():
         _lib = lib
     return _lib
 
+
+
+def set_threads(n):
+    """Threads for the token loops of route and combine (default 1).  Tokens
+    are independent and each is computed the same way, so results do not
+    depend on n; only the CPU baseline's timing uses more than one."""
+    return int(_load().oracle_set_threads(int(n)))
 
 def _ptr(a):
     return None if a is None else a.ctypes.data_as(ctypes.c_void_p)

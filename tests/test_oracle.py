@@ -690,3 +690,26 @@ def test_grouped_linear_rejects_bad_offsets():
         O.grouped_linear(x, W, np.array([0, 3, 2], np.int32), "f32")   # decreasing
     with pytest.raises(ValueError):
         O.grouped_linear(x, W, np.array([1, 2, 4], np.int32), "f32")   # not from 0
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_threaded_route_and_combine_equal_one_thread(dtype):
+    # the CPU baseline's all-cores run splits the token loops over OpenMP
+    # threads; every output must be bit for bit the one-thread result
+    d = I.random_case(31, 777, 64, 24, 3, dtype, bias=True)
+    one = O.route(d["x"], d["gate_w"], d["bias"], 3, dtype)
+    _, _, _, inv = O.dispatch(one[0], 24)
+    c1 = O.combine(d["y"], inv, one[1], dtype)
+    try:
+        assert O.set_threads(4) == 4
+        many = O.route(d["x"], d["gate_w"], d["bias"], 3, dtype)
+        c4 = O.combine(d["y"], inv, one[1], dtype)
+    finally:
+        O.set_threads(1)
+    for a, b in zip(one, many):
+        np.testing.assert_array_equal(a, b)
+    np.testing.assert_array_equal(c1.view(np.uint8), c4.view(np.uint8))
+    bad = inv.copy()
+    bad[5] = 10 ** 6
+    with pytest.raises(ValueError):
+        O.combine(d["y"], bad, one[1], dtype)
