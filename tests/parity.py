@@ -8,6 +8,15 @@ must pick valid experts (each within 1e-3 of the K-th logit).  Weights are
 matched by (token, expert): within 2e-3 for bf16 inputs, 1e-5 for fp32.
 Combine outputs: |gpu - ref| <= 1e-2*|ref| + 1e-4 for bf16 and
 1e-5*|ref| + 1e-6 for fp32.
+
+Beside those contract rules, the arithmetic the kernels claim is checked
+tightly (check_sum_tight): a sum of n terms accumulated in fp32 and rounded
+once differs from the oracle's exactly rounded sum by at most one unit in the
+last place of the output format plus the fp32 accumulation error
+n * 2^-24 * sum|terms|, and for bf16 outputs all but a few elements in 10^4
+are bit-identical (they differ only where the fp32 error straddles a bf16
+rounding point).  A kernel that accumulated in bf16, rounded a product or a
+partial sum to bf16, or truncated instead of rounding fails it.
 """
 import numpy as np
 import torch
@@ -15,7 +24,13 @@ import torch
 from moe_token_routing_router_amd import inputs as I
 
 MARGIN = 1e-3
+U32 = 2.0 ** -24           # unit roundoff of fp32
+MIN_EXACT = {"bf16": 0.9995}
 W_TOL = {"bf16": 2e-3, "f32": 1e-5}
+# what fp32 accumulation of the logits (exact bf16 products, or fp32 FMAs)
+# and an fp32 softmax leave in the weights: logit errors of a few 1e-6 at
+# most at these sizes, and |dw| <= max|dl| / 2
+W_TIGHT = {"bf16": 1e-5, "f32": 1e-6}
 C_REL = {"bf16": 1e-2, "f32": 1e-5}
 C_ABS = {"bf16": 1e-4, "f32": 1e-6}
 
@@ -78,6 +93,8 @@ def check_route(ids_g, w_g, ids_o, w_o, logits_o, K, dtype):
     wo = np.take_along_axis(w_o[rows], oo, 1).astype(np.float64)
     err = np.abs(wg - wo).max() if len(rows) else 0.0
     assert err <= tol, f"router weight error {err} > {tol}"
+    print(f"    router weight error {err:.3g} (tight bound {W_TIGHT[dtype]:g})", flush=True)
+    assert err <= W_TIGHT[dtype], f"router weight error {err} > {W_TIGHT[dtype]}"
     # rows inside the margin: valid picks, weights = softmax of the chosen
     # oracle logits, summing to one
     ex = np.nonzero(~sure)[0]
@@ -88,6 +105,7 @@ def check_route(ids_g, w_g, ids_o, w_o, logits_o, K, dtype):
         ref = np.exp(chosen - chosen.max(1, keepdims=True))
         ref /= ref.sum(1, keepdims=True)
         assert np.abs(ref - w_g[ex]).max() <= tol
+        assert np.abs(ref - w_g[ex]).max() <= W_TIGHT[dtype]
     assert np.abs(w_g.astype(np.float64).sum(1) - 1).max() <= 1e-5
     return int((~sure).sum())
 
@@ -101,3 +119,52 @@ def check_combine(out_g, out_o, dtype):
     assert not bad.any(), f"{bad.sum()} combine elements out of tolerance, worst " \
                           f"{(err - lim).max()} at {np.unravel_index(np.argmax(err - lim), err.shape)}"
     return float((err / (np.abs(o) + C_ABS[dtype])).max())
+
+
+def sum_of_abs_terms(y, inv, K, dtype, w=None, residual=None, chunk=1024):
+    """S[n, :] = sum_k |w[n,k]| * |y[inv[n*K+k], :]| (+ |residual[n, :]|) in
+    float64, by chunks of tokens; w None means unit weights."""
+    inv = np.asarray(inv, dtype=np.int64)
+    N = inv.shape[0] // K
+    H = y.shape[1]
+    S = np.zeros((N, H))
+    for n0 in range(0, N, chunk):
+        n1 = min(N, n0 + chunk)
+        acc = np.zeros((n1 - n0, H))
+        for k in range(K):
+            rows = np.abs(decode(y[inv[n0 * K + k:n1 * K:K]], dtype))
+            if w is not None:
+                rows *= np.abs(w[n0:n1, k].astype(np.float64))[:, None]
+            acc += rows
+        if residual is not None:
+            acc += np.abs(decode(residual[n0:n1], dtype))
+        S[n0:n1] = acc
+    return S
+
+
+def ulp(v, dtype):
+    """Spacing of the format at |v| (normal range; the smallest normal
+    spacing below it)."""
+    p = 7 if dtype == "bf16" else 23
+    a = np.maximum(np.abs(v), 2.0 ** -126)
+    return 2.0 ** (np.floor(np.log2(a)) - p)
+
+
+def check_sum_tight(out_g, out_o, S, nterms, dtype):
+    """Assert |g - o| <= max(ulp(g), ulp(o)) + nterms * 2^-24 * S on every
+    element (see the module docstring) and, for bf16, that at least
+    MIN_EXACT of the elements are bit-identical.  Returns the bit-identical
+    fraction."""
+    g = decode(out_g, dtype)
+    o = decode(out_o, dtype)
+    lim = np.maximum(ulp(g, dtype), ulp(o, dtype)) + nterms * U32 * S
+    err = np.abs(g - o)
+    bad = err > lim
+    assert not bad.any(), f"{bad.sum()} elements beyond one ulp plus the fp32 accumulation " \
+                          f"error, worst {(err - lim).max()} at " \
+                          f"{np.unravel_index(np.argmax(err - lim), err.shape)}"
+    exact = float((np.asarray(out_g) == np.asarray(out_o)).mean()) if np.asarray(out_g).size else 1.0
+    print(f"    bit-identical fraction {exact:.6f}", flush=True)
+    if dtype in MIN_EXACT:
+        assert exact >= MIN_EXACT[dtype], f"only {exact} of the outputs are bit-identical"
+    return exact

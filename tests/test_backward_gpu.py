@@ -20,7 +20,8 @@ import torch
 from moe_token_routing_router_amd import _lib as L
 from moe_token_routing_router_amd import inputs as I
 from oracle import oracle as O
-from tests.parity import check_combine, decode, from_dev, to_dev
+from tests.parity import (check_combine, check_sum_tight, decode, from_dev, sum_of_abs_terms,
+                          to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -107,7 +108,10 @@ def test_dispatch_backward_full_size(name):
     _, _, _, inv = O.dispatch(ids, d["E"])
     dx = L.dispatch_backward(to_dev(d["y"], d["dtype"]), torch.from_numpy(inv).cuda(), d["N"])
     torch.cuda.synchronize()
-    check_combine(from_dev(dx), O.dispatch_backward(d["y"], inv, d["K"], d["dtype"]), d["dtype"])
+    ref = O.dispatch_backward(d["y"], inv, d["K"], d["dtype"])
+    check_combine(from_dev(dx), ref, d["dtype"])
+    S = sum_of_abs_terms(d["y"], inv, d["K"], d["dtype"])
+    check_sum_tight(from_dev(dx), ref, S, d["K"], d["dtype"])
 
 
 @pytest.mark.parametrize("name", WORKLOADS)

@@ -12,7 +12,8 @@ import torch
 from moe_token_routing_router_amd import _lib as L
 from moe_token_routing_router_amd import inputs as I
 from oracle import oracle as O
-from tests.parity import check_combine, check_route, from_dev, to_dev
+from tests.parity import (check_combine, check_route, check_sum_tight, from_dev,
+                          sum_of_abs_terms, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -94,7 +95,10 @@ def test_combine_full_size(name):
     out = L.combine(to_dev(d["y"], d["dtype"]), torch.from_numpy(o["inv"]).cuda(),
                     torch.from_numpy(o["w"]).cuda())
     torch.cuda.synchronize()
-    check_combine(from_dev(out), o["out"], d["dtype"])
+    got = from_dev(out)
+    check_combine(got, o["out"], d["dtype"])
+    S = sum_of_abs_terms(d["y"], o["inv"], d["K"], d["dtype"], w=o["w"])
+    check_sum_tight(got, o["out"], S, d["K"], d["dtype"])
 
 
 @pytest.mark.parametrize("name", WORKLOADS)
@@ -158,7 +162,9 @@ def test_edge_case_full_chain(N, H, E, K, dtype, bias):
     np.testing.assert_array_equal(gx.view(np.uint8), O.permute_rows(d["x"], op, K).view(np.uint8))
     out = L.combine(to_dev(d["y"], dtype), torch.from_numpy(oi).cuda(),
                     torch.from_numpy(w_o).cuda())
-    check_combine(from_dev(out), O.combine(d["y"], oi, w_o, dtype), dtype)
+    ref = O.combine(d["y"], oi, w_o, dtype)
+    check_combine(from_dev(out), ref, dtype)
+    check_sum_tight(from_dev(out), ref, sum_of_abs_terms(d["y"], oi, K, dtype, w=w_o), K, dtype)
 
 
 @pytest.mark.parametrize("skew", [0.0, 1.5, 4.0])
@@ -442,7 +448,10 @@ def test_aggregate_full_size(name):
     out = L.aggregate(to_dev(d["y"], dt), torch.from_numpy(o["inv"]).cuda(),
                       torch.from_numpy(o["w"]).cuda(), to_dev(d["x"], dt))
     torch.cuda.synchronize()
-    check_combine(from_dev(out), O.aggregate(d["y"], o["inv"], o["w"], d["x"], dt), dt)
+    ref = O.aggregate(d["y"], o["inv"], o["w"], d["x"], dt)
+    check_combine(from_dev(out), ref, dt)
+    S = sum_of_abs_terms(d["y"], o["inv"], d["K"], dt, w=o["w"], residual=d["x"])
+    check_sum_tight(from_dev(out), ref, S, d["K"] + 1, dt)
 
 
 @pytest.mark.parametrize("N,H,E,K,dtype,bias", EDGE[:6] + EDGE[-2:])
@@ -458,3 +467,5 @@ def test_aggregate_edge_cases_and_in_place(N, H, E, K, dtype, bias):
                     torch.from_numpy(w).cuda(), res, res)  # out aliases the residual
     torch.cuda.synchronize()
     check_combine(from_dev(res), ref, dtype)
+    S = sum_of_abs_terms(d["y"], inv, K, dtype, w=w, residual=d["x"])
+    check_sum_tight(from_dev(res), ref, S, K + 1, dtype)
