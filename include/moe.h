@@ -43,7 +43,16 @@
 extern "C" {
 #endif
 
-typedef enum {
+/* In C++ the two enums get int as their fixed underlying type, so any int a C
+ * caller passes (e.g. an unknown status code) is a valid value of the type
+ * rather than undefined behaviour; in C an enum is an int anyway. */
+#ifdef __cplusplus
+#define MOE_ENUM_BASE : int
+#else
+#define MOE_ENUM_BASE
+#endif
+
+typedef enum MOE_ENUM_BASE {
   MOE_OK = 0,
   MOE_ERR_INVALID_ARGUMENT = 1,   /* NULL required pointer, bad size, K > E */
   MOE_ERR_UNSUPPORTED = 2,        /* outside the limits listed above */
@@ -52,7 +61,7 @@ typedef enum {
   MOE_ERR_HIP = 5                 /* a kernel launch reported an error */
 } moe_status_t;
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
+typedef enum MOE_ENUM_BASE { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char *moe_status_string(moe_status_t status);

@@ -17,7 +17,9 @@ from typing import Optional
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmoe.so")
+# MOE_LIB points the binding at another build of the same library (the host
+# sanitizer run of the CPU tests uses one); default: the in-tree build.
+LIB_PATH = os.environ.get("MOE_LIB") or os.path.join(_HERE, "libmoe.so")
 
 MOE_F32 = 0
 MOE_BF16 = 1
