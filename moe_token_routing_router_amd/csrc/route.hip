@@ -22,7 +22,8 @@
 //    through LDS and keep complete logits (route_bf16_esplit_kernel);
 //  * softmax/top-K/renorm happen in registers: a token's logits live in one
 //    16-lane row of the wave (lane r holds experts r, r+16, ...), and each of
-//    the K rounds is a 16-lane arg-max butterfly.
+//    the K rounds is a 16-lane max butterfly on order-preserving integer keys
+//    followed by a min butterfly on the expert indices holding the maximum.
 //
 // Selection is on logits (softmax is monotone), ties go to the lower expert
 // index, and since the renormalised weights equal a softmax over the K kept
@@ -89,19 +90,6 @@ constexpr int kDppXor2 = 0x4E;        // quad_perm(2,3,0,1)
 constexpr int kDppHalfMirror = 0x141;  // row_half_mirror
 constexpr int kDppMirror = 0x140;      // row_mirror
 
-// (value, index) arg-max step: larger value wins, equal values go to the
-// lower index.  Symmetric, so the order of the partners does not matter.
-// Written with bitwise operators and selects: short-circuit conditions here
-// compile to divergent branches.
-template <int CTRL>
-__device__ __forceinline__ void argmax_step(float& bv, int& bi) {
-  const float ov = dpp_f<CTRL>(bv);
-  const int oi = dpp_i<CTRL>(bi);
-  const bool take = (ov > bv) | ((ov == bv) & (oi < bi));
-  bv = take ? ov : bv;
-  bi = take ? oi : bi;
-}
-
 __device__ __forceinline__ float sum16(float v) {
   v += dpp_f<kDppXor1>(v);
   v += dpp_f<kDppXor2>(v);
@@ -117,61 +105,88 @@ __device__ __forceinline__ float sum16(float v) {
 // writes ids[t_u*K + r], w[t_u*K + r].
 // v[u][q] is the logit of expert 16*q + r for token t[u] (already biased);
 // experts >= E are never candidates.
+//
+// Each round is two 16-lane reductions on integer keys that order like the
+// logits: the largest remaining key (a max butterfly), then the lowest expert
+// index holding it (a min butterfly), so equal logits go to the lower index.
+// key(x) flips the magnitude bits of negative values, so signed integer order
+// equals float order; x + 0 first turns -0 into +0, so the two zeros are equal
+// as they are for floats; a NaN logit (outside the finite-input precondition)
+// is ranked as -inf.  A value that is no longer a candidate (already picked,
+// or an expert index >= E) holds INT_MIN, below every key.  Integer max/min
+// fold into one DPP instruction per butterfly step (a float max would also
+// need the NaN-quieting of fmaxf).
+__device__ __forceinline__ int order_key(float x) {
+  x = (x == x) ? x + 0.0f : -__builtin_inff();
+  const int b = __float_as_int(x);
+  return b ^ ((b >> 31) & 0x7fffffff);
+}
+
 template <int NT, int U>
 __device__ __forceinline__ void select_topk_store(const float (&v)[U][NT], int r, int E, int K,
                                                   const int64_t (&t)[U], int64_t N,
                                                   int32_t* __restrict__ ids,
                                                   float* __restrict__ topw, int* hist,
                                                   int (&pick)[U]) {
-  uint32_t taken[U];
-  float my_val[U], top[U];
-  int my_id[U];
+  constexpr int kGone = (int)0x80000000;
+  int c[U][NT];
+  int my_key[U], top_key[U], my_id[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    taken[u] = 0u;
-    my_val[u] = 0.f;
-    top[u] = 0.f;
+    my_key[u] = 0;
+    top_key[u] = 0;
     my_id[u] = 0;
+#pragma unroll
+    for (int q = 0; q < NT; ++q) c[u][q] = (16 * q + r < E) ? order_key(v[u][q]) : kGone;
   }
   for (int k = 0; k < K; ++k) {
-    float bv[U];
-    int bi[U];
+    int m[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      bv[u] = -__builtin_inff();
-      bi[u] = kSentinel;
+      m[u] = c[u][0];
 #pragma unroll
-      for (int q = 0; q < NT; ++q) {
-        const int e = 16 * q + r;
-        const bool cand = (e < E) & (((taken[u] >> q) & 1u) == 0u);
-        // experts are visited in ascending index: strict '>' keeps the lower
-        // index on ties; the first candidate always replaces the sentinel
-        const bool better = cand & ((bi[u] == kSentinel) | (v[u][q] > bv[u]));
-        bv[u] = better ? v[u][q] : bv[u];
-        bi[u] = better ? e : bi[u];
-      }
+      for (int q = 1; q < NT; ++q) m[u] = max(m[u], c[u][q]);
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) argmax_step<kDppXor1>(bv[u], bi[u]);
+    for (int u = 0; u < U; ++u) m[u] = max(m[u], dpp_i<kDppXor1>(m[u]));
 #pragma unroll
-    for (int u = 0; u < U; ++u) argmax_step<kDppXor2>(bv[u], bi[u]);
+    for (int u = 0; u < U; ++u) m[u] = max(m[u], dpp_i<kDppXor2>(m[u]));
 #pragma unroll
-    for (int u = 0; u < U; ++u) argmax_step<kDppHalfMirror>(bv[u], bi[u]);
+    for (int u = 0; u < U; ++u) m[u] = max(m[u], dpp_i<kDppHalfMirror>(m[u]));
 #pragma unroll
-    for (int u = 0; u < U; ++u) argmax_step<kDppMirror>(bv[u], bi[u]);
+    for (int u = 0; u < U; ++u) m[u] = max(m[u], dpp_i<kDppMirror>(m[u]));
+    int ix[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      ix[u] = kSentinel;
+#pragma unroll
+      for (int q = NT - 1; q >= 0; --q) ix[u] = (c[u][q] == m[u]) ? 16 * q + r : ix[u];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) ix[u] = min(ix[u], dpp_i<kDppXor1>(ix[u]));
+#pragma unroll
+    for (int u = 0; u < U; ++u) ix[u] = min(ix[u], dpp_i<kDppXor2>(ix[u]));
+#pragma unroll
+    for (int u = 0; u < U; ++u) ix[u] = min(ix[u], dpp_i<kDppHalfMirror>(ix[u]));
+#pragma unroll
+    for (int u = 0; u < U; ++u) ix[u] = min(ix[u], dpp_i<kDppMirror>(ix[u]));
     const bool mine = (r == k);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      top[u] = (k == 0) ? bv[u] : top[u];
-      my_val[u] = mine ? bv[u] : my_val[u];
-      my_id[u] = mine ? bi[u] : my_id[u];
-      taken[u] |= ((bi[u] & 15) == r) ? (1u << ((bi[u] >> 4) & 31)) : 0u;
+      top_key[u] = (k == 0) ? m[u] : top_key[u];
+      my_key[u] = mine ? m[u] : my_key[u];
+      my_id[u] = mine ? ix[u] : my_id[u];
+#pragma unroll
+      for (int q = 0; q < NT; ++q) c[u][q] = (16 * q + r == ix[u]) ? kGone : c[u][q];
     }
   }
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     pick[u] = my_id[u];
-    const float ex = (r < K) ? expf(my_val[u] - top[u]) : 0.f;
+    // the key transform is its own inverse
+    const float my_val = __int_as_float(my_key[u] ^ ((my_key[u] >> 31) & 0x7fffffff));
+    const float top = __int_as_float(top_key[u] ^ ((top_key[u] >> 31) & 0x7fffffff));
+    const float ex = (r < K) ? expf(my_val - top) : 0.f;
     const float sum = sum16(ex);
     if ((t[u] < N) & (r < K)) {
       ids[t[u] * K + r] = my_id[u];

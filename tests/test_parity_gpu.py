@@ -355,6 +355,50 @@ def test_router_kernel_paths(N, H, E, K, bias, dtype):
     check_route(gids, gw_, ids_o, w_o, logits_o, K, dtype)
 
 
+TIE_CASES = [
+    # (N, H, E, K, dtype): every router kernel family, K from 1 to 16
+    (300, 256, 20, 3, "bf16"),      # H-split kernel, E padded
+    (5000, 512, 64, 2, "bf16"),     # H-split kernel, 32-token workgroups
+    (17000, 128, 64, 4, "bf16"),    # H-split kernel, 64-token workgroups
+    (2000, 128, 128, 8, "bf16"),    # experts-split kernel
+    (9000, 64, 256, 16, "bf16"),    # experts-split kernel, 256 experts
+    (600, 64, 256, 5, "bf16"),      # H-split kernel, 256 experts
+    (333, 32, 48, 6, "f32"),        # fp32 kernel
+]
+
+
+@pytest.mark.parametrize("N,H,E,K,dtype", TIE_CASES)
+def test_router_exact_ties_go_to_the_lower_index(N, H, E, K, dtype):
+    # Gate columns in groups of three identical columns (and a shared bias per
+    # group): every logit ties exactly with two others, on the GPU as in the
+    # oracle.  Some token rows are all zero (every logit ties).  Where the
+    # distinct logit values among the top K+1 are more than 1e-3 apart, the
+    # ids must equal the oracle's exactly, order included: ties in descending
+    # order of logit, equal logits by ascending expert index.
+    print(f"[ties] N={N} H={H} E={E} K={K} {dtype}", flush=True)
+    d = I.random_case(N + 7 * E, N, H, (E + 2) // 3, 1, dtype, bias=True, with_y=False)
+    col = np.arange(E) // 3
+    d["gate_w"] = np.ascontiguousarray(d["gate_w"][:, col])
+    d["bias"] = np.ascontiguousarray(d["bias"][col])
+    d["x"][::97] = 0
+    d["E"], d["K"] = E, K
+    ids_o, w_o, logits_o, _ = O.route(d["x"], d["gate_w"], d["bias"], K, dtype)
+    ids, w, _ = gpu_route(d)
+    srt = -np.sort(-logits_o, axis=1)[:, :K + 1]
+    gaps = srt[:, :-1] - srt[:, 1:]
+    clear = ((gaps == 0) | (gaps > 1e-3)).all(axis=1)
+    assert clear.mean() > 0.5
+    bad = clear & (ids != ids_o).any(axis=1)
+    assert not bad.any(), f"{bad.sum()} rows differ, e.g. row {np.nonzero(bad)[0][:3]}: " \
+                          f"{ids[bad][:1]} vs {ids_o[bad][:1]}"
+    zero_rows = np.arange(0, N, 97)
+    b = d["bias"]
+    exp_ids = np.argsort(-b.astype(np.float64), kind="stable")[:K]
+    np.testing.assert_array_equal(ids[zero_rows], np.broadcast_to(exp_ids, (len(zero_rows), K)))
+    gids, gw_ = _fused_and_check(d, K, E, dtype)
+    np.testing.assert_array_equal(gids[clear], ids_o[clear])
+
+
 def test_route_dispatch_metadata_only():
     d = I.random_case(11, 777, 256, 64, 4, "bf16", bias=True)
     _fused_and_check(d, 4, 64, "bf16", with_rows=False)
