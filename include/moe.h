@@ -68,8 +68,9 @@ const char *moe_status_string(moe_status_t status);
 
 /*
  * Bytes of device workspace moe_route needs for (H, E, dtype); 0 if none.
- * (bf16: the gate matrix re-laid out expert-major, padded to a multiple of
- * 16 experts.)
+ * (bf16: the gate matrix re-laid out in MFMA fragment order, padded to a
+ * power-of-two multiple of 16 experts; none at exactly 64 experts, where the
+ * router reads gate_w as it is.)
  */
 size_t moe_route_workspace_size(int32_t H, int32_t E, moe_dtype_t dtype);
 

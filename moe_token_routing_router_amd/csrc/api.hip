@@ -73,6 +73,7 @@ const char* moe_status_string(moe_status_t status) {
 
 size_t moe_route_workspace_size(int32_t H, int32_t E, moe_dtype_t dtype) {
   if (dtype != MOE_BF16 || H <= 0 || E <= 0 || E > moe::kMaxExperts) return 0;
+  if (moe::route_gate_raw(E)) return 0;  // the router reads gate_w itself
   return round_up((size_t)moe::route_padded_experts(E) * (size_t)moe::route_gate_rows(H) * 2, 256);
 }
 
@@ -94,9 +95,15 @@ moe_status_t moe_route(const void* x, const void* gate_w, const float* bias, int
   if (N == 0) return counts ? from_hip(moe::launch_fill_i32(counts, E, 0, s)) : MOE_OK;
 
   if (dtype == MOE_BF16) {
-    uint16_t* wgt = reinterpret_cast<uint16_t*>(workspace);
-    hipError_t e = moe::launch_gate_transpose(reinterpret_cast<const uint16_t*>(gate_w), H, E, wgt,
-                                              counts, s);
+    const uint16_t* wgt = reinterpret_cast<const uint16_t*>(gate_w);
+    hipError_t e = hipSuccess;
+    if (moe::route_gate_raw(E)) {
+      if (counts) e = moe::launch_fill_i32(counts, E, 0, s);
+    } else {
+      uint16_t* packed = reinterpret_cast<uint16_t*>(workspace);
+      e = moe::launch_gate_transpose(wgt, H, E, packed, counts, s);
+      wgt = packed;
+    }
     if (e != hipSuccess) return MOE_ERR_HIP;
     return from_hip(moe::launch_route_bf16(reinterpret_cast<const uint16_t*>(x), wgt, bias, N, H,
                                            E, K, topk_ids, topk_w, counts, nullptr, nullptr, s));
@@ -230,9 +237,14 @@ moe_status_t launch_route_dispatch(const void* x, const void* gate_w, const floa
     // histograms into them, and each scatter workgroup sums the blocks before
     // its own, so no scan kernel runs.  Many blocks: the scan kernel.
     const bool prefix = moe::dispatch_num_blocks(N, bt) <= kPrefixMaxBlocks && K <= 2;
-    uint16_t* wgt = reinterpret_cast<uint16_t*>(workspace);
-    e = moe::launch_gate_transpose(reinterpret_cast<const uint16_t*>(gate_w), H, E, wgt,
-                                   prefix ? counts : nullptr, s);
+    const uint16_t* wgt = reinterpret_cast<const uint16_t*>(gate_w);
+    if (moe::route_gate_raw(E)) {
+      e = prefix ? moe::launch_fill_i32(counts, E, 0, s) : hipSuccess;
+    } else {
+      uint16_t* packed = reinterpret_cast<uint16_t*>(workspace);
+      e = moe::launch_gate_transpose(wgt, H, E, packed, prefix ? counts : nullptr, s);
+      wgt = packed;
+    }
     if (e != hipSuccess) return MOE_ERR_HIP;
     e = moe::launch_route_bf16(reinterpret_cast<const uint16_t*>(x), wgt, bias, N, H, E, K,
                                topk_ids, topk_w, prefix ? counts : nullptr, lrank, bhist, s);

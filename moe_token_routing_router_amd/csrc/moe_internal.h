@@ -173,6 +173,9 @@ __device__ __forceinline__ void block_stable_rank(const int* sids, int S, int E,
 int route_padded_experts(int E);
 int route_gate_rows(int H);  // H rounded up to whole 64-wide steps (packed gate)
 int route_tokens_per_block(int E, int64_t N);  // tokens per router workgroup
+// True when the bf16 router reads gate_w as it is (no packed copy, no
+// packing kernel; wgt is then gate_w itself).
+bool route_gate_raw(int E);
 hipError_t launch_gate_transpose(const uint16_t* gate_w, int H, int E, uint16_t* wgt,
                                  int32_t* counts, hipStream_t s);
 hipError_t launch_route_bf16(const uint16_t* x, const uint16_t* wgt, const float* bias,

@@ -56,6 +56,9 @@
 #ifndef MOE_ROUTE_F32_UNROLL
 #define MOE_ROUTE_F32_UNROLL 8  // fp32 router: h steps of 4 unrolled together
 #endif
+#ifndef MOE_ROUTE_RAW_GATE
+#define MOE_ROUTE_RAW_GATE 1  // 64 experts: read the row-major gate through LDS, no packing kernel
+#endif
 #ifndef MOE_ROUTE_ESPLIT128
 #define MOE_ROUTE_ESPLIT128 1  // 65..128 experts: waves split the experts instead of H
 #endif
@@ -220,7 +223,17 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4 u) {
 // both operands use the same (g, j) -> h map, so each MFMA pair sums h over
 // [h0, h0 + 64) once.  Accumulator element i of lane l is D[4g + i][r]:
 // token 16m + 4g + i, expert 16q + r.
-template <int NT, int MT, int NW, int D>
+//
+// RAW (64 experts): the B operand comes straight from the row-major gate_w
+// instead of the packed copy.  A step's 64 gate rows are one contiguous 8 KiB
+// block; the wave copies it into its own LDS gate tile (row-major, 32-byte
+// quarters of each row XOR-swizzled by (row & 3) ^ ((row >> 4) & 1), which
+// keeps both the 16-byte writes and the transposing reads free of bank
+// conflicts) and reads each B fragment with two ds_read_b64_tr_b16: in a
+// 16-lane group, lane 4a + b points at row R + a, experts 16q + 4b .. +3, and
+// the transpose hands lane r the four rows R .. R+3 of expert 16q + r.  No
+// packing kernel runs.
+template <int NT, int MT, int NW, int D, bool RAW>
 __global__ __launch_bounds__(NW * 64) void route_bf16_kernel(
     const uint16_t* __restrict__ x, const u32x4* __restrict__ gfrag,
     const float* __restrict__ bias, int64_t N, int H, int E, int K, int32_t* __restrict__ ids,
@@ -231,7 +244,9 @@ __global__ __launch_bounds__(NW * 64) void route_bf16_kernel(
   constexpr int ROWP = EP + 4;
   constexpr int ALD = BM / 8;  // A load instructions per step (8 rows x 128 B each)
   constexpr int TILE = BM * 128;
-  constexpr int SMEM_A = NW * TILE;
+  constexpr int GTILE = RAW ? 64 * EP * 2 : 0;  // the wave's gate rows of one step
+  static_assert(!RAW || EP == 64, "the gate tile swizzle is laid out for 64 experts");
+  constexpr int SMEM_A = NW * (TILE + GTILE);
   constexpr int SMEM_P = NW * BM * ROWP * 4;
   static_assert(BM % (4 * NW) == 0, "epilogue maps 4 tokens per wave per pass");
   static_assert((BM * kMaxRouteK + (NW + 1) * kMaxExperts) * 4 <= (SMEM_A > SMEM_P ? SMEM_A : SMEM_P),
@@ -272,7 +287,16 @@ __global__ __launch_bounds__(NW * 64) void route_bf16_kernel(
       const int row = 16 * m + r;
       rofs[m][hf] = row * 128 + (((2 * g + hf) ^ (row & 7)) << 4);
     }
-  char* tile = smem + wid * TILE;
+  char* tile = smem + wid * (TILE + GTILE);
+  char* gtile = tile + TILE;
+  // RAW gate tile: chunk j of lane l is row 8j + l/8, 16-byte chunk l%8 of it;
+  // its quarter (l%8)/2 moves to (l%8)/2 ^ ((l/8) & 3) ^ ((j/2) & 1)
+  const int gw0 = (lane >> 3) * 128 + (((((lane & 7) >> 1) ^ ((lane >> 3) & 3)) << 5) | ((lane & 1) << 4));
+  const int gw1 = (lane >> 3) * 128 + ((((((lane & 7) >> 1) ^ ((lane >> 3) & 3)) ^ 1) << 5) | ((lane & 1) << 4));
+  // transposing reads: lane (g, r) of fragment (q, hf), half t4 reads row
+  // 16g + 8hf + 4t4 + r/4, quarter q ^ ((r/4) & 3) ^ (g & 1), bytes 8(r%4)
+  const int trb = (16 * g + (r >> 2)) * 128 + 8 * (r & 3);
+  const int trs = ((r >> 2) & 3) ^ (g & 1);
 
   f32x4_t acc[MT][NT];
 #pragma unroll
@@ -292,6 +316,8 @@ __global__ __launch_bounds__(NW * 64) void route_bf16_kernel(
   auto load = [&](Buf& bf, int s) {
 #pragma unroll
     for (int j = 0; j < ALD; ++j) bf.a[j] = *reinterpret_cast<const u32x4*>(aptr[j] + s * 64);
+    // packed: fragment (q, hf) of the step; RAW: 1 KiB chunk 2q + hf of the
+    // step's 64 row-major gate rows
     const u32x4* gb = gfrag + (size_t)s * NT * 128 + lane;
 #pragma unroll
     for (int q = 0; q < NT; ++q) {
@@ -313,8 +339,18 @@ __global__ __launch_bounds__(NW * 64) void route_bf16_kernel(
     const u32x4* gb = gfrag + (size_t)s * NT * 128 + lane;
 #pragma unroll
     for (int q = 0; q < NT; ++q) {
-      bf.b[q][0] = gb[(2 * q) * 64];
-      bf.b[q][1] = gb[(2 * q + 1) * 64];
+      if constexpr (RAW) {
+        // rows at or beyond H are zero (chunk 2q + hf holds rows 16q + 8hf + lane/8)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const bool in = s * 64 + 16 * q + 8 * hf + lrow < H;
+          const u32x4 v = gb[in ? (2 * q + hf) * 64 : 0];
+          bf.b[q][hf] = in ? v : zero;
+        }
+      } else {
+        bf.b[q][0] = gb[(2 * q) * 64];
+        bf.b[q][1] = gb[(2 * q + 1) * 64];
+      }
     }
   };
   // A tile through the wave's LDS tile, then MT*NT*2 MFMAs; consecutive
@@ -325,6 +361,15 @@ __global__ __launch_bounds__(NW * 64) void route_bf16_kernel(
   auto mma = [&](const Buf& bf) {
 #pragma unroll
     for (int j = 0; j < ALD; ++j) *reinterpret_cast<u32x4*>(tile + wofs[j]) = bf.a[j];
+    if constexpr (RAW) {
+#pragma unroll
+      for (int q = 0; q < NT; ++q)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const int j = 2 * q + hf;  // rows 8j .. 8j+7
+          *reinterpret_cast<u32x4*>(gtile + 1024 * j + (((j >> 1) & 1) ? gw1 : gw0)) = bf.b[q][hf];
+        }
+    }
     asm volatile("" ::: "memory");
     u32x4 af[MT][2];
 #pragma unroll
@@ -332,6 +377,30 @@ __global__ __launch_bounds__(NW * 64) void route_bf16_kernel(
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf)
         af[m][hf] = *reinterpret_cast<const u32x4*>(tile + rofs[m][hf]);
+    bf16x8_t bfr[NT][2];
+    if constexpr (RAW) {
+      typedef short v4s __attribute__((ext_vector_type(4)));
+#pragma unroll
+      for (int q = 0; q < NT; ++q)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          v4s h2[2];
+#pragma unroll
+          for (int t4 = 0; t4 < 2; ++t4)
+            h2[t4] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) v4s*)(gtile + trb + (8 * hf + 4 * t4) * 128 +
+                                                         ((q ^ trs) << 5)));
+          bfr[q][hf] = __builtin_bit_cast(
+              bf16x8_t, (short __attribute__((ext_vector_type(8)))){h2[0][0], h2[0][1], h2[0][2],
+                                                                     h2[0][3], h2[1][0], h2[1][1],
+                                                                     h2[1][2], h2[1][3]});
+        }
+    } else {
+#pragma unroll
+      for (int q = 0; q < NT; ++q)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) bfr[q][hf] = as_bf16x8(bf.b[q][hf]);
+    }
     asm volatile("" ::: "memory");
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf)
@@ -340,7 +409,7 @@ __global__ __launch_bounds__(NW * 64) void route_bf16_kernel(
 #pragma unroll
         for (int q = 0; q < NT; ++q)
           acc[m][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              as_bf16x8(af[m][hf]), as_bf16x8(bf.b[q][hf]), acc[m][q], 0, 0, 0);
+              as_bf16x8(af[m][hf]), bfr[q][hf], acc[m][q], 0, 0, 0);
   };
 
   // Each workgroup walks its range starting at a different step (rotated by
@@ -845,11 +914,19 @@ template <int NT, int MT, int NW = (NT <= 4 ? MOE_ROUTE_NW : NT == 8 ? MOE_ROUTE
           int D = (NT <= 4 ? MOE_ROUTE_DEPTH : 1)>
 hipError_t launch_bf16_nt(const uint16_t* x, const uint16_t* wgt, const float* bias, int64_t N,
                           int H, int E, int K, int32_t* ids, float* w, int32_t* counts,
-                          int32_t* lrank, int32_t* bhist, hipStream_t s) {
+                          int32_t* lrank, int32_t* bhist, hipStream_t s, bool raw = false) {
   const int64_t blocks = (N + 16 * MT - 1) / (16 * MT);
-  hipLaunchKernelGGL((route_bf16_kernel<NT, MT, NW, D>), dim3((unsigned)blocks), dim3(NW * 64), 0,
-                     s, x, reinterpret_cast<const u32x4*>(wgt), bias, N, H, E, K, ids, w, counts,
-                     lrank, bhist, (int)blocks);
+  if constexpr (NT == 4) {
+    if (raw) {
+      hipLaunchKernelGGL((route_bf16_kernel<NT, MT, NW, D, true>), dim3((unsigned)blocks),
+                         dim3(NW * 64), 0, s, x, reinterpret_cast<const u32x4*>(wgt), bias, N, H,
+                         E, K, ids, w, counts, lrank, bhist, (int)blocks);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((route_bf16_kernel<NT, MT, NW, D, false>), dim3((unsigned)blocks),
+                     dim3(NW * 64), 0, s, x, reinterpret_cast<const u32x4*>(wgt), bias, N, H, E, K,
+                     ids, w, counts, lrank, bhist, (int)blocks);
   return hipGetLastError();
 }
 
@@ -920,9 +997,12 @@ int route_tokens_per_block(int E, int64_t N) {
   return route_small(EP, N) ? 32 : 16 * route_mt(EP);
 }
 
+bool route_gate_raw(int E) { return MOE_ROUTE_RAW_GATE && E == 64; }
+
 hipError_t launch_route_bf16(const uint16_t* x, const uint16_t* wgt, const float* bias, int64_t N,
                              int H, int E, int K, int32_t* ids, float* w, int32_t* counts,
                              int32_t* lrank, int32_t* bhist, hipStream_t s) {
+  const bool raw = route_gate_raw(E);
   switch (route_padded_experts(E)) {
     case 16:
       return launch_bf16_nt<1, route_mt(16)>(x, wgt, bias, N, H, E, K, ids, w, counts, lrank,
@@ -932,11 +1012,12 @@ hipError_t launch_route_bf16(const uint16_t* x, const uint16_t* wgt, const float
                                              bhist, s);
     case 64:
       if (route_tiny64(N))
-        return launch_bf16_nt<4, 1, 4, 1>(x, wgt, bias, N, H, E, K, ids, w, counts, lrank, bhist, s);
+        return launch_bf16_nt<4, 1, 4, 1>(x, wgt, bias, N, H, E, K, ids, w, counts, lrank, bhist, s,
+                                          raw);
       if (route_small(64, N))
-        return launch_bf16_nt<4, 2>(x, wgt, bias, N, H, E, K, ids, w, counts, lrank, bhist, s);
+        return launch_bf16_nt<4, 2>(x, wgt, bias, N, H, E, K, ids, w, counts, lrank, bhist, s, raw);
       return launch_bf16_nt<4, route_mt(64)>(x, wgt, bias, N, H, E, K, ids, w, counts, lrank,
-                                             bhist, s);
+                                             bhist, s, raw);
     case 128:
       if (MOE_ROUTE_ESPLIT128) {
         if (route_small(128, N))

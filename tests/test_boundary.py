@@ -56,10 +56,13 @@ def test_status_strings(lib):
 
 
 def test_workspace_sizes(lib):
-    # bf16 router: expert-major gate padded to a power-of-two multiple of 16
-    for H, E, EP in ((4096, 64, 64), (2048, 128, 128), (256, 20, 32), (8, 1, 16)):
+    # bf16 router: the gate packed fragment-major, padded to a power-of-two
+    # multiple of 16 experts; at exactly 64 experts the router reads gate_w
+    # itself and needs none
+    for H, E, EP in ((2048, 128, 128), (256, 20, 32), (8, 1, 16), (4096, 48, 64)):
         n = lib.moe_route_workspace_size(H, E, BF16)
         assert n >= EP * H * 2 and n % 256 == 0 and n <= EP * (H + 256) * 2 + 256
+    assert lib.moe_route_workspace_size(4096, 64, BF16) == 0
     assert lib.moe_route_workspace_size(256, 16, F32) == 0
     assert lib.moe_route_workspace_size(256, 300, BF16) == 0
     # dispatch: per-block expert histograms (blocks of <= 64 tokens) plus one
@@ -70,8 +73,10 @@ def test_workspace_sizes(lib):
         assert n >= N * K * 4 + -(-N // bt) * E * 4 and n % 256 == 0
     assert lib.moe_dispatch_workspace_size(-1, 3, 2) == 0
     # fused route+dispatch: the router's packed gate plus the dispatch scratch
+    n = lib.moe_route_dispatch_workspace_size(16384, 4096, 128, 2, BF16)
+    assert n >= lib.moe_route_workspace_size(4096, 128, BF16) + 16384 * 2 * 4
     n = lib.moe_route_dispatch_workspace_size(16384, 4096, 64, 2, BF16)
-    assert n >= lib.moe_route_workspace_size(4096, 64, BF16) + 16384 * 2 * 4
+    assert n >= 16384 * 2 * 4 + (16384 // 64) * 64 * 4
     # fp32: no packed gate; the router ranks its own blocks of 16 tokens
     n = lib.moe_route_dispatch_workspace_size(512, 256, 16, 2, F32)
     assert n >= 512 * 2 * 4 + (512 // 16) * 16 * 4 and n % 256 == 0
