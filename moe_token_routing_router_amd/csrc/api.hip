@@ -119,12 +119,17 @@ moe_status_t moe_route(const void* x, const void* gate_w, const float* bias, int
 
 namespace {
 
-// Fused bf16 route+dispatch: up to this many router blocks, the scatter sums
-// the per-block counts itself instead of running the scan kernel.
+// Fused bf16 route+dispatch: up to this many router blocks (and K), the
+// scatter sums the per-block counts and expert prefixes itself instead of
+// running the scan kernel.
 #ifndef MOE_PREFIX_MAX_BLOCKS
 #define MOE_PREFIX_MAX_BLOCKS 512
 #endif
 constexpr int64_t kPrefixMaxBlocks = MOE_PREFIX_MAX_BLOCKS;
+#ifndef MOE_PREFIX_MAX_K
+#define MOE_PREFIX_MAX_K 4
+#endif
+constexpr int kPrefixMaxK = MOE_PREFIX_MAX_K;
 
 // dispatch scratch: bhist [E][blocks of bt tokens] then lrank [N*K]
 size_t bhist_bytes(int64_t N, int32_t E, int bt) {
@@ -196,7 +201,10 @@ size_t moe_route_dispatch_workspace_size(int64_t N, int32_t H, int32_t E, int32_
   if (N < 0 || H <= 0 || E <= 0 || E > moe::kMaxExperts || K < 1 || !valid_dtype(dtype)) return 0;
   const int bt =
       dtype == MOE_BF16 ? moe::route_tokens_per_block(E, N) : moe::kRouteF32Tokens;
-  return moe_route_workspace_size(H, E, dtype) + dispatch_scratch_bytes(N, E, K, bt);
+  // packed gate (if any), block histograms, in-block ranks, then (bf16) the
+  // blocks' expert prefixes
+  return moe_route_workspace_size(H, E, dtype) + dispatch_scratch_bytes(N, E, K, bt) +
+         (dtype == MOE_BF16 ? bhist_bytes(N, E, bt) : 0);
 }
 
 namespace {
@@ -233,26 +241,28 @@ moe_status_t launch_route_dispatch(const void* x, const void* gate_w, const floa
       base + rws + round_up((size_t)moe::dispatch_num_blocks(N, bt) * E * sizeof(int32_t), 256));
   hipError_t e;
   if (dtype == MOE_BF16) {
-    // Few blocks: the pack zeroes counts, the router adds its per-block
-    // histograms into them, and each scatter workgroup sums the blocks before
-    // its own, so no scan kernel runs.  Many blocks: the scan kernel.
-    const bool prefix = moe::dispatch_num_blocks(N, bt) <= kPrefixMaxBlocks && K <= 2;
+    // Few blocks: the router also stores each block's exclusive prefix over
+    // the experts, and each scatter workgroup sums what its slots need
+    // itself, so neither a scan kernel nor zeroed counts are needed.  Many
+    // blocks: the scan kernel.
+    const bool prefix = moe::dispatch_num_blocks(N, bt) <= kPrefixMaxBlocks && K <= kPrefixMaxK;
+    int32_t* bpre = reinterpret_cast<int32_t*>(
+        base + rws + dispatch_scratch_bytes(N, E, K, bt));
     const uint16_t* wgt = reinterpret_cast<const uint16_t*>(gate_w);
-    if (moe::route_gate_raw(E)) {
-      e = prefix ? moe::launch_fill_i32(counts, E, 0, s) : hipSuccess;
-    } else {
+    if (!moe::route_gate_raw(E)) {
       uint16_t* packed = reinterpret_cast<uint16_t*>(workspace);
-      e = moe::launch_gate_transpose(wgt, H, E, packed, prefix ? counts : nullptr, s);
+      e = moe::launch_gate_transpose(wgt, H, E, packed, nullptr, s);
+      if (e != hipSuccess) return MOE_ERR_HIP;
       wgt = packed;
     }
-    if (e != hipSuccess) return MOE_ERR_HIP;
     e = moe::launch_route_bf16(reinterpret_cast<const uint16_t*>(x), wgt, bias, N, H, E, K,
-                               topk_ids, topk_w, prefix ? counts : nullptr, lrank, bhist, s);
+                               topk_ids, topk_w, nullptr, lrank, bhist, s,
+                               prefix ? bpre : nullptr);
     if (e != hipSuccess) return MOE_ERR_HIP;
     if (prefix)
-      return from_hip(moe::launch_dispatch_scatter_prefix(
+      return from_hip(moe::launch_dispatch_scatter_blockpre(
           topk_ids, x, N, (int64_t)H * elem_bytes(dtype), E, K, bt, counts, offsets, perm, inv,
-          x_perm, lrank, bhist, s));
+          x_perm, lrank, bhist, bpre, s));
   } else {
     // the fp32 router ranks its own 16-token blocks: no count kernel
     e = moe::launch_route_f32(reinterpret_cast<const float*>(x),

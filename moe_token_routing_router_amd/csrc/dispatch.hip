@@ -143,20 +143,25 @@ __device__ __forceinline__ int64_t scatter_token(int64_t g, int64_t N, int xbt) 
 // before the index work (they do not depend on it), so the E-wide offset
 // scan and the index arithmetic overlap them.
 // MODE 0: bhist holds the scanned block bases and counts the totals (the
-// scan kernel ran).  MODE 1: bhist holds the raw per-block counts and counts
-// their totals (the fused router added them); each workgroup sums the blocks
-// before its own for the experts of its slots (at most nb entries of one
-// bhist row per slot).  MODE 2: as MODE 1, and every workgroup also sums
-// whole bhist rows for the totals (small bhist only), workgroup 0 storing
-// them to counts.
+// scan kernel ran).  MODE 2: bhist holds the raw per-block counts (small
+// bhist only); each workgroup sums the blocks before its own for the experts
+// of its slots (at most nb entries of one bhist row per slot) and whole bhist
+// rows for the totals, workgroup 0 storing them to counts.
+// MODE 3: bhist holds the raw per-block counts and bpre, per block, the
+// exclusive prefix of the block's histogram over the experts; nothing else is
+// needed.  A slot's position is sum_b bpre[e][b] (the slots of lower experts
+// in every block, i.e. offsets[e]) + sum_{b < its block} bhist[e][b] + its
+// in-block rank: one wave per slot sums both rows, so no counts have to be
+// zeroed or added atomically beforehand and no E-wide scan runs.  The first
+// workgroups also store counts and offsets.
 template <int MODE>
 __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
     const int32_t* __restrict__ ids, int32_t* __restrict__ counts,
     const int32_t* __restrict__ bhist, const int32_t* __restrict__ lrank, int64_t N, int K,
     int E, int nb, int bt, int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
     int32_t* __restrict__ inv, const u32x4* __restrict__ x, u32x4* __restrict__ x_perm,
-    int row_vecs, int64_t dlim, int xbt) {
-  extern __shared__ int dst[];  // [kScatterTokens*K], then (MODE >= 1) red[4][kScatterTokens*K]
+    int row_vecs, int64_t dlim, int xbt, const int32_t* __restrict__ bpre) {
+  extern __shared__ int dst[];  // [kScatterTokens*K], then (MODE >= 2) red[4][kScatterTokens*K]
   __shared__ int off[kMaxExperts];
   __shared__ int scan_lds[4];
   const int tid = threadIdx.x;
@@ -178,7 +183,37 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
 
   const int S = ntok * K;
   const int64_t s0 = n0 * K;
-  if constexpr (MODE >= 1) {
+  if constexpr (MODE == 3) {
+    const int wv = tid >> 6, ln = tid & 63;
+    for (int j = wv; j < S; j += 4) {
+      const int64_t slot = s0 + j;
+      const int e = ids[slot];
+      int part = 0;
+      if ((unsigned)e < (unsigned)E) {
+        const int64_t b0 = (slot / K) / bt;
+        const int32_t* pr = bpre + (int64_t)e * nb;
+        const int32_t* hr = bhist + (int64_t)e * nb;
+        for (int bb = ln; bb < nb; bb += 64) part += pr[bb] + (bb < b0 ? hr[bb] : 0);
+      }
+      part = wave_inclusive_sum(part);
+      if (ln == 63) red[j] = part;
+    }
+    for (int g = blockIdx.x; g < E; g += gridDim.x) {  // uniform in the workgroup
+      int c = 0, o = 0;
+      for (int bb = tid; bb < nb; bb += 256) {
+        c += bhist[(int64_t)g * nb + bb];
+        o += bpre[(int64_t)g * nb + bb];
+      }
+      int ct, ot;
+      block_exclusive_scan_256(c, scan_lds, &ct);
+      block_exclusive_scan_256(o, scan_lds, &ot);
+      if (tid == 0) {
+        counts[g] = ct;
+        offsets[g] = ot;
+        if (g == E - 1) offsets[E] = ot + ct;
+      }
+    }
+  } else if constexpr (MODE == 2) {
     // per slot: the counts of its expert in the blocks before its own (the
     // barriers of the offset scan below publish red)
     for (int j = 0; j < S; ++j) {
@@ -194,7 +229,7 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
   }
 
   // offsets = exclusive scan of counts (E <= 256: one expert per thread)
-  {
+  if constexpr (MODE != 3) {
     int c = 0;
     if constexpr (MODE == 2) {
       if (tid < E) {
@@ -222,10 +257,15 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
     int d = -1;
     if ((unsigned)e < (unsigned)E) {
       const int64_t b = (slot / K) / bt;
-      const int64_t base = MODE >= 1
-                               ? (int64_t)((red[j] + red[S + j]) + red[2 * S + j]) + red[3 * S + j]
-                               : (int64_t)bhist[(int64_t)e * nb + b];
-      const int64_t dd = (int64_t)off[e] + base + lrank[slot];
+      int64_t dd;
+      if constexpr (MODE == 3) {
+        dd = (int64_t)red[j] + lrank[slot];
+      } else {
+        const int64_t base =
+            MODE == 2 ? (int64_t)((red[j] + red[S + j]) + red[2 * S + j]) + red[3 * S + j]
+                      : (int64_t)bhist[(int64_t)e * nb + b];
+        dd = (int64_t)off[e] + base + lrank[slot];
+      }
       if (dd >= 0 && dd < dlim) {  // always true for consistent inputs
         d = (int)dd;
         perm[d] = (int32_t)slot;
@@ -291,21 +331,6 @@ static int scatter_xbt(int64_t N, int router_bt) {
   return N % (8 * (int64_t)router_bt) == 0 ? router_bt : 0;
 }
 
-hipError_t launch_dispatch_scatter_prefix(const int32_t* ids, const void* x, int64_t N,
-                                          int64_t row_bytes, int E, int K, int bt,
-                                          const int32_t* counts, int32_t* offsets, int32_t* perm,
-                                          int32_t* inv, void* x_perm, const int32_t* lrank,
-                                          const int32_t* bhist, hipStream_t s) {
-  const int nb = (int)dispatch_num_blocks(N, bt);
-  const int64_t blocks = (N + kScatterTokens - 1) / kScatterTokens;
-  const size_t dyn = sizeof(int) * 5 * (size_t)kScatterTokens * K;
-  hipLaunchKernelGGL(dispatch_scatter_kernel<1>, dim3((unsigned)blocks), dim3(256), dyn, s, ids,
-                     const_cast<int32_t*>(counts), bhist, lrank, N, K, E, nb, bt, offsets, perm, inv,
-                     reinterpret_cast<const u32x4*>(x), reinterpret_cast<u32x4*>(x_perm),
-                     (int)(row_bytes / 16), N * K, scatter_xbt(N, bt));
-  return hipGetLastError();
-}
-
 hipError_t launch_dispatch_finish(const int32_t* ids, const void* x, int64_t N, int64_t row_bytes,
                                   int E, int K, int bt, int32_t* counts, int32_t* offsets,
                                   int32_t* perm, int32_t* inv, void* x_perm,
@@ -320,7 +345,8 @@ hipError_t launch_dispatch_finish(const int32_t* ids, const void* x, int64_t N, 
     hipLaunchKernelGGL(dispatch_scatter_kernel<2>, dim3((unsigned)blocks), dim3(256), dyn, s, ids,
                        counts, bhist, lrank, N, K, E, nb, bt, offsets, perm, inv,
                        reinterpret_cast<const u32x4*>(x), reinterpret_cast<u32x4*>(x_perm),
-                       (int)(row_bytes / 16), dlim, scatter_xbt(N, router_bt));
+                       (int)(row_bytes / 16), dlim, scatter_xbt(N, router_bt),
+                       (const int32_t*)nullptr);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(dispatch_scan_kernel, dim3(E), dim3(256), 0, s, bhist, nb, counts, E,
@@ -331,7 +357,24 @@ hipError_t launch_dispatch_finish(const int32_t* ids, const void* x, int64_t N, 
   hipLaunchKernelGGL(dispatch_scatter_kernel<0>, dim3((unsigned)blocks), dim3(256), dyn, s, ids,
                      counts, bhist, lrank, N, K, E, nb, bt, offsets, perm, inv,
                      reinterpret_cast<const u32x4*>(x), reinterpret_cast<u32x4*>(x_perm),
-                     (int)(row_bytes / 16), dlim, scatter_xbt(N, router_bt));
+                     (int)(row_bytes / 16), dlim, scatter_xbt(N, router_bt),
+                     (const int32_t*)nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_dispatch_scatter_blockpre(const int32_t* ids, const void* x, int64_t N,
+                                            int64_t row_bytes, int E, int K, int bt,
+                                            int32_t* counts, int32_t* offsets, int32_t* perm,
+                                            int32_t* inv, void* x_perm, const int32_t* lrank,
+                                            const int32_t* bhist, const int32_t* bpre,
+                                            hipStream_t s) {
+  const int nb = (int)dispatch_num_blocks(N, bt);
+  const int64_t blocks = (N + kScatterTokens - 1) / kScatterTokens;
+  const size_t dyn = sizeof(int) * 5 * (size_t)kScatterTokens * K;
+  hipLaunchKernelGGL(dispatch_scatter_kernel<3>, dim3((unsigned)blocks), dim3(256), dyn, s, ids,
+                     counts, bhist, lrank, N, K, E, nb, bt, offsets, perm, inv,
+                     reinterpret_cast<const u32x4*>(x), reinterpret_cast<u32x4*>(x_perm),
+                     (int)(row_bytes / 16), N * K, scatter_xbt(N, bt), bpre);
   return hipGetLastError();
 }
 

@@ -178,9 +178,12 @@ int route_tokens_per_block(int E, int64_t N);  // tokens per router workgroup
 bool route_gate_raw(int E);
 hipError_t launch_gate_transpose(const uint16_t* gate_w, int H, int E, uint16_t* wgt,
                                  int32_t* counts, hipStream_t s);
+// bpre (fused path, optional): each block's exclusive prefix of its histogram
+// over the experts, [E][blocks], for launch_dispatch_scatter_blockpre.
 hipError_t launch_route_bf16(const uint16_t* x, const uint16_t* wgt, const float* bias,
                              int64_t N, int H, int E, int K, int32_t* ids, float* w,
-                             int32_t* counts, int32_t* lrank, int32_t* bhist, hipStream_t s);
+                             int32_t* counts, int32_t* lrank, int32_t* bhist, hipStream_t s,
+                             int32_t* bpre = nullptr);
 // The fp32 router works on blocks of kRouteF32Tokens tokens; with lrank it
 // ranks its own picks per block like the bf16 router.
 constexpr int kRouteF32Tokens = 16;
@@ -210,15 +213,15 @@ hipError_t launch_dispatch_finish(const int32_t* ids, const void* x, int64_t N, 
                                   const int32_t* lrank, int32_t* bhist, int64_t dlim,
                                   hipStream_t s, int router_bt = 0);
 
-// scatter only, for the fused path: bhist holds raw per-block counts and
-// counts their totals (the router's atomic histogram); each scatter
-// workgroup sums the blocks before its own.  Tokens in the router's XCD
-// order (blocks of bt tokens).
-hipError_t launch_dispatch_scatter_prefix(const int32_t* ids, const void* x, int64_t N,
-                                          int64_t row_bytes, int E, int K, int bt,
-                                          const int32_t* counts, int32_t* offsets, int32_t* perm,
-                                          int32_t* inv, void* x_perm, const int32_t* lrank,
-                                          const int32_t* bhist, hipStream_t s);
+// scatter only: bhist holds raw per-block counts (blocks of bt tokens) and
+// bpre each block's exclusive prefix over the experts (both from the router's
+// epilogue); writes counts and offsets too.  Tokens in the router's XCD order.
+hipError_t launch_dispatch_scatter_blockpre(const int32_t* ids, const void* x, int64_t N,
+                                            int64_t row_bytes, int E, int K, int bt,
+                                            int32_t* counts, int32_t* offsets, int32_t* perm,
+                                            int32_t* inv, void* x_perm, const int32_t* lrank,
+                                            const int32_t* bhist, const int32_t* bpre,
+                                            hipStream_t s);
 
 // Scan of `rows` bhist rows of nb blocks (in place, exclusive); the totals
 // of rows below `split` go to counts[row], the others to counts2[row - split].

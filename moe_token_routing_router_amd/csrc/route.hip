@@ -199,6 +199,28 @@ __device__ __forceinline__ void select_topk_store(const float (&v)[U][NT], int r
   }
 }
 
+// bpre[e * nb + b] = sum over experts e' < e of rhist[e'], for e < E <= 256:
+// the exclusive prefix of block b's histogram over the experts (the fused
+// dispatch's scatter adds these up over the blocks to get the expert
+// offsets).  The first four waves scan; every thread of the workgroup must
+// call it; wsum needs 4 ints of LDS.
+__device__ __forceinline__ void store_expert_prefix(const int* rhist, int E, int32_t* bpre, int nb,
+                                                    int b, int* wsum) {
+  const int tid = threadIdx.x;
+  int v = 0, incl = 0;
+  if (tid < 256) {
+    v = tid < E ? rhist[tid] : 0;
+    incl = wave_inclusive_sum(v);
+    if ((tid & 63) == 63) wsum[tid >> 6] = incl;
+  }
+  __syncthreads();
+  if (tid < E) {
+    int base = 0;
+    for (int w = 0; w < (tid >> 6); ++w) base += wsum[w];
+    bpre[(int64_t)tid * nb + b] = base + incl - v;
+  }
+}
+
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4 u) {
   return __builtin_bit_cast(bf16x8_t, u);
 }
@@ -238,7 +260,8 @@ __global__ __launch_bounds__(NW * 64) void route_bf16_kernel(
     const uint16_t* __restrict__ x, const u32x4* __restrict__ gfrag,
     const float* __restrict__ bias, int64_t N, int H, int E, int K, int32_t* __restrict__ ids,
     float* __restrict__ topw, int32_t* __restrict__ counts, int32_t* __restrict__ lrank,
-    int32_t* __restrict__ bhist, int nb) {
+    int32_t* __restrict__ bhist, int nb,
+    int32_t* __restrict__ bpre) {
   constexpr int BM = 16 * MT;
   constexpr int EP = 16 * NT;
   constexpr int ROWP = EP + 4;
@@ -528,6 +551,7 @@ __global__ __launch_bounds__(NW * 64) void route_bf16_kernel(
     const int ntok = (int)min((int64_t)BM, N - t0);
     block_stable_rank<NW>(sids, ntok * K, E, lrank + t0 * K, rhist, wcnt);
     for (int e = tid; e < E; e += NW * 64) bhist[(int64_t)e * nb + blockIdx.x] = rhist[e];
+    if (bpre) store_expert_prefix(rhist, E, bpre, nb, blockIdx.x, hist);
   }
 
   if (counts) {
@@ -553,7 +577,8 @@ __global__ __launch_bounds__(NW * 64) void route_bf16_esplit_kernel(
     const uint16_t* __restrict__ x, const u32x4* __restrict__ gfrag,
     const float* __restrict__ bias, int64_t N, int H, int E, int K, int32_t* __restrict__ ids,
     float* __restrict__ topw, int32_t* __restrict__ counts, int32_t* __restrict__ lrank,
-    int32_t* __restrict__ bhist, int nb) {
+    int32_t* __restrict__ bhist, int nb,
+    int32_t* __restrict__ bpre) {
   constexpr int BM = 16 * MT;
   constexpr int EP = 16 * NT;
   constexpr int NTW = NT / NW;   // expert tiles per wave
@@ -764,6 +789,7 @@ __global__ __launch_bounds__(NW * 64) void route_bf16_esplit_kernel(
     const int ntok = (int)min((int64_t)BM, N - t0);
     block_stable_rank<NW>(sids, ntok * K, E, lrank + t0 * K, rhist, wcnt);
     for (int e = tid; e < E; e += NW * 64) bhist[(int64_t)e * nb + blockIdx.x] = rhist[e];
+    if (bpre) store_expert_prefix(rhist, E, bpre, nb, blockIdx.x, hist);
   }
 
   if (counts) {
@@ -902,11 +928,11 @@ __global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
 template <int NT, int MT, int NW>
 hipError_t launch_bf16_esplit(const uint16_t* x, const uint16_t* wgt, const float* bias, int64_t N,
                               int H, int E, int K, int32_t* ids, float* w, int32_t* counts,
-                              int32_t* lrank, int32_t* bhist, hipStream_t s) {
+                              int32_t* lrank, int32_t* bhist, int32_t* bpre, hipStream_t s) {
   const int64_t blocks = (N + 16 * MT - 1) / (16 * MT);
   hipLaunchKernelGGL((route_bf16_esplit_kernel<NT, MT, NW>), dim3((unsigned)blocks),
                      dim3(NW * 64), 0, s, x, reinterpret_cast<const u32x4*>(wgt), bias, N, H, E,
-                     K, ids, w, counts, lrank, bhist, (int)blocks);
+                     K, ids, w, counts, lrank, bhist, (int)blocks, bpre);
   return hipGetLastError();
 }
 
@@ -914,19 +940,20 @@ template <int NT, int MT, int NW = (NT <= 4 ? MOE_ROUTE_NW : NT == 8 ? MOE_ROUTE
           int D = (NT <= 4 ? MOE_ROUTE_DEPTH : 1)>
 hipError_t launch_bf16_nt(const uint16_t* x, const uint16_t* wgt, const float* bias, int64_t N,
                           int H, int E, int K, int32_t* ids, float* w, int32_t* counts,
-                          int32_t* lrank, int32_t* bhist, hipStream_t s, bool raw = false) {
+                          int32_t* lrank, int32_t* bhist, int32_t* bpre, hipStream_t s,
+                          bool raw = false) {
   const int64_t blocks = (N + 16 * MT - 1) / (16 * MT);
   if constexpr (NT == 4) {
     if (raw) {
       hipLaunchKernelGGL((route_bf16_kernel<NT, MT, NW, D, true>), dim3((unsigned)blocks),
                          dim3(NW * 64), 0, s, x, reinterpret_cast<const u32x4*>(wgt), bias, N, H,
-                         E, K, ids, w, counts, lrank, bhist, (int)blocks);
+                         E, K, ids, w, counts, lrank, bhist, (int)blocks, bpre);
       return hipGetLastError();
     }
   }
   hipLaunchKernelGGL((route_bf16_kernel<NT, MT, NW, D, false>), dim3((unsigned)blocks),
                      dim3(NW * 64), 0, s, x, reinterpret_cast<const u32x4*>(wgt), bias, N, H, E, K,
-                     ids, w, counts, lrank, bhist, (int)blocks);
+                     ids, w, counts, lrank, bhist, (int)blocks, bpre);
   return hipGetLastError();
 }
 
@@ -1001,45 +1028,45 @@ bool route_gate_raw(int E) { return MOE_ROUTE_RAW_GATE && E == 64; }
 
 hipError_t launch_route_bf16(const uint16_t* x, const uint16_t* wgt, const float* bias, int64_t N,
                              int H, int E, int K, int32_t* ids, float* w, int32_t* counts,
-                             int32_t* lrank, int32_t* bhist, hipStream_t s) {
+                             int32_t* lrank, int32_t* bhist, hipStream_t s, int32_t* bpre) {
   const bool raw = route_gate_raw(E);
   switch (route_padded_experts(E)) {
     case 16:
       return launch_bf16_nt<1, route_mt(16)>(x, wgt, bias, N, H, E, K, ids, w, counts, lrank,
-                                             bhist, s);
+                                             bhist, bpre, s);
     case 32:
       return launch_bf16_nt<2, route_mt(32)>(x, wgt, bias, N, H, E, K, ids, w, counts, lrank,
-                                             bhist, s);
+                                             bhist, bpre, s);
     case 64:
       if (route_tiny64(N))
-        return launch_bf16_nt<4, 1, 4, 1>(x, wgt, bias, N, H, E, K, ids, w, counts, lrank, bhist, s,
+        return launch_bf16_nt<4, 1, 4, 1>(x, wgt, bias, N, H, E, K, ids, w, counts, lrank, bhist, bpre, s,
                                           raw);
       if (route_small(64, N))
-        return launch_bf16_nt<4, 2>(x, wgt, bias, N, H, E, K, ids, w, counts, lrank, bhist, s, raw);
+        return launch_bf16_nt<4, 2>(x, wgt, bias, N, H, E, K, ids, w, counts, lrank, bhist, bpre, s, raw);
       return launch_bf16_nt<4, route_mt(64)>(x, wgt, bias, N, H, E, K, ids, w, counts, lrank,
-                                             bhist, s, raw);
+                                             bhist, bpre, s, raw);
     case 128:
       if (MOE_ROUTE_ESPLIT128) {
         if (route_small(128, N))
           return launch_bf16_esplit<8, 2, 4>(x, wgt, bias, N, H, E, K, ids, w, counts, lrank,
-                                             bhist, s);
+                                             bhist, bpre, s);
         return launch_bf16_esplit<8, route_mt(128), 4>(x, wgt, bias, N, H, E, K, ids, w, counts,
-                                                       lrank, bhist, s);
+                                                       lrank, bhist, bpre, s);
       }
       if (route_small(128, N))
-        return launch_bf16_nt<8, 2>(x, wgt, bias, N, H, E, K, ids, w, counts, lrank, bhist, s);
+        return launch_bf16_nt<8, 2>(x, wgt, bias, N, H, E, K, ids, w, counts, lrank, bhist, bpre, s);
       return launch_bf16_nt<8, route_mt(128)>(x, wgt, bias, N, H, E, K, ids, w, counts, lrank,
-                                              bhist, s);
+                                              bhist, bpre, s);
     case 256:
       if (route_esplit256(N)) {
         if (N < kRouteSmallN)
           return launch_bf16_esplit<16, 2, 4>(x, wgt, bias, N, H, E, K, ids, w, counts, lrank,
-                                              bhist, s);
+                                              bhist, bpre, s);
         return launch_bf16_esplit<16, 4, 4>(x, wgt, bias, N, H, E, K, ids, w, counts, lrank,
-                                            bhist, s);
+                                            bhist, bpre, s);
       }
       return launch_bf16_nt<16, route_mt(256), 4>(x, wgt, bias, N, H, E, K, ids, w, counts,
-                                                  lrank, bhist, s);
+                                                  lrank, bhist, bpre, s);
   }
   return hipErrorInvalidValue;
 }
