@@ -165,7 +165,9 @@ moe_status_t zero_counts_offsets(int32_t* counts, int32_t* offsets, int32_t E, h
 
 size_t moe_dispatch_workspace_size(int64_t N, int32_t E, int32_t K) {
   if (N < 0 || E <= 0 || E > moe::kMaxExperts || K < 1) return 0;
-  return dispatch_scratch_bytes(N, E, K, moe::dispatch_count_tokens(K));
+  // block histograms, in-block ranks, the blocks' expert prefixes
+  const int bt = moe::dispatch_count_tokens(K);
+  return dispatch_scratch_bytes(N, E, K, bt) + bhist_bytes(N, E, bt);
 }
 
 moe_status_t moe_dispatch(const int32_t* topk_ids, const void* x, int64_t N, int32_t H, int32_t E,
@@ -186,14 +188,27 @@ moe_status_t moe_dispatch(const int32_t* topk_ids, const void* x, int64_t N, int
   int32_t* lrank = reinterpret_cast<int32_t*>(
       reinterpret_cast<char*>(workspace) +
       round_up((size_t)moe::dispatch_num_blocks(N, bt) * E * sizeof(int32_t), 256));
-  hipError_t e = moe::launch_dispatch_count(topk_ids, N, E, K, lrank, bhist, s);
-  if (e != hipSuccess) return MOE_ERR_HIP;
   // the usual caller has just run the bf16 router over x: scatter in its
   // XCD order
   const int router_bt = dtype == MOE_BF16 ? moe::route_tokens_per_block(E, N) : 0;
-  return from_hip(moe::launch_dispatch_finish(topk_ids, x, N, (int64_t)H * elem_bytes(dtype), E, K,
-                                              bt, counts, offsets, perm, inv, x_perm, lrank,
-                                              bhist, s, router_bt));
+  const int64_t row_bytes = (int64_t)H * elem_bytes(dtype);
+  const int64_t nb = moe::dispatch_num_blocks(N, bt);
+  if (moe::dispatch_needs_scan(nb, E) && nb <= kPrefixMaxBlocks && K <= kPrefixMaxK) {
+    // instead of the scan kernel: the count kernel also stores each block's
+    // prefix over the experts and the scatter sums what its slots need
+    int32_t* bpre = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(workspace) +
+                                               dispatch_scratch_bytes(N, E, K, bt));
+    hipError_t e = moe::launch_dispatch_count(topk_ids, N, E, K, lrank, bhist, s, bpre);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    return from_hip(moe::launch_dispatch_scatter_blockpre(topk_ids, x, N, row_bytes, E, K, bt,
+                                                          counts, offsets, perm, inv, x_perm,
+                                                          lrank, bhist, bpre, s, router_bt));
+  }
+  hipError_t e = moe::launch_dispatch_count(topk_ids, N, E, K, lrank, bhist, s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  return from_hip(moe::launch_dispatch_finish(topk_ids, x, N, row_bytes, E, K, bt, counts,
+                                              offsets, perm, inv, x_perm, lrank, bhist, s,
+                                              router_bt));
 }
 
 size_t moe_route_dispatch_workspace_size(int64_t N, int32_t H, int32_t E, int32_t K,

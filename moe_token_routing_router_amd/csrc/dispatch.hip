@@ -81,13 +81,17 @@ __device__ __forceinline__ void st_row(u32x4* p, u32x4 v) {
 #endif
 }
 
+// With bpre, also each block's exclusive prefix of its histogram over the
+// experts (for the scan-free scatter, MODE 3).
 __global__ __launch_bounds__(256) void dispatch_count_kernel(const int32_t* __restrict__ ids,
                                                              int64_t N, int K, int E, int bt,
                                                              int nb, int32_t* __restrict__ lrank,
-                                                             int32_t* __restrict__ bhist) {
+                                                             int32_t* __restrict__ bhist,
+                                                             int32_t* __restrict__ bpre) {
   extern __shared__ int sids[];  // [bt*K]
   __shared__ int hist[kMaxExperts];
   __shared__ int wcnt[4 * kMaxExperts];
+  __shared__ int wsum[4];
   const int tid = threadIdx.x;
   const int64_t n0 = (int64_t)blockIdx.x * bt;
   const int ntok = (int)min((int64_t)bt, N - n0);
@@ -96,6 +100,7 @@ __global__ __launch_bounds__(256) void dispatch_count_kernel(const int32_t* __re
   for (int j = tid; j < S; j += 256) sids[j] = ids[s0 + j];
   block_stable_rank<4>(sids, S, E, lrank + s0, hist, wcnt);
   for (int e = tid; e < E; e += 256) bhist[(int64_t)e * nb + blockIdx.x] = hist[e];
+  if (bpre) store_expert_prefix(hist, E, bpre, nb, blockIdx.x, wsum);
 }
 
 // rows below `split` total into counts[row], the others into counts2[row - split]
@@ -305,13 +310,15 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
 
 int64_t dispatch_num_blocks(int64_t N, int bt) { return (N + bt - 1) / bt; }
 
+bool dispatch_needs_scan(int64_t nb, int E) { return nb * E > kSumAllMaxInts; }
+
 hipError_t launch_dispatch_count(const int32_t* ids, int64_t N, int E, int K, int32_t* lrank,
-                                 int32_t* bhist, hipStream_t s) {
+                                 int32_t* bhist, hipStream_t s, int32_t* bpre) {
   const int bt = dispatch_count_tokens(K);
   const int nb = (int)dispatch_num_blocks(N, bt);
   const size_t dyn = sizeof(int) * (size_t)bt * K;
   hipLaunchKernelGGL(dispatch_count_kernel, dim3(nb), dim3(256), dyn, s, ids, N, K, E, bt, nb,
-                     lrank, bhist);
+                     lrank, bhist, bpre);
   return hipGetLastError();
 }
 
@@ -367,14 +374,15 @@ hipError_t launch_dispatch_scatter_blockpre(const int32_t* ids, const void* x, i
                                             int32_t* counts, int32_t* offsets, int32_t* perm,
                                             int32_t* inv, void* x_perm, const int32_t* lrank,
                                             const int32_t* bhist, const int32_t* bpre,
-                                            hipStream_t s) {
+                                            hipStream_t s, int router_bt) {
   const int nb = (int)dispatch_num_blocks(N, bt);
   const int64_t blocks = (N + kScatterTokens - 1) / kScatterTokens;
   const size_t dyn = sizeof(int) * 5 * (size_t)kScatterTokens * K;
   hipLaunchKernelGGL(dispatch_scatter_kernel<3>, dim3((unsigned)blocks), dim3(256), dyn, s, ids,
                      counts, bhist, lrank, N, K, E, nb, bt, offsets, perm, inv,
                      reinterpret_cast<const u32x4*>(x), reinterpret_cast<u32x4*>(x_perm),
-                     (int)(row_bytes / 16), N * K, scatter_xbt(N, bt), bpre);
+                     (int)(row_bytes / 16), N * K, scatter_xbt(N, router_bt < 0 ? bt : router_bt),
+                     bpre);
   return hipGetLastError();
 }
 

@@ -166,6 +166,28 @@ __device__ __forceinline__ void block_stable_rank(const int* sids, int S, int E,
   }
 }
 
+// bpre[e * nb + b] = sum over experts e' < e of rhist[e'], for e < E <= 256:
+// the exclusive prefix of block b's histogram over the experts (the
+// dispatch's scatter adds these up over the blocks to get the expert
+// offsets).  The first four waves scan; every thread of the workgroup must
+// call it; wsum needs 4 ints of LDS.
+__device__ __forceinline__ void store_expert_prefix(const int* rhist, int E, int32_t* bpre, int nb,
+                                                    int b, int* wsum) {
+  const int tid = threadIdx.x;
+  int v = 0, incl = 0;
+  if (tid < 256) {
+    v = tid < E ? rhist[tid] : 0;
+    incl = wave_inclusive_sum(v);
+    if ((tid & 63) == 63) wsum[tid >> 6] = incl;
+  }
+  __syncthreads();
+  if (tid < E) {
+    int base = 0;
+    for (int w = 0; w < (tid >> 6); ++w) base += wsum[w];
+    bpre[(int64_t)tid * nb + b] = base + incl - v;
+  }
+}
+
 // ---- launchers (each validates nothing: the C ABI layer has done it) -----
 // Router.  wgt is the fragment-major packed gate (bf16 path only).  When
 // lrank is not null the router also ranks its own selections for the dispatch
@@ -197,8 +219,13 @@ hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
 // finish: scan of bhist (in place) + counts, then scatter (offsets, inv,
 // perm, rows).
 int64_t dispatch_num_blocks(int64_t N, int bt);
+// True when launch_dispatch_finish would run the scan kernel (the scatter
+// sums a block histogram of nb blocks x E experts itself only when it is
+// small).
+bool dispatch_needs_scan(int64_t nb, int E);
+// bpre (optional): each block's exclusive prefix over the experts, [E][nb].
 hipError_t launch_dispatch_count(const int32_t* ids, int64_t N, int E, int K, int32_t* lrank,
-                                 int32_t* bhist, hipStream_t s);
+                                 int32_t* bhist, hipStream_t s, int32_t* bpre = nullptr);
 // router_bt > 0: x was just read by the router in blocks of that many
 // tokens; the scatter then takes its tokens in the router's XCD order.
 hipError_t launch_dispatch_finish(const int32_t* ids, const void* x, int64_t N, int64_t row_bytes,
@@ -214,14 +241,16 @@ hipError_t launch_dispatch_finish(const int32_t* ids, const void* x, int64_t N, 
                                   hipStream_t s, int router_bt = 0);
 
 // scatter only: bhist holds raw per-block counts (blocks of bt tokens) and
-// bpre each block's exclusive prefix over the experts (both from the router's
-// epilogue); writes counts and offsets too.  Tokens in the router's XCD order.
+// bpre each block's exclusive prefix over the experts (from the router's
+// epilogue or the count kernel); writes counts and offsets too.  Tokens in
+// the XCD order of a router that read x in blocks of router_bt tokens (-1:
+// bt).
 hipError_t launch_dispatch_scatter_blockpre(const int32_t* ids, const void* x, int64_t N,
                                             int64_t row_bytes, int E, int K, int bt,
                                             int32_t* counts, int32_t* offsets, int32_t* perm,
                                             int32_t* inv, void* x_perm, const int32_t* lrank,
                                             const int32_t* bhist, const int32_t* bpre,
-                                            hipStream_t s);
+                                            hipStream_t s, int router_bt = -1);
 
 // Scan of `rows` bhist rows of nb blocks (in place, exclusive); the totals
 // of rows below `split` go to counts[row], the others to counts2[row - split].

@@ -199,28 +199,6 @@ __device__ __forceinline__ void select_topk_store(const float (&v)[U][NT], int r
   }
 }
 
-// bpre[e * nb + b] = sum over experts e' < e of rhist[e'], for e < E <= 256:
-// the exclusive prefix of block b's histogram over the experts (the fused
-// dispatch's scatter adds these up over the blocks to get the expert
-// offsets).  The first four waves scan; every thread of the workgroup must
-// call it; wsum needs 4 ints of LDS.
-__device__ __forceinline__ void store_expert_prefix(const int* rhist, int E, int32_t* bpre, int nb,
-                                                    int b, int* wsum) {
-  const int tid = threadIdx.x;
-  int v = 0, incl = 0;
-  if (tid < 256) {
-    v = tid < E ? rhist[tid] : 0;
-    incl = wave_inclusive_sum(v);
-    if ((tid & 63) == 63) wsum[tid >> 6] = incl;
-  }
-  __syncthreads();
-  if (tid < E) {
-    int base = 0;
-    for (int w = 0; w < (tid >> 6); ++w) base += wsum[w];
-    bpre[(int64_t)tid * nb + b] = base + incl - v;
-  }
-}
-
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4 u) {
   return __builtin_bit_cast(bf16x8_t, u);
 }
