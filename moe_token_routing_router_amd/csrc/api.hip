@@ -463,7 +463,7 @@ moe_status_t moe_dispatch_backward(const void* dx_perm, const int32_t* inv, int6
 namespace {
 
 struct RouteBwdLayout {
-  size_t gate_t, dlsel, chunk_base, part, part_b, total;
+  size_t gate_t, part, part_b, total;
 };
 
 RouteBwdLayout route_bwd_layout(int64_t N, int32_t H, int32_t E, int32_t K, moe_dtype_t dtype) {
@@ -471,9 +471,7 @@ RouteBwdLayout route_bwd_layout(int64_t N, int32_t H, int32_t E, int32_t K, moe_
   const int64_t chunks = moe::route_bwd_max_chunks(T, E);
   RouteBwdLayout l;
   l.gate_t = 0;
-  l.dlsel = l.gate_t + round_up((size_t)E * (size_t)H * elem_bytes(dtype), 256);
-  l.chunk_base = l.dlsel + round_up((size_t)T * sizeof(float), 256);
-  l.part = l.chunk_base + round_up(((size_t)E + 1) * sizeof(int32_t), 256);
+  l.part = l.gate_t + round_up((size_t)E * (size_t)H * elem_bytes(dtype), 256);
   l.part_b = l.part + round_up((size_t)chunks * (size_t)H * sizeof(float), 256);
   l.total = l.part_b + round_up((size_t)chunks * sizeof(float), 256);
   return l;
@@ -522,7 +520,6 @@ moe_status_t moe_route_backward(const void* x_perm, const void* gate_w, const in
   return from_hip(moe::launch_route_backward(
       x_perm, gate_w, topk_ids, topk_w, dtopk_w, perm, offsets, inv, dx_perm, N, H, E, K,
       dtype == MOE_BF16, dgate_w, dbias, dx, base + l.gate_t,
-      reinterpret_cast<float*>(base + l.dlsel), reinterpret_cast<int32_t*>(base + l.chunk_base),
       reinterpret_cast<float*>(base + l.part), reinterpret_cast<float*>(base + l.part_b), s));
 }
 

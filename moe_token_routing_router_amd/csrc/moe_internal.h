@@ -283,15 +283,15 @@ hipError_t launch_grouped_linear(const void* x_perm, const void* weight, const i
 hipError_t launch_combine_backward(const void* dout, const void* y, const int32_t* inv,
                                    const float* w, int64_t N, int H, int K, bool bf16, void* dy,
                                    float* dw, hipStream_t s);
-// Router backward workspace: gate_t [E][H] (dtype), dlsel [N*K] fp32, chunk
-// bases [E+1] int32, partials [route_bwd_max_chunks][H] fp32, bias partials
-// [route_bwd_max_chunks] fp32 -- laid out by the caller from these sizes.
+// Router backward workspace: gate_t [E][H] (dtype), partials
+// [route_bwd_max_chunks][H] fp32, bias partials [route_bwd_max_chunks] fp32
+// -- laid out by the caller from these sizes.
 int64_t route_bwd_max_chunks(int64_t T, int E);
 hipError_t launch_route_backward(const void* x_perm, const void* gate_w, const int32_t* ids,
                                  const float* w, const float* dw, const int32_t* perm,
                                  const int32_t* offsets, const int32_t* inv, const void* dx_perm,
                                  int64_t N, int H, int E, int K, bool bf16, float* dgate_w,
-                                 float* dbias, void* dx, void* gate_t, float* dlsel,
-                                 int32_t* chunk_base, float* part, float* part_b, hipStream_t s);
+                                 float* dbias, void* dx, void* gate_t, float* part, float* part_b,
+                                 hipStream_t s);
 
 }  // namespace moe

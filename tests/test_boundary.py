@@ -280,10 +280,12 @@ def test_backward_validation(lib):
     assert rb(xp=MIS8) == MISALIGNED
     assert rb(dbias=MIS) == MISALIGNED
     assert rb(wsb=64) == WS_SMALL
-    # workspace: the expert-major gate, dl, chunk bases, and one fp32 row of
-    # partials per chunk of 32 dispatched rows (plus one per expert)
+    # workspace: the expert-major gate and one fp32 row of partials per range
+    # of dispatched rows (32..256 rows, about 512 ranges) plus one per expert
     n = lib.moe_route_backward_workspace_size(16384, 4096, 64, 2, BF16)
-    assert n >= 64 * 4096 * 2 + 32768 * 4 + (32768 // 32 + 64) * 4096 * 4
+    assert n >= 64 * 4096 * 2 + (32768 // 64 + 64) * 4096 * 4
+    n_small = lib.moe_route_backward_workspace_size(1000, 64, 8, 2, BF16)
+    assert n_small >= 8 * 64 * 2 + (-(-2000 // 32) + 8) * 64 * 4
     assert lib.moe_route_backward_workspace_size(16, 64, 8, 9, BF16) == 0
 
 
