@@ -995,8 +995,14 @@ constexpr int64_t kRouteTinyN = 256 * 16;
 static bool route_tiny64(int64_t N) { return N <= kRouteTinyN; }
 static bool route_esplit256(int64_t N) { return MOE_ROUTE_ESPLIT256 && N >= kRoute256SplitN; }
 
+#ifndef MOE_ROUTE_ESPLIT128_BIG
+#define MOE_ROUTE_ESPLIT128_BIG 1  // 65..128 experts from 2*kRouteSmallN tokens: 128-token, 8-wave tiles
+#endif
+static bool route_esplit128_big(int64_t N) { return MOE_ROUTE_ESPLIT128_BIG && N >= 2 * kRouteSmallN; }
+
 int route_tokens_per_block(int E, int64_t N) {
   const int EP = route_padded_experts(E);
+  if (EP == 128 && MOE_ROUTE_ESPLIT128 && route_esplit128_big(N)) return 128;
   if (EP == 64 && route_tiny64(N)) return 16;
   if (EP == 256 && route_esplit256(N)) return N < kRouteSmallN ? 32 : 64;
   return route_small(EP, N) ? 32 : 16 * route_mt(EP);
@@ -1025,6 +1031,9 @@ hipError_t launch_route_bf16(const uint16_t* x, const uint16_t* wgt, const float
                                              bhist, bpre, s, raw);
     case 128:
       if (MOE_ROUTE_ESPLIT128) {
+        if (route_esplit128_big(N))
+          return launch_bf16_esplit<8, 8, 8>(x, wgt, bias, N, H, E, K, ids, w, counts, lrank,
+                                             bhist, bpre, s);
         if (route_small(128, N))
           return launch_bf16_esplit<8, 2, 4>(x, wgt, bias, N, H, E, K, ids, w, counts, lrank,
                                              bhist, bpre, s);
