@@ -98,9 +98,12 @@ __global__ __launch_bounds__(256) void dispatch_count_kernel(const int32_t* __re
   const int S = ntok * K;
   const int64_t s0 = n0 * K;
   for (int j = tid; j < S; j += 256) sids[j] = ids[s0 + j];
+  if (bpre) {  // the scatter ranks each slot itself: histogram and prefix only
+    block_hist_prefix<256>(sids, S, E, hist, bhist, bpre, nb, blockIdx.x, wsum);
+    return;
+  }
   block_stable_rank<4>(sids, S, E, lrank + s0, hist, wcnt);
   for (int e = tid; e < E; e += 256) bhist[(int64_t)e * nb + blockIdx.x] = hist[e];
-  if (bpre) store_expert_prefix(hist, E, bpre, nb, blockIdx.x, wsum);
 }
 
 // rows below `split` total into counts[row], the others into counts2[row - split]
@@ -154,11 +157,12 @@ __device__ __forceinline__ int64_t scatter_token(int64_t g, int64_t N, int xbt) 
 // rows for the totals, workgroup 0 storing them to counts.
 // MODE 3: bhist holds the raw per-block counts and bpre, per block, the
 // exclusive prefix of the block's histogram over the experts; nothing else is
-// needed.  A slot's position is sum_b bpre[e][b] (the slots of lower experts
-// in every block, i.e. offsets[e]) + sum_{b < its block} bhist[e][b] + its
-// in-block rank: one wave per slot sums both rows, so no counts have to be
-// zeroed or added atomically beforehand and no E-wide scan runs.  The first
-// workgroups also store counts and offsets.
+// needed (no in-block ranks).  A slot's position is sum_b bpre[e][b] (the
+// slots of lower experts in every block, i.e. offsets[e]) + sum_{b < its
+// block} bhist[e][b] + the number of earlier slots of its block with the
+// same id: one wave per slot sums all three, so no counts have to be zeroed
+// or added atomically beforehand, no E-wide scan runs and nobody ranks the
+// blocks in advance.  The first workgroups also store counts and offsets.
 template <int MODE>
 __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
     const int32_t* __restrict__ ids, int32_t* __restrict__ counts,
@@ -199,6 +203,8 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
         const int32_t* pr = bpre + (int64_t)e * nb;
         const int32_t* hr = bhist + (int64_t)e * nb;
         for (int bb = ln; bb < nb; bb += 64) part += pr[bb] + (bb < b0 ? hr[bb] : 0);
+        // its rank in its block: the block's earlier slots with the same id
+        for (int64_t q = b0 * bt * K + ln; q < slot; q += 64) part += ids[q] == e ? 1 : 0;
       }
       part = wave_inclusive_sum(part);
       if (ln == 63) red[j] = part;
@@ -264,7 +270,7 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
       const int64_t b = (slot / K) / bt;
       int64_t dd;
       if constexpr (MODE == 3) {
-        dd = (int64_t)red[j] + lrank[slot];
+        dd = (int64_t)red[j];
       } else {
         const int64_t base =
             MODE == 2 ? (int64_t)((red[j] + red[S + j]) + red[2 * S + j]) + red[3 * S + j]

@@ -188,6 +188,28 @@ __device__ __forceinline__ void store_expert_prefix(const int* rhist, int E, int
   }
 }
 
+// The block's histogram of its S slot ids (E <= 256) in LDS by integer
+// atomics (their order does not matter), then bhist[e * nb + b] and the
+// block's exclusive prefix over the experts bpre[e * nb + b]: what the
+// scatter needs when it ranks each slot itself.  Every thread of the
+// workgroup (NTH of them) calls it after writing its sids; rhist holds E
+// ints, wsum 4.
+template <int NTH>
+__device__ __forceinline__ void block_hist_prefix(const int* sids, int S, int E, int* rhist,
+                                                  int32_t* bhist, int32_t* bpre, int nb, int b,
+                                                  int* wsum) {
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += NTH) rhist[e] = 0;
+  __syncthreads();
+  for (int j = tid; j < S; j += NTH) {
+    const int e = sids[j];
+    if ((unsigned)e < (unsigned)E) atomicAdd(&rhist[e], 1);
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += NTH) bhist[(int64_t)e * nb + b] = rhist[e];
+  store_expert_prefix(rhist, E, bpre, nb, b, wsum);
+}
+
 // ---- launchers (each validates nothing: the C ABI layer has done it) -----
 // Router.  wgt is the fragment-major packed gate (bf16 path only).  When
 // lrank is not null the router also ranks its own selections for the dispatch

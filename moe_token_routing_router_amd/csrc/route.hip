@@ -527,9 +527,12 @@ __global__ __launch_bounds__(NW * 64) void route_bf16_kernel(
       }
     }
     const int ntok = (int)min((int64_t)BM, N - t0);
-    block_stable_rank<NW>(sids, ntok * K, E, lrank + t0 * K, rhist, wcnt);
-    for (int e = tid; e < E; e += NW * 64) bhist[(int64_t)e * nb + blockIdx.x] = rhist[e];
-    if (bpre) store_expert_prefix(rhist, E, bpre, nb, blockIdx.x, hist);
+    if (bpre) {  // the scatter ranks each slot itself: histogram and prefix only
+      block_hist_prefix<NW * 64>(sids, ntok * K, E, rhist, bhist, bpre, nb, blockIdx.x, hist);
+    } else {
+      block_stable_rank<NW>(sids, ntok * K, E, lrank + t0 * K, rhist, wcnt);
+      for (int e = tid; e < E; e += NW * 64) bhist[(int64_t)e * nb + blockIdx.x] = rhist[e];
+    }
   }
 
   if (counts) {
@@ -765,9 +768,12 @@ __global__ __launch_bounds__(NW * 64) void route_bf16_esplit_kernel(
       }
     }
     const int ntok = (int)min((int64_t)BM, N - t0);
-    block_stable_rank<NW>(sids, ntok * K, E, lrank + t0 * K, rhist, wcnt);
-    for (int e = tid; e < E; e += NW * 64) bhist[(int64_t)e * nb + blockIdx.x] = rhist[e];
-    if (bpre) store_expert_prefix(rhist, E, bpre, nb, blockIdx.x, hist);
+    if (bpre) {  // the scatter ranks each slot itself: histogram and prefix only
+      block_hist_prefix<NW * 64>(sids, ntok * K, E, rhist, bhist, bpre, nb, blockIdx.x, hist);
+    } else {
+      block_stable_rank<NW>(sids, ntok * K, E, lrank + t0 * K, rhist, wcnt);
+      for (int e = tid; e < E; e += NW * 64) bhist[(int64_t)e * nb + blockIdx.x] = rhist[e];
+    }
   }
 
   if (counts) {
