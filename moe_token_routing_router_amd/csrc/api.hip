@@ -256,10 +256,11 @@ moe_status_t launch_route_dispatch(const void* x, const void* gate_w, const floa
       base + rws + round_up((size_t)moe::dispatch_num_blocks(N, bt) * E * sizeof(int32_t), 256));
   hipError_t e;
   if (dtype == MOE_BF16) {
-    // Few blocks: the router also stores each block's exclusive prefix over
-    // the experts, and each scatter workgroup sums what its slots need
-    // itself, so neither a scan kernel nor zeroed counts are needed.  Many
-    // blocks: the scan kernel.
+    // Few blocks (K <= 4): the router stores each block's histogram and its
+    // exclusive prefix over the experts, and each scatter workgroup finds its
+    // slots' positions itself, so neither a ranking pass, a scan kernel nor
+    // zeroed counts are needed.  Otherwise the router ranks its picks and the
+    // scan kernel runs.
     const bool prefix = moe::dispatch_num_blocks(N, bt) <= kPrefixMaxBlocks && K <= kPrefixMaxK;
     int32_t* bpre = reinterpret_cast<int32_t*>(
         base + rws + dispatch_scratch_bytes(N, E, K, bt));

@@ -21,14 +21,18 @@
 //          the token's row is read once with 16-byte loads (issued before the
 //          index work) and written to its K rows with 16-byte stores.
 //
-// The fused router (route.hip) produces lrank and bhist in its own epilogue,
-// so moe_route_dispatch skips the count kernel; for K <= 2 the router also
-// adds its block histograms into counts and the scatter sums the earlier
-// blocks' counts itself, so the scan kernel is skipped too.  With a bhist of
-// at most kSumAllMaxInts entries (small N and E) every scatter workgroup also
-// sums whole histogram rows for the totals, so no scan kernel runs either.
-// Right after the router, the scatter takes its tokens in the router's XCD
-// order (see scatter_token) so part of its read of x hits L2.
+// The block-prefix form (K <= 4 and at most 512 blocks; api.hip decides):
+// the count kernel -- or, in moe_route_dispatch, the router's epilogue -- stores
+// only each block's histogram and its exclusive prefix over the experts, and
+// the scatter (MODE 3) finds each slot's position from those and from the
+// earlier equal ids of its block: no ranking pass, no scan kernel.  Beyond
+// those limits the count kernel (or the router's epilogue) ranks the slots
+// and the scan kernel runs.  With a bhist of at most kSumAllMaxInts entries
+// (small N and E) every scatter workgroup also sums whole histogram rows for
+// the totals, so no scan kernel runs either.  Right after the router, the
+// scatter takes its tokens in the router's XCD order, the router's last
+// blocks first (see scatter_token), so its re-read of x finds the rows the
+// memory-side cache received most recently.
 //
 // Atomics only ever produce counts; every position comes from a deterministic
 // rank, so the output is bitwise reproducible and equal to a stable argsort.
@@ -136,8 +140,10 @@ __global__ __launch_bounds__(256) void dispatch_scan_kernel(int32_t* __restrict_
 // Token of scatter workgroup g.  With xbt > 0 (one token per workgroup, N a
 // multiple of 8 * xbt): the router has just read x in blocks of xbt tokens,
 // block j on XCD j % 8 (the dispatcher's round robin), so the last blocks'
-// rows may still sit in that XCD's L2.  Workgroup g runs on XCD g % 8 and is
-// given a token of a block of that XCD, the XCD's last blocks first.
+// rows are the likeliest to still sit in the caches (the measured gain comes
+// from the memory-side cache, which the L2 fetch counters cannot see).
+// Workgroup g runs on XCD g % 8 and is given a token of a block of that XCD,
+// the XCD's last blocks first.
 // Otherwise tokens are taken in order.
 __device__ __forceinline__ int64_t scatter_token(int64_t g, int64_t N, int xbt) {
   if (xbt == 0) return g * kScatterTokens;
