@@ -511,9 +511,10 @@ __global__ __launch_bounds__(NW * 64) void route_bf16_kernel(
   select_topk_store<NT, U>(v, r, E, K, tt, N, ids, topw, (counts && !lrank) ? hist : nullptr,
                            pick);
 
-  // For the fused dispatch: stable rank of every selected slot among the
-  // equal ids of this workgroup's BM tokens, and the workgroup's per-expert
-  // histogram (the dispatch count kernel's outputs for blocks of BM tokens).
+  // For the fused dispatch (the dispatch count kernel's outputs for blocks of
+  // BM tokens): the workgroup's per-expert histogram with, given bpre, its
+  // exclusive prefix over the experts (the scatter ranks the slots), else the
+  // stable rank of every selected slot among the equal ids of the block.
   int* sids = reinterpret_cast<int*>(smem);
   int* rhist = sids + BM * kMaxRouteK;
   if (lrank) {
