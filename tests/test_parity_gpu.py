@@ -301,10 +301,11 @@ def test_route_dispatch_edge_cases(N, H, E, K, dtype, bias):
     check_route(gids, gw_, ids_o, w_o, logits_o, K, dtype)
 
 
-# The fused call's two ways to the block bases: for K <= 2 and up to 512
-# router blocks (64 tokens each) the scatter sums the earlier blocks' counts
-# itself (more than 256 blocks: each thread sums several), beyond that the
-# scan kernel runs.
+# The fused call's two ways to the block bases: for K <= 4 and up to 512
+# router blocks (64 tokens each) the router stores its blocks' histograms
+# and expert prefixes and the scatter sums them over the blocks and ranks
+# each slot in its block itself (more than 64 blocks: each lane sums
+# several), beyond that the router ranks its picks and the scan kernel runs.
 @pytest.mark.parametrize("N,K,bias", [(30000, 2, True), (20000, 1, False), (40000, 2, False)])
 def test_route_dispatch_block_counts(N, K, bias):
     print(f"[route_dispatch blocks] N={N} K={K}", flush=True)
@@ -325,6 +326,11 @@ ROUTER_PATHS = [
     (16384 + 5, 136, 200, 16, False, "bf16"),   # experts split, 64-token workgroups, E padded
     (8191, 72, 256, 4, True, "bf16"),           # just below the split: the H-split kernel
     (16384 + 40, 128, 100, 6, True, "bf16"),    # 65..128 experts, 64-token workgroups
+    # 65..128 experts from 32768 tokens: 128-token, 8-wave workgroups, whose
+    # blocks the fused dispatch uses (257 blocks with K = 4: the scatter
+    # ranks; 514 blocks: the router ranks and the scan kernel runs)
+    (32768 + 100, 64, 96, 4, True, "bf16"),
+    (65536 + 200, 64, 128, 2, False, "bf16"),
     (3000, 96, 128, 8, False, "bf16"),          # 65..128 experts, 32-token workgroups
     # 65..128 experts by the number of 64-wide H steps (the prefetch loop
     # takes three steps per pass): 3 (one pass), 4 (a pass and one more),
