@@ -367,6 +367,7 @@ TIE_CASES = [
     (5000, 512, 64, 2, "bf16"),     # H-split kernel, 32-token workgroups
     (17000, 128, 64, 4, "bf16"),    # H-split kernel, 64-token workgroups
     (2000, 128, 128, 8, "bf16"),    # experts-split kernel
+    (33000, 64, 128, 4, "bf16"),    # experts-split kernel, 128-token workgroups
     (9000, 64, 256, 16, "bf16"),    # experts-split kernel, 256 experts
     (600, 64, 256, 5, "bf16"),      # H-split kernel, 256 experts
     (333, 32, 48, 6, "f32"),        # fp32 kernel
