@@ -1,0 +1,70 @@
+"""Seeded random shapes through the whole forward path on the GPU against the
+oracle: the router (ids where the logit gaps are clear, weights), the fused
+route+dispatch and the two-call sequence (bit for bit against each other and
+against the oracle's counting sort of the GPU's ids), the standalone dispatch
+of the oracle's ids, and the combine.
+
+The shapes are drawn once from a fixed seed: token counts from 1 to about
+40000 (so the dispatch takes each of its forms: the small histogram summed
+by the scatter, the block-prefix scatter and the scan kernel), hidden sizes
+that are and are not multiples of 64, expert counts from 1 to 256 and K from
+1 to min(E, 8).  Each case prints its shape before it runs."""
+import numpy as np
+import pytest
+import torch
+
+from moe_token_routing_router_amd import _lib as L
+from moe_token_routing_router_amd import inputs as I
+from oracle import oracle as O
+from tests.parity import check_combine, check_route, check_sum_tight, from_dev, \
+    sum_of_abs_terms, to_dev
+from tests.test_parity_gpu import _fused_and_check, gpu_dispatch, gpu_route
+
+pytestmark = pytest.mark.gpu
+
+
+def _shapes(n_cases=18, seed=2024):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n_cases):
+        E = int(rng.choice([1, 2, 5, 16, 24, 48, 64, 64, 96, 128, 200, 256]))
+        K = int(rng.integers(1, min(E, 8) + 1))
+        N = int(np.exp(rng.uniform(0, np.log(40000))))
+        dtype = "f32" if i % 6 == 5 else "bf16"
+        step = 8 if dtype == "bf16" else 4
+        H = int(rng.choice([step, 64, 72, 136, 256, 264]))
+        H = max(step, H - H % step)
+        out.append((N, H, E, K, dtype, bool(rng.integers(0, 2))))
+    return out
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    L.library()
+
+
+@pytest.mark.parametrize("N,H,E,K,dtype,bias", _shapes())
+def test_random_shape_forward(N, H, E, K, dtype, bias):
+    print(f"[random] N={N} H={H} E={E} K={K} {dtype} bias={bias}", flush=True)
+    d = I.random_case(N * 31 + H * 7 + E, N, H, E, K, dtype, bias=bias)
+    ids_o, w_o, logits_o, _ = O.route(d["x"], d["gate_w"], d["bias"], K, dtype)
+    ids, w, counts = gpu_route(d)
+    check_route(ids, w, ids_o, w_o, logits_o, K, dtype)
+    np.testing.assert_array_equal(counts, np.bincount(ids.ravel(), minlength=E))
+    # fused call == two calls == the oracle's counting sort of the GPU's ids
+    _fused_and_check(d, K, E, dtype)
+    # standalone dispatch of the oracle's ids
+    oc, oo, op, oi = O.dispatch(ids_o, E)
+    gc, go, gp, gi, gx = gpu_dispatch(ids_o, d["x"], E, dtype)
+    for a, b in ((gc, oc), (go, oo), (gp, op), (gi, oi)):
+        np.testing.assert_array_equal(a, b)
+    np.testing.assert_array_equal(gx.view(np.uint8), O.permute_rows(d["x"], op, K).view(np.uint8))
+    # combine of expert outputs in the oracle's dispatched order
+    out = L.combine(to_dev(d["y"], dtype), torch.from_numpy(oi).cuda(),
+                    torch.from_numpy(w_o).cuda())
+    torch.cuda.synchronize()
+    ref = O.combine(d["y"], oi, w_o, dtype)
+    check_combine(from_dev(out), ref, dtype)
+    check_sum_tight(from_dev(out), ref, sum_of_abs_terms(d["y"], oi, K, dtype, w=w_o), K, dtype)
