@@ -16,10 +16,16 @@
 
 // Tuning knobs (compile-time; the defaults are the measured best on MI355X).
 #ifndef MOE_COMBINE_TOKENS
-#define MOE_COMBINE_TOKENS 2   // tokens per workgroup
+#define MOE_COMBINE_TOKENS 2   // tokens per workgroup (K = 2: MOE_COMBINE_TOKENS2)
+#endif
+#ifndef MOE_COMBINE_TOKENS2
+#define MOE_COMBINE_TOKENS2 1  // tokens per workgroup for K = 2
 #endif
 #ifndef MOE_COMBINE_U2
-#define MOE_COMBINE_U2 4        // output vectors per lane in flight for K = 2
+#define MOE_COMBINE_U2 2        // output vectors per lane in flight for K = 2
+#endif
+#ifndef MOE_COMBINE_U4
+#define MOE_COMBINE_U4 2        // ... for K = 4
 #endif
 #ifndef MOE_COMBINE_U8
 #define MOE_COMBINE_U8 4        // ... for K = 8
@@ -35,7 +41,6 @@ namespace moe {
 
 namespace {
 
-constexpr int kCombineTokens = MOE_COMBINE_TOKENS;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -101,7 +106,7 @@ __device__ __forceinline__ void add_vec(float (&acc)[BF16 ? 8 : 4], u32x4 v) {
   }
 }
 
-template <bool BF16, int KT, int U, bool RES>
+template <bool BF16, int KT, int U, int TPW, bool RES>
 __global__ __launch_bounds__(256) void combine_kernel(const u32x4* __restrict__ y,
                                                       const int32_t* __restrict__ inv,
                                                       const float* __restrict__ w, int64_t N,
@@ -110,12 +115,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4* __restrict__ 
                                                       u32x4* out) {
   constexpr int L = BF16 ? 8 : 4;
   const int K = KT > 0 ? KT : Krt;
-  extern __shared__ int dyn[];  // rows[kCombineTokens*K] then weights
+  extern __shared__ int dyn[];  // rows[TPW*K] then weights
   int* lrow = dyn;
-  float* lw = reinterpret_cast<float*>(dyn + kCombineTokens * K);
+  float* lw = reinterpret_cast<float*>(dyn + TPW * K);
   const int tid = threadIdx.x;
-  const int64_t n0 = (int64_t)blockIdx.x * kCombineTokens;
-  const int ntok = (int)min((int64_t)kCombineTokens, N - n0);
+  const int64_t n0 = (int64_t)blockIdx.x * TPW;
+  const int ntok = (int)min((int64_t)TPW, N - n0);
   const int64_t T = N * K;
   for (int j = tid; j < ntok * K; j += 256) {
     const int rrow = inv[n0 * K + j];
@@ -183,20 +188,20 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4* __restrict__ 
   }
 }
 
-template <bool BF16, int KT, int U>
+template <bool BF16, int KT, int U, int TPW = MOE_COMBINE_TOKENS>
 hipError_t launch_k(const void* y, const int32_t* inv, const float* w, int64_t N, int H, int K,
                     const void* res, void* out, hipStream_t s) {
-  const int64_t blocks = (N + kCombineTokens - 1) / kCombineTokens;
+  const int64_t blocks = (N + TPW - 1) / TPW;
   const int row_vecs = BF16 ? H / 8 : H / 4;
-  const size_t dyn = (sizeof(int) + sizeof(float)) * (size_t)kCombineTokens * K;
+  const size_t dyn = (sizeof(int) + sizeof(float)) * (size_t)TPW * K;
   if (res)
-    hipLaunchKernelGGL((combine_kernel<BF16, KT, U, true>), dim3((unsigned)blocks), dim3(256), dyn,
-                       s, reinterpret_cast<const u32x4*>(y), inv, w, N, K, row_vecs,
+    hipLaunchKernelGGL((combine_kernel<BF16, KT, U, TPW, true>), dim3((unsigned)blocks), dim3(256),
+                       dyn, s, reinterpret_cast<const u32x4*>(y), inv, w, N, K, row_vecs,
                        reinterpret_cast<const u32x4*>(res), reinterpret_cast<u32x4*>(out));
   else
-    hipLaunchKernelGGL((combine_kernel<BF16, KT, U, false>), dim3((unsigned)blocks), dim3(256),
-                       dyn, s, reinterpret_cast<const u32x4*>(y), inv, w, N, K, row_vecs,
-                       nullptr, reinterpret_cast<u32x4*>(out));
+    hipLaunchKernelGGL((combine_kernel<BF16, KT, U, TPW, false>), dim3((unsigned)blocks),
+                       dim3(256), dyn, s, reinterpret_cast<const u32x4*>(y), inv, w, N, K,
+                       row_vecs, nullptr, reinterpret_cast<u32x4*>(out));
   return hipGetLastError();
 }
 
@@ -205,8 +210,10 @@ hipError_t launch_dtype(const void* y, const int32_t* inv, const float* w, int64
                         int K, const void* res, void* out, hipStream_t s) {
   switch (K) {
     case 1: return launch_k<BF16, 1, 8>(y, inv, w, N, H, K, res, out, s);
-    case 2: return launch_k<BF16, 2, MOE_COMBINE_U2>(y, inv, w, N, H, K, res, out, s);
-    case 4: return launch_k<BF16, 4, 2>(y, inv, w, N, H, K, res, out, s);
+    case 2:
+      return launch_k<BF16, 2, MOE_COMBINE_U2, MOE_COMBINE_TOKENS2>(y, inv, w, N, H, K, res, out,
+                                                                    s);
+    case 4: return launch_k<BF16, 4, MOE_COMBINE_U4>(y, inv, w, N, H, K, res, out, s);
     case 8: return launch_k<BF16, 8, MOE_COMBINE_U8>(y, inv, w, N, H, K, res, out, s);
     default: return launch_k<BF16, 0, 1>(y, inv, w, N, H, K, res, out, s);
   }
