@@ -53,6 +53,9 @@
 #ifndef MOE_ROUTE_DEPTH
 #define MOE_ROUTE_DEPTH 1    // steps of register prefetch (1 or 2) for E <= 64
 #endif
+#ifndef MOE_ROUTE_F32_SPLIT_H
+#define MOE_ROUTE_F32_SPLIT_H 128  // fp32 router: H split four ways from this H on
+#endif
 #ifndef MOE_ROUTE_F32_UNROLL
 #define MOE_ROUTE_F32_UNROLL 8  // fp32 router: h steps of 4 unrolled together
 #endif
@@ -71,6 +74,7 @@ namespace moe {
 namespace {
 
 constexpr int kSentinel = 0x7fffffff;
+constexpr int kRouteF32SplitH = MOE_ROUTE_F32_SPLIT_H;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -786,44 +790,57 @@ __global__ __launch_bounds__(NW * 64) void route_bf16_esplit_kernel(
 }
 
 // ---------------------------------------------------------------- fp32 VALU
-// kRouteF32Tokens = 16 tokens per 256-thread workgroup: wave w, lane group g
-// owns token 16*blockIdx + 4w + g; lane r accumulates experts r, r+16, ...
-// with one fp32 FMA chain per expert in ascending h.  With lrank (the fused
-// call) the workgroup ranks its picks for the dispatch like the bf16 kernels.
-template <int NT>
-__global__ __launch_bounds__(256) void route_f32_kernel(const float* __restrict__ x,
-                                                        const float* __restrict__ gate_w,
-                                                        const float* __restrict__ bias, int64_t N,
-                                                        int H, int E, int K,
-                                                        int32_t* __restrict__ ids,
-                                                        float* __restrict__ topw,
-                                                        int32_t* __restrict__ counts,
-                                                        int32_t* __restrict__ lrank,
-                                                        int32_t* __restrict__ bhist, int nb) {
-  static_assert(kRouteF32Tokens == 16, "four tokens per wave, four waves");
+// kRouteF32Tokens = 16 tokens per workgroup of 256 * HS threads: wave w
+// (w % 4 = token group, w / 4 = quarter of H when HS = 4), lane group g owns
+// token 16*blockIdx + 4(w % 4) + g; lane r accumulates experts r, r+16, ...
+// with one fp32 FMA chain per expert and H part in ascending h; with HS = 4
+// the four parts' sums are added in part order through LDS.  With lrank (the
+// fused call) the workgroup ranks its picks for the dispatch like the bf16
+// kernels.
+template <int NT, int HS>
+__global__ __launch_bounds__(256 * HS) void route_f32_kernel(const float* __restrict__ x,
+                                                             const float* __restrict__ gate_w,
+                                                             const float* __restrict__ bias,
+                                                             int64_t N, int H, int E, int K,
+                                                             int32_t* __restrict__ ids,
+                                                             float* __restrict__ topw,
+                                                             int32_t* __restrict__ counts,
+                                                             int32_t* __restrict__ lrank,
+                                                             int32_t* __restrict__ bhist,
+                                                             int nb) {
+  static_assert(kRouteF32Tokens == 16, "four tokens per wave, four token groups");
+  static_assert(HS == 1 || HS == 4, "one or four parts of H");
   constexpr int EP = 16 * NT;
   __shared__ int hist[EP];
   __shared__ int sids[kRouteF32Tokens * kMaxRouteK];
   __shared__ int rhist[kMaxExperts];
-  __shared__ int wcnt[4 * kMaxExperts];
+  __shared__ int wcnt[4 * HS * kMaxExperts];
+  __shared__ float part[HS > 1 ? (HS - 1) * kRouteF32Tokens * EP : 1];
   const int tid = threadIdx.x;
+  const int wid = tid >> 6;
   const int lane = tid & 63;
   const int r = lane & 15;
   const int g = lane >> 4;
-  const int64_t t = (int64_t)blockIdx.x * 16 + (tid >> 6) * 4 + g;
+  const int tl = (wid & 3) * 4 + g;  // token within the workgroup
+  const int hq = wid >> 2;           // part of H
+  const int64_t t = (int64_t)blockIdx.x * 16 + tl;
   if (counts) {
-    for (int e = tid; e < EP; e += 256) hist[e] = 0;
+    for (int e = tid; e < EP; e += 256 * HS) hist[e] = 0;
     __syncthreads();
   }
   const int64_t tc = t < N ? t : N - 1;
   const float* xr = x + tc * H;
+  // this wave's part of H: whole 4-value steps
+  const int nst = H >> 2;
+  const int h_begin = 4 * ((hq * nst) / HS);
+  const int h_end = 4 * (((hq + 1) * nst) / HS);
   float acc[NT];
 #pragma unroll
   for (int q = 0; q < NT; ++q) acc[q] = 0.f;
   // (unrolled so that several steps' loads are in flight; the FMA order per
   // expert stays h ascending)
 #pragma unroll MOE_ROUTE_F32_UNROLL
-  for (int h = 0; h < H; h += 4) {
+  for (int h = h_begin; h < h_end; h += 4) {
     const float4 xv = *reinterpret_cast<const float4*>(xr + h);
     const float* wr = gate_w + (int64_t)h * E;
 #pragma unroll
@@ -837,32 +854,47 @@ __global__ __launch_bounds__(256) void route_f32_kernel(const float* __restrict_
       }
     }
   }
-  if (bias) {
+  if constexpr (HS > 1) {
+    if (hq > 0) {
 #pragma unroll
-    for (int q = 0; q < NT; ++q) {
-      const int e = 16 * q + r;
-      acc[q] += bias[e < E ? e : 0];  // e >= E is never a candidate
+      for (int q = 0; q < NT; ++q) part[((hq - 1) * kRouteF32Tokens + tl) * EP + 16 * q + r] = acc[q];
+    }
+    __syncthreads();
+    if (hq == 0) {
+#pragma unroll
+      for (int p = 0; p < HS - 1; ++p)
+#pragma unroll
+        for (int q = 0; q < NT; ++q) acc[q] += part[(p * kRouteF32Tokens + tl) * EP + 16 * q + r];
     }
   }
-  float v1[1][NT];
+  int pick[1] = {0};
+  if (hq == 0) {
+    if (bias) {
 #pragma unroll
-  for (int q = 0; q < NT; ++q) v1[0][q] = acc[q];
-  const int64_t t1[1] = {t};
-  int pick[1];
-  select_topk_store<NT, 1>(v1, r, E, K, t1, N, ids, topw, (counts && !lrank) ? hist : nullptr,
-                           pick);
+      for (int q = 0; q < NT; ++q) {
+        const int e = 16 * q + r;
+        acc[q] += bias[e < E ? e : 0];  // e >= E is never a candidate
+      }
+    }
+    float v1[1][NT];
+#pragma unroll
+    for (int q = 0; q < NT; ++q) v1[0][q] = acc[q];
+    const int64_t t1[1] = {t};
+    select_topk_store<NT, 1>(v1, r, E, K, t1, N, ids, topw, (counts && !lrank) ? hist : nullptr,
+                             pick);
+  }
   if (lrank) {
     const int64_t t0 = (int64_t)blockIdx.x * kRouteF32Tokens;
-    if (r < K) sids[((tid >> 6) * 4 + g) * K + r] = pick[0];
+    if (hq == 0 && r < K) sids[tl * K + r] = pick[0];
     const int ntok = (int)min((int64_t)kRouteF32Tokens, N - t0);
     // (the ranking's first barrier publishes sids)
-    block_stable_rank<4>(sids, ntok * K, E, lrank + t0 * K, rhist, wcnt);
-    for (int e = tid; e < E; e += 256) bhist[(int64_t)e * nb + blockIdx.x] = rhist[e];
+    block_stable_rank<4 * HS>(sids, ntok * K, E, lrank + t0 * K, rhist, wcnt);
+    for (int e = tid; e < E; e += 256 * HS) bhist[(int64_t)e * nb + blockIdx.x] = rhist[e];
   }
   if (counts) {
     __syncthreads();
     const int* h = lrank ? rhist : hist;
-    for (int e = tid; e < E; e += 256)
+    for (int e = tid; e < E; e += 256 * HS)
       if (h[e]) atomicAdd(&counts[e], h[e]);
   }
 }
@@ -953,8 +985,13 @@ hipError_t launch_f32_nt(const float* x, const float* gw, const float* bias, int
                          int E, int K, int32_t* ids, float* w, int32_t* counts, int32_t* lrank,
                          int32_t* bhist, hipStream_t s) {
   const int64_t blocks = (N + kRouteF32Tokens - 1) / kRouteF32Tokens;
-  hipLaunchKernelGGL((route_f32_kernel<NT>), dim3((unsigned)blocks), dim3(256), 0, s, x, gw,
-                     bias, N, H, E, K, ids, w, counts, lrank, bhist, (int)blocks);
+  // four waves per token group over H once each part keeps a long chain
+  if (H >= kRouteF32SplitH)
+    hipLaunchKernelGGL((route_f32_kernel<NT, 4>), dim3((unsigned)blocks), dim3(1024), 0, s, x,
+                       gw, bias, N, H, E, K, ids, w, counts, lrank, bhist, (int)blocks);
+  else
+    hipLaunchKernelGGL((route_f32_kernel<NT, 1>), dim3((unsigned)blocks), dim3(256), 0, s, x,
+                       gw, bias, N, H, E, K, ids, w, counts, lrank, bhist, (int)blocks);
   return hipGetLastError();
 }
 
