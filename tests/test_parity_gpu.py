@@ -346,6 +346,8 @@ ROUTER_PATHS = [
     (4097, 128, 64, 2, False, "bf16"),
     (700, 72, 256, 16, True, "f32"),            # fp32 router ranking 16-token blocks, E, K at limits
     (3001, 40, 128, 8, False, "f32"),           # fp32, block histogram above the scatter's own sum
+    (700, 136, 256, 16, True, "f32"),           # fp32, H split across four waves, E, K at limits
+    (2500, 520, 64, 4, False, "f32"),           # fp32, H split, ragged quarters
 ]
 
 
@@ -371,6 +373,7 @@ TIE_CASES = [
     (9000, 64, 256, 16, "bf16"),    # experts-split kernel, 256 experts
     (600, 64, 256, 5, "bf16"),      # H-split kernel, 256 experts
     (333, 32, 48, 6, "f32"),        # fp32 kernel
+    (333, 256, 48, 6, "f32"),       # fp32 kernel, H split across four waves
 ]
 
 
