@@ -1,8 +1,13 @@
-"""Seeded random shapes through the whole forward path on the GPU against the
-oracle: the router (ids where the logit gaps are clear, weights), the fused
+"""Seeded random shapes through the whole path on the GPU against the oracle.
+
+Forward: the router (ids where the logit gaps are clear, weights), the fused
 route+dispatch and the two-call sequence (bit for bit against each other and
 against the oracle's counting sort of the GPU's ids), the standalone dispatch
-of the oracle's ids, and the combine.
+of the oracle's ids, and the combine.  Backward and the widened calls, on the
+oracle's routing of the same inputs: the combine backward, the dispatch
+backward, the router backward with and without dx_perm, the aggregate with
+its residual, and the expert-parallel send metadata over a random number of
+ranks.
 
 The shapes are drawn once from a fixed seed: token counts from 1 to about
 40000 (so the dispatch takes each of its forms: the small histogram summed
@@ -18,7 +23,8 @@ from moe_token_routing_router_amd import inputs as I
 from oracle import oracle as O
 from tests.parity import check_combine, check_route, check_sum_tight, from_dev, \
     sum_of_abs_terms, to_dev
-from tests.test_parity_gpu import _fused_and_check, gpu_dispatch, gpu_route
+from tests.test_backward_gpu import _case, _check_combine_backward, _check_route_backward
+from tests.test_parity_gpu import _ep_check, _fused_and_check, gpu_dispatch, gpu_route
 
 pytestmark = pytest.mark.gpu
 
@@ -68,3 +74,31 @@ def test_random_shape_forward(N, H, E, K, dtype, bias):
     ref = O.combine(d["y"], oi, w_o, dtype)
     check_combine(from_dev(out), ref, dtype)
     check_sum_tight(from_dev(out), ref, sum_of_abs_terms(d["y"], oi, K, dtype, w=w_o), K, dtype)
+
+
+@pytest.mark.parametrize("N,H,E,K,dtype,bias", _shapes())
+def test_random_shape_backward_aggregate_ep(N, H, E, K, dtype, bias):
+    print(f"[random bwd] N={N} H={H} E={E} K={K} {dtype} bias={bias}", flush=True)
+    d = I.random_case(N * 31 + H * 7 + E, N, H, E, K, dtype, bias=bias)
+    c = _case(d)
+    _check_combine_backward(d, c)
+    _check_route_backward(d, c)
+    _check_route_backward(d, c, with_dx_perm=False)
+    # dispatch backward (unit weights) and aggregate (weights + residual)
+    inv_d = torch.from_numpy(c["inv"]).cuda()
+    dx = L.dispatch_backward(to_dev(d["y"], dtype), inv_d, N)
+    out = L.aggregate(to_dev(d["y"], dtype), inv_d, torch.from_numpy(c["w"]).cuda(),
+                      to_dev(d["x"], dtype))
+    torch.cuda.synchronize()
+    ref = O.dispatch_backward(d["y"], c["inv"], K, dtype)
+    check_combine(from_dev(dx), ref, dtype)
+    check_sum_tight(from_dev(dx), ref, sum_of_abs_terms(d["y"], c["inv"], K, dtype), K, dtype)
+    ref = O.aggregate(d["y"], c["inv"], c["w"], d["x"], dtype)
+    check_combine(from_dev(out), ref, dtype)
+    S = sum_of_abs_terms(d["y"], c["inv"], K, dtype, w=c["w"], residual=d["x"])
+    check_sum_tight(from_dev(out), ref, S, K + 1, dtype)
+    # expert-parallel metadata: a rank count that divides E
+    divisors = [r for r in range(1, E + 1) if E % r == 0]
+    R = int(np.random.default_rng(N + E).choice(divisors))
+    print(f"[random ep] ep_size={R}", flush=True)
+    _ep_check(c["ids"], d["x"], E, R, dtype)
