@@ -30,6 +30,9 @@
 #ifndef MOE_COMBINE_U8
 #define MOE_COMBINE_U8 4        // ... for K = 8
 #endif
+#ifndef MOE_COMBINE_WGS2
+#define MOE_COMBINE_WGS2 6      // K = 2 from kCombineCapN tokens: workgroups per CU at most
+#endif
 #ifndef MOE_COMBINE_NT_LOAD
 #define MOE_COMBINE_NT_LOAD 1   // non-temporal loads of y (each row is read once)
 #endif
@@ -188,12 +191,20 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4* __restrict__ 
   }
 }
 
+// from this many tokens the K = 2 gather caps its workgroups per CU
+constexpr int64_t kCombineCapN = 16384;
+
 template <bool BF16, int KT, int U, int TPW = MOE_COMBINE_TOKENS>
 hipError_t launch_k(const void* y, const int32_t* inv, const float* w, int64_t N, int H, int K,
                     const void* res, void* out, hipStream_t s) {
   const int64_t blocks = (N + TPW - 1) / TPW;
   const int row_vecs = BF16 ? H / 8 : H / 4;
-  const size_t dyn = (sizeof(int) + sizeof(float)) * (size_t)TPW * K;
+  size_t dyn = (sizeof(int) + sizeof(float)) * (size_t)TPW * K;
+  // K = 2 over a large batch: at most MOE_COMBINE_WGS2 tokens in flight per
+  // CU (66.6 -> 65.3 us at N = 16384, H = 4096; smaller batches need every
+  // slot)
+  if (KT == 2 && N >= kCombineCapN)
+    dyn = std::max(dyn, lds_for_workgroups_per_cu(MOE_COMBINE_WGS2));
   if (res)
     hipLaunchKernelGGL((combine_kernel<BF16, KT, U, TPW, true>), dim3((unsigned)blocks), dim3(256),
                        dyn, s, reinterpret_cast<const u32x4*>(y), inv, w, N, K, row_vecs,

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 namespace moe {
 
 // ---- limits -------------------------------------------------------------
@@ -13,6 +15,15 @@ constexpr int kMaxRouteK = 16;       // one 16-lane group keeps one pick per lan
 // tokens per block of the standalone count kernel (at most 4096 slots, so
 // its LDS copy of the ids stays at 16 KiB)
 inline int dispatch_count_tokens(int K) { return K <= 64 ? 64 : 4096 / K; }
+
+// ---- occupancy ------------------------------------------------------------
+// Dynamic LDS reserved per workgroup so that at most w workgroups share a CU
+// (160 KiB of LDS per CU on gfx950; 2 KiB below the exact share, which covers
+// the kernel's own LDS and the allocation granularity, and still leaves no
+// room for a (w+1)-th).  The gathers over large batches run faster with
+// fewer token rows in flight per CU than the wave slots would allow.
+constexpr size_t kLdsPerCu = 160 * 1024;
+inline size_t lds_for_workgroups_per_cu(int w) { return kLdsPerCu / w - 2048; }
 
 // ---- vector types -------------------------------------------------------
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
