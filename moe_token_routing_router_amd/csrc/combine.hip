@@ -33,6 +33,9 @@
 #ifndef MOE_COMBINE_WGS2
 #define MOE_COMBINE_WGS2 6      // K = 2 from kCombineCapN tokens: workgroups per CU at most
 #endif
+#ifndef MOE_AGG_WGS2
+#define MOE_AGG_WGS2 4          // ... with the residual row (aggregate)
+#endif
 #ifndef MOE_COMBINE_NT_LOAD
 #define MOE_COMBINE_NT_LOAD 1   // non-temporal loads of y (each row is read once)
 #endif
@@ -200,11 +203,12 @@ hipError_t launch_k(const void* y, const int32_t* inv, const float* w, int64_t N
   const int64_t blocks = (N + TPW - 1) / TPW;
   const int row_vecs = BF16 ? H / 8 : H / 4;
   size_t dyn = (sizeof(int) + sizeof(float)) * (size_t)TPW * K;
-  // K = 2 over a large batch: at most MOE_COMBINE_WGS2 tokens in flight per
-  // CU (66.6 -> 65.3 us at N = 16384, H = 4096; smaller batches need every
-  // slot)
+  // K = 2 over a large batch: at most 6 tokens in flight per CU, 4 with the
+  // residual (N = 16384, H = 4096: combine 66.6 -> 65.1 us, aggregate
+  // 88.3 -> 84.1 us; smaller batches need every slot, and K = 8 gains
+  // nothing)
   if (KT == 2 && N >= kCombineCapN)
-    dyn = std::max(dyn, lds_for_workgroups_per_cu(MOE_COMBINE_WGS2));
+    dyn = std::max(dyn, lds_for_workgroups_per_cu(res ? MOE_AGG_WGS2 : MOE_COMBINE_WGS2));
   if (res)
     hipLaunchKernelGGL((combine_kernel<BF16, KT, U, TPW, true>), dim3((unsigned)blocks), dim3(256),
                        dyn, s, reinterpret_cast<const u32x4*>(y), inv, w, N, K, row_vecs,

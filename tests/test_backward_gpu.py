@@ -133,6 +133,12 @@ BWD_EDGE = [
     (1000, 264, 32, 3, "f32", False),     # generic K, fp32
     (5000, 128, 64, 6, "bf16", True),
     (600, 8192, 64, 2, "bf16", False),    # rows wider than one pass of the row loops
+    # from 4096 tokens on, E <= 64 and K in {1, 2, 4, 8}: dx with the gate's
+    # column slices in LDS
+    (4096, 264, 64, 8, "bf16", True),     # K = 8; 33 vectors: one ragged slice
+    (5000, 520, 16, 1, "f32", True),      # K = 1 (dx = the dispatch term), fp32
+    (4500, 72, 33, 2, "bf16", False),     # 9 vectors per row: 55 idle lanes per wave
+    (4100, 4104, 64, 4, "bf16", True),    # 513 vectors: a last slice of one vector
 ]
 
 
