@@ -53,9 +53,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #define MOE_BWD_ROWS 8     // dispatched rows in flight per lane (gate partials)
 #endif
 
-#ifndef MOE_CBWD_WGS
-#define MOE_CBWD_WGS 4     // combine backward from kCbwdCapN tokens: workgroups per CU
-#endif                     // at most for K <= 2 (one fewer for larger K)
+#ifndef MOE_CBWD_CAP_KIB
+#define MOE_CBWD_CAP_KIB 160  // combine backward: rows in flight per CU (KiB), large batches
+#endif
 
 #ifndef MOE_BWD_GROUPS
 #define MOE_BWD_GROUPS 512 // gate-gradient partial-sum workgroups (about; see below)
@@ -193,18 +193,15 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const u32x4* __restric
   }
 }
 
-constexpr int64_t kCbwdCapN = 16384;  // from this many tokens (see launch_cbwd)
-
 template <bool BF16, int KT>
 hipError_t launch_cbwd(const void* dout, const void* y, const int32_t* inv, const float* w,
                        int64_t N, int H, int K, void* dy, float* dw, hipStream_t s) {
   const int row_vecs = BF16 ? H / 8 : H / 4;
-  // a large batch: fewer tokens in flight per CU (their 3K + 1 rows) read
-  // and write faster (127.4 -> 122.4 us at N = 16384, H = 4096, K = 2;
-  // 423 -> 411 us at N = 32768, H = 2048, K = 8; small batches need every
-  // slot)
-  const size_t dyn =
-      N >= kCbwdCapN ? lds_for_workgroups_per_cu(K <= 2 ? MOE_CBWD_WGS : MOE_CBWD_WGS - 1) : 0;
+  // a workgroup moves one token's 2K + 1 rows: four workgroups per CU at
+  // N = 16384, H = 4096, K = 2 (127.4 -> 121.7 us), three at N = 32768,
+  // H = 2048, K = 8 (423 -> 410 us)
+  const size_t dyn = gather_lds_cap(N, (size_t)H * (BF16 ? 2 : 4), (size_t)(2 * K + 1),
+                                    (size_t)MOE_CBWD_CAP_KIB * 1024);
   hipLaunchKernelGGL((combine_bwd_kernel<BF16, KT>), dim3((unsigned)N), dim3(256), dyn, s,
                      reinterpret_cast<const u32x4*>(dout), reinterpret_cast<const u32x4*>(y),
                      inv, w, N, K, row_vecs, reinterpret_cast<u32x4*>(dy), dw);

@@ -30,11 +30,8 @@
 #ifndef MOE_COMBINE_U8
 #define MOE_COMBINE_U8 4        // ... for K = 8
 #endif
-#ifndef MOE_COMBINE_WGS2
-#define MOE_COMBINE_WGS2 6      // K = 2 from kCombineCapN tokens: workgroups per CU at most
-#endif
-#ifndef MOE_AGG_WGS2
-#define MOE_AGG_WGS2 4          // ... with the residual row (aggregate)
+#ifndef MOE_COMBINE_CAP_KIB
+#define MOE_COMBINE_CAP_KIB 144 // rows in flight per CU (KiB) for large batches (gather_lds_cap)
 #endif
 #ifndef MOE_COMBINE_NT_LOAD
 #define MOE_COMBINE_NT_LOAD 1   // non-temporal loads of y (each row is read once)
@@ -194,21 +191,19 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4* __restrict__ 
   }
 }
 
-// from this many tokens the K = 2 gather caps its workgroups per CU
-constexpr int64_t kCombineCapN = 16384;
-
 template <bool BF16, int KT, int U, int TPW = MOE_COMBINE_TOKENS>
 hipError_t launch_k(const void* y, const int32_t* inv, const float* w, int64_t N, int H, int K,
                     const void* res, void* out, hipStream_t s) {
   const int64_t blocks = (N + TPW - 1) / TPW;
   const int row_vecs = BF16 ? H / 8 : H / 4;
   size_t dyn = (sizeof(int) + sizeof(float)) * (size_t)TPW * K;
-  // K = 2 over a large batch: at most 6 tokens in flight per CU, 4 with the
-  // residual (N = 16384, H = 4096: combine 66.6 -> 65.1 us, aggregate
-  // 88.3 -> 84.1 us; smaller batches need every slot, and K = 8 gains
-  // nothing)
-  if (KT == 2 && N >= kCombineCapN)
-    dyn = std::max(dyn, lds_for_workgroups_per_cu(res ? MOE_AGG_WGS2 : MOE_COMBINE_WGS2));
+  // a workgroup moves TPW tokens' K rows read, the residual and the output:
+  // at N = 16384, H = 4096, K = 2 (24 KiB) six workgroups per CU, with the
+  // residual (32 KiB) four: combine 66.6 -> 65.1 us, aggregate
+  // 88.3 -> 84.1 us
+  const size_t row_bytes = (size_t)row_vecs * 16;
+  dyn = std::max(dyn, gather_lds_cap(N, row_bytes, (size_t)TPW * (K + 1 + (res ? 1 : 0)),
+                                     (size_t)MOE_COMBINE_CAP_KIB * 1024));
   if (res)
     hipLaunchKernelGGL((combine_kernel<BF16, KT, U, TPW, true>), dim3((unsigned)blocks), dim3(256),
                        dyn, s, reinterpret_cast<const u32x4*>(y), inv, w, N, K, row_vecs,

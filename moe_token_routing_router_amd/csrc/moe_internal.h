@@ -20,10 +20,25 @@ inline int dispatch_count_tokens(int K) { return K <= 64 ? 64 : 4096 / K; }
 // Dynamic LDS reserved per workgroup so that at most w workgroups share a CU
 // (160 KiB of LDS per CU on gfx950; 2 KiB below the exact share, which covers
 // the kernel's own LDS and the allocation granularity, and still leaves no
-// room for a (w+1)-th).  The gathers over large batches run faster with
-// fewer token rows in flight per CU than the wave slots would allow.
+// room for a (w+1)-th).
 constexpr size_t kLdsPerCu = 160 * 1024;
 inline size_t lds_for_workgroups_per_cu(int w) { return kLdsPerCu / w - 2048; }
+
+// The per-token gathers (combine, aggregate, dispatch and combine backward)
+// over large batches with large rows run faster with fewer workgroups in
+// flight per CU than the wave slots allow: about `budget` bytes of rows
+// moved per CU at once.  From 16384 tokens, 4 KiB rows and 24 KiB of rows
+// per workgroup on, the dynamic LDS that caps a CU at budget / (rows *
+// row_bytes) workgroups (at least 3); 0 (no cap) otherwise.  Smaller rows
+// or batches need every slot (measured: 1-2 KiB rows at 16384 tokens run
+// 8-60 % slower under a cap).
+inline size_t gather_lds_cap(int64_t N, size_t row_bytes, size_t rows, size_t budget) {
+  const size_t bytes_per_workgroup = rows * row_bytes;
+  if (N < 16384 || row_bytes < 4096 || bytes_per_workgroup < 24 * 1024) return 0;
+  const size_t w = budget / bytes_per_workgroup;
+  if (w >= 8) return 0;
+  return lds_for_workgroups_per_cu(w < 3 ? 3 : (int)w);
+}
 
 // ---- vector types -------------------------------------------------------
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
