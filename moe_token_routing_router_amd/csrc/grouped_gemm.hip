@@ -28,7 +28,7 @@
 //    at the end.
 // When H % 32 != 0: 256 x 256 or 128 x 128 tiles of 4 waves with 64-wide K
 // steps double-buffered through registers, chunk c of row r at c ^ (r & 7).
-// fp32 inputs use a plain fp32 FMA kernel (one output per thread).
+// fp32 inputs use an LDS-tiled fp32 FMA kernel (64 x 64 tiles).
 #include "moe_internal.h"
 
 #ifndef MOE_GEMM_SMALL_RING
@@ -449,31 +449,70 @@ __global__ __launch_bounds__(512) void grouped_gemm_ring_kernel(
     }
 }
 
-// fp32: one output per thread, h ascending (small shapes).
+// fp32: 64 x 64 output tiles of one expert (the tiles numbered expert by
+// expert, as above), 256 threads with 4 x 4 outputs each; 16-wide K steps of
+// both operands staged through LDS (transposed, so each thread reads its
+// four rows' and four outputs' values as float4), fp32 FMAs with h
+// ascending -- one sum per output in a fixed order.
+constexpr int kF32Tile = 64;
+constexpr int kF32K = 16;
 __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(const float* __restrict__ x,
                                                                const float* __restrict__ w,
                                                                const int32_t* __restrict__ offsets,
                                                                int E, int64_t T, int H, int F,
                                                                float* __restrict__ y) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= T * F) return;
-  const int64_t p = idx / F;
-  const int f = (int)(idx - p * F);
-  // the segment holding p (offsets clamped to [0, T]); rows past offsets[E]
-  // belong to no expert
-  int e = -1;
-  int64_t lo = 0;
-  for (int j = 0; j < E; ++j) {
-    const int64_t hi = min(max((int64_t)offsets[j + 1], lo), T);
-    if (e < 0 && p >= lo && p < hi) e = j;
-    lo = hi;
+  __shared__ __align__(16) float xs[kF32K][kF32Tile];
+  __shared__ __align__(16) float ws[kF32K][kF32Tile];
+  __shared__ int s_e, s_rows;
+  __shared__ int64_t s_m0;
+  __shared__ int s_scan[4];
+  if (!tile_of<kF32Tile>(offsets, E, T, (int)blockIdx.x, &s_e, &s_m0, &s_rows, s_scan)) return;
+  const int e = s_e;
+  const int64_t m0 = s_m0;
+  const int rows = s_rows;
+  const int n0 = (int)blockIdx.y * kF32Tile;
+  const int tid = threadIdx.x;
+  // staging: thread -> row (or output) tid / 4, h quarter tid % 4 of the step
+  const int lr = tid >> 2, lq = (tid & 3) * 4;
+  const float* xrow = x + (m0 + min(lr, rows - 1)) * (int64_t)H;
+  const float* wrow = w + ((int64_t)e * F + min(n0 + lr, F - 1)) * (int64_t)H;
+  // compute: thread -> rows 4ty..4ty+3, outputs 4tx..4tx+3
+  const int tx = tid & 15, ty = tid >> 4;
+  float acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+  for (int k0 = 0; k0 < H; k0 += kF32K) {
+    const int kn = min(kF32K, H - k0);  // the ragged last step: fewer FMAs, not zero ones
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int h = k0 + lq + q;
+      xs[lq + q][lr] = h < H ? xrow[h] : 0.f;
+      ws[lq + q][lr] = h < H ? wrow[h] : 0.f;
+    }
+    __syncthreads();
+    for (int kk = 0; kk < kn; ++kk) {
+      const float4 a = *reinterpret_cast<const float4*>(&xs[kk][4 * ty]);
+      const float4 b = *reinterpret_cast<const float4*>(&ws[kk][4 * tx]);
+      const float av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
+    }
+    __syncthreads();
   }
-  if (e < 0) return;
-  const float* xr = x + p * H;
-  const float* wr = w + ((int64_t)e * F + f) * H;
-  float acc = 0.f;
-  for (int h = 0; h < H; ++h) acc = fmaf(xr[h], wr[h], acc);
-  y[p * F + f] = acc;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 4 * ty + i;
+    if (r >= rows) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int f = n0 + 4 * tx + j;
+      if (f < F) y[(m0 + r) * F + f] = acc[i][j];
+    }
+  }
 }
 
 #ifndef MOE_GEMM_TILE
@@ -539,8 +578,10 @@ hipError_t launch_grouped_linear(const void* x_perm, const void* weight, const i
       return launch_ring<128, 32>(x_perm, weight, offsets, T, H, E, F, y, s);
     return launch_gg<128, 128>(x_perm, weight, offsets, T, H, E, F, y, s);
   } else {
-    hipLaunchKernelGGL(grouped_gemm_f32_kernel, dim3((unsigned)((T * F + 255) / 256)), dim3(256),
-                       0, s, reinterpret_cast<const float*>(x_perm),
+    const int64_t mtiles = (T + kF32Tile - 1) / kF32Tile + E;
+    hipLaunchKernelGGL(grouped_gemm_f32_kernel,
+                       dim3((unsigned)mtiles, (unsigned)((F + kF32Tile - 1) / kF32Tile)),
+                       dim3(256), 0, s, reinterpret_cast<const float*>(x_perm),
                        reinterpret_cast<const float*>(weight), offsets, E, T, H, F,
                        reinterpret_cast<float*>(y));
   }
