@@ -339,7 +339,7 @@ size_t moe_route_backward_workspace_size(int64_t N, int32_t H, int32_t E, int32_
  * fp32 (moe_route's outputs); perm [N*K], offsets [E+1] and inv [N*K]
  * int32 (moe_dispatch's outputs for those ids); dx_perm [N*K,H] dtype or
  * NULL.  Sums of dgate_w and dbias run over each expert's dispatched rows in
- * order, within fixed ranges of 32..256 dispatched rows (a function of N*K
+ * order, within fixed ranges of 8..256 dispatched rows (a function of N*K
  * only), then over the ranges in order: bitwise reproducible.
  *   workspace >= moe_route_backward_workspace_size(N, H, E, K, dtype); scratch
  * N == 0 is a valid call: dgate_w (and dbias) are zero-filled.

@@ -61,7 +61,10 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #define MOE_BWD_GROUPS 512 // gate-gradient partial-sum workgroups (about; see below)
 #endif
 
-constexpr int kBwdChunk = 32;   // fewest dispatched rows per partial-sum workgroup
+#ifndef MOE_BWD_CHUNK
+#define MOE_BWD_CHUNK 8
+#endif
+constexpr int kBwdChunk = MOE_BWD_CHUNK;  // fewest dispatched rows per partial-sum workgroup
 constexpr int kBwdCoef = 256;   // most dispatched rows per partial-sum workgroup
 constexpr int kBwdGroups = MOE_BWD_GROUPS;
 #ifndef MOE_BWD_COPY_LAST

@@ -285,7 +285,7 @@ def test_backward_validation(lib):
     n = lib.moe_route_backward_workspace_size(16384, 4096, 64, 2, BF16)
     assert n >= 64 * 4096 * 2 + (32768 // 64 + 64) * 4096 * 4
     n_small = lib.moe_route_backward_workspace_size(1000, 64, 8, 2, BF16)
-    assert n_small >= 8 * 64 * 2 + (-(-2000 // 32) + 8) * 64 * 4
+    assert n_small >= 8 * 64 * 2 + (-(-2000 // 8) + 8) * 64 * 4
     assert lib.moe_route_backward_workspace_size(16, 64, 8, 9, BF16) == 0
 
 
