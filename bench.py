@@ -491,6 +491,28 @@ def main():
             call(name, i)
         _, ms = timed(lambda i, n=name: call(n, i), args.steps)
         stage_ms[name] = ms / args.steps
+    # the router with its gate packed once beforehand (moe_route_pack_gate:
+    # inference, or a training step that packs the gate right after the
+    # weight update): context, not part of the step; only where moe_route
+    # packs the gate on every call
+    if L.moe_route_workspace_size(H, E, tdt):
+        packed = L.pack_gate(gw)
+        torch.cuda.synchronize()
+        for c, st in zip(calls, sets):
+            c.update(
+                route_prepacked=(P(st["x"]), P(packed), P(bias), N, H, E, K, dt, P(st["ids"]),
+                                 P(st["w"]), None, sp),
+                route_dispatch_prepacked=(P(st["x"]), P(packed), P(bias), N, H, E, K, dt,
+                                          P(st["ids"]), P(st["w"]), P(st["counts"]),
+                                          P(st["offsets"]), P(st["perm"]), P(st["inv"]),
+                                          P(st["x_perm"]), P(fws), fws.numel(), sp))
+        fn.update(route_prepacked=lib.moe_route_prepacked,
+                  route_dispatch_prepacked=lib.moe_route_dispatch_prepacked)
+        for name in ("route_prepacked", "route_dispatch_prepacked"):
+            for i in range(3):
+                call(name, i)
+            _, ms = timed(lambda i, n=name: call(n, i), args.steps)
+            stage_ms[name] = ms / args.steps
     # context for the grouped GEMM: the platform library's dense GEMM of the
     # same total shape (all T rows through one expert's F x H weights), i.e.
     # what a tuned library GEMM reaches without per-expert segments
@@ -519,6 +541,8 @@ def main():
 
     alg = algorithmic_bytes(N, H, E, K, b)
     alg["route_dispatch"] = alg["route"] + alg["dispatch"]
+    alg["route_prepacked"] = alg["route"]
+    alg["route_dispatch_prepacked"] = alg["route_dispatch"]
     # ep_dispatch: ids in, x read once, S deduplicated rows out, the expert
     # metadata (counts, offsets, perm, inv) and the send metadata (send
     # counts/offsets, send_tok [S], send_row and expand_idx [N*K])
@@ -565,6 +589,10 @@ def main():
         "cold inputs, but the call's own scatter re-reads x right after its router: that "
         "re-read is cache-warm")
     stages["ep_dispatch"].update(ep_size=R, send_rows=S, slots=T)
+    for k in ("route_prepacked", "route_dispatch_prepacked"):
+        if k in stages:
+            stages[k]["note"] = ("gate packed once before the timed calls (moe_route_pack_gate); "
+                                 "context, not part of the step")
     g_flops = 2.0 * T * H * F
     stages["grouped_linear"].update(
         F=F, tflops=round(g_flops / (stage_ms["grouped_linear"] * 1e-3) / 1e12, 1),

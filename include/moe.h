@@ -104,6 +104,38 @@ moe_status_t moe_route(const void *x, const void *gate_w, const float *bias,
                        void *stream);
 
 /*
+ * moe_route_pack_gate -- the gate re-laid out once, for callers whose gate
+ * does not change between router calls (inference; or a training step that
+ * packs it once after each weight update, off the path of the forward
+ * pass): the layout moe_route builds in its workspace on every call (bf16:
+ * MFMA fragment order, padded to a power-of-two multiple of 16 experts).
+ * moe_route_prepacked and moe_route_dispatch_prepacked take it instead of
+ * gate_w and skip that re-layout (one kernel launch; about 4.5 us of the
+ * router call at N = 32768, H = 2048, E = 128 and 6 us at N = 16384,
+ * H = 4096, E = 128 on MI355X).
+ *   gate_w [H,E] dtype; packed: moe_route_workspace_size(H, E, dtype) bytes,
+ *   out, 16-byte aligned.  When that size is 0 (fp32, or bf16 at exactly 64
+ *   experts, where the router reads gate_w as it is) nothing is written and
+ *   the packed gate of the prepacked calls is gate_w itself.
+ * The packed bytes depend on gate_w only; the caller owns them and repacks
+ * after changing gate_w.
+ */
+moe_status_t moe_route_pack_gate(const void *gate_w, int32_t H, int32_t E, moe_dtype_t dtype,
+                                 void *packed, size_t packed_bytes, void *stream);
+
+/*
+ * moe_route_prepacked -- moe_route with packed_gate = moe_route_pack_gate's
+ * output for (gate_w, H, E, dtype) (gate_w itself when that size is 0) in
+ * place of gate_w, and no workspace.  Outputs, limits and status codes are
+ * those of moe_route, bit for bit.  A packed_gate that is not such an
+ * output gives wrong results (never an access outside it).
+ */
+moe_status_t moe_route_prepacked(const void *x, const void *packed_gate, const float *bias,
+                                 int64_t N, int32_t H, int32_t E, int32_t K, moe_dtype_t dtype,
+                                 int32_t *topk_ids, float *topk_w, int32_t *counts,
+                                 void *stream);
+
+/*
  * Bytes of device workspace moe_dispatch needs for (N, E, K).
  */
 size_t moe_dispatch_workspace_size(int64_t N, int32_t E, int32_t K);
@@ -163,6 +195,19 @@ moe_status_t moe_route_dispatch(const void *x, const void *gate_w, const float *
                                 int32_t *counts, int32_t *offsets, int32_t *perm,
                                 int32_t *inv, void *x_perm, void *workspace,
                                 size_t workspace_bytes, void *stream);
+
+/*
+ * moe_route_dispatch_prepacked -- moe_route_dispatch with the packed gate of
+ * moe_route_pack_gate in place of gate_w (gate_w itself when the packed size
+ * is 0).  Workspace as for moe_route_dispatch (its packed-gate part is not
+ * used); outputs bit for bit those of moe_route_dispatch.
+ */
+moe_status_t moe_route_dispatch_prepacked(const void *x, const void *packed_gate,
+                                          const float *bias, int64_t N, int32_t H, int32_t E,
+                                          int32_t K, moe_dtype_t dtype, int32_t *topk_ids,
+                                          float *topk_w, int32_t *counts, int32_t *offsets,
+                                          int32_t *perm, int32_t *inv, void *x_perm,
+                                          void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Bytes of the built-in workspace of moe_route_dispatch_noalloc (one copy per

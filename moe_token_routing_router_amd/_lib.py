@@ -29,7 +29,9 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARGUMENT", 2: "MOE_ERR_UNSUPPORTED",
 
 EXPORTS = ("moe_status_string", "moe_route_workspace_size", "moe_route",
            "moe_dispatch_workspace_size", "moe_dispatch", "moe_route_dispatch_workspace_size",
-           "moe_route_dispatch", "moe_route_dispatch_noalloc", "moe_ep_dispatch_workspace_size", "moe_ep_dispatch",
+           "moe_route_dispatch", "moe_route_dispatch_noalloc", "moe_route_pack_gate",
+           "moe_route_prepacked", "moe_route_dispatch_prepacked",
+           "moe_ep_dispatch_workspace_size", "moe_ep_dispatch",
            "moe_combine", "moe_aggregate", "moe_grouped_linear", "moe_combine_backward",
            "moe_dispatch_backward",
            "moe_route_backward_workspace_size", "moe_route_backward")
@@ -73,6 +75,14 @@ def library() -> ctypes.CDLL:
         lib.moe_route_dispatch_noalloc.argtypes = [P, P, P, i64, i32, i32, i32, ctypes.c_int, P,
                                                    P, P, P, P, P, P, P]
         lib.moe_route_dispatch_noalloc.restype = ctypes.c_int
+        lib.moe_route_pack_gate.argtypes = [P, i32, i32, ctypes.c_int, P, sz, P]
+        lib.moe_route_pack_gate.restype = ctypes.c_int
+        lib.moe_route_prepacked.argtypes = [P, P, P, i64, i32, i32, i32, ctypes.c_int, P, P, P,
+                                            P]
+        lib.moe_route_prepacked.restype = ctypes.c_int
+        lib.moe_route_dispatch_prepacked.argtypes = [P, P, P, i64, i32, i32, i32, ctypes.c_int,
+                                                     P, P, P, P, P, P, P, P, sz, P]
+        lib.moe_route_dispatch_prepacked.restype = ctypes.c_int
         lib.moe_ep_dispatch_workspace_size.argtypes = [i64, i32, i32, i32]
         lib.moe_ep_dispatch_workspace_size.restype = sz
         lib.moe_ep_dispatch.argtypes = [P, P, i64, i32, i32, i32, i32, ctypes.c_int, P, P, P, P,
@@ -390,7 +400,108 @@ def moe_route_backward(x_perm: torch.Tensor, gate_w: torch.Tensor, topk_ids: tor
         _stream(dev)))
 
 
+def _packed_gate(packed_gate: torch.Tensor, H: int, E: int, dtype: torch.dtype,
+                 dev: torch.device):
+    """The packed gate of moe_route_pack_gate: uint8 of the packed size, or
+    gate_w itself ([H, E] of the tokens' dtype) when that size is 0."""
+    n = moe_route_workspace_size(H, E, dtype)
+    if n:
+        return _dev(packed_gate, "packed_gate", torch.uint8, n, dev)
+    return _dev(packed_gate, "packed_gate (gate_w itself at this size)", dtype, H * E, dev)
+
+
+def moe_route_pack_gate(gate_w: torch.Tensor, packed: Optional[torch.Tensor]) -> None:
+    """Re-lay gate_w [H,E] out once for the prepacked router calls into
+    packed (uint8, moe_route_workspace_size(H, E, dtype) bytes; None when
+    that size is 0: then the packed gate is gate_w itself)."""
+    H, E = gate_w.shape
+    dev = gate_w.device
+    n = moe_route_workspace_size(H, E, gate_w.dtype)
+    _check("moe_route_pack_gate", library().moe_route_pack_gate(
+        _dev(gate_w, "gate_w", gate_w.dtype, H * E, dev), H, E, _dtype_code(gate_w.dtype),
+        _dev(packed, "packed", torch.uint8, n, dev) if n else None, n, _stream(dev)))
+
+
+def moe_route_prepacked(x: torch.Tensor, packed_gate: torch.Tensor, E: int,
+                        bias: Optional[torch.Tensor], K: int, topk_ids: torch.Tensor,
+                        topk_w: torch.Tensor, counts: Optional[torch.Tensor] = None) -> None:
+    """moe_route with the gate packed by moe_route_pack_gate (no workspace)."""
+    N, H = x.shape
+    dev = x.device
+    _check("moe_route_prepacked", library().moe_route_prepacked(
+        _dev(x, "x", x.dtype, N * H, dev), _packed_gate(packed_gate, H, E, x.dtype, dev),
+        _dev(bias, "bias", torch.float32, E, dev), N, H, E, K, _dtype_code(x.dtype),
+        _dev(topk_ids, "topk_ids", torch.int32, N * K, dev),
+        _dev(topk_w, "topk_w", torch.float32, N * K, dev),
+        _dev(counts, "counts", torch.int32, E, dev), _stream(dev)))
+
+
+def moe_route_dispatch_prepacked(x: torch.Tensor, packed_gate: torch.Tensor, E: int,
+                                 bias: Optional[torch.Tensor], K: int, topk_ids: torch.Tensor,
+                                 topk_w: torch.Tensor, counts: torch.Tensor,
+                                 offsets: torch.Tensor, perm: torch.Tensor, inv: torch.Tensor,
+                                 x_perm: Optional[torch.Tensor], workspace: torch.Tensor) -> None:
+    """moe_route_dispatch with the gate packed by moe_route_pack_gate."""
+    N, H = x.shape
+    dev = x.device
+    _check("moe_route_dispatch_prepacked", library().moe_route_dispatch_prepacked(
+        _dev(x, "x", x.dtype, N * H, dev), _packed_gate(packed_gate, H, E, x.dtype, dev),
+        _dev(bias, "bias", torch.float32, E, dev), N, H, E, K, _dtype_code(x.dtype),
+        _dev(topk_ids, "topk_ids", torch.int32, N * K, dev),
+        _dev(topk_w, "topk_w", torch.float32, N * K, dev),
+        _dev(counts, "counts", torch.int32, E, dev),
+        _dev(offsets, "offsets", torch.int32, E + 1, dev),
+        _dev(perm, "perm", torch.int32, N * K, dev), _dev(inv, "inv", torch.int32, N * K, dev),
+        _dev(x_perm, "x_perm", x.dtype, N * K * H, dev),
+        _dev(workspace, "workspace", torch.uint8, workspace.numel(), dev), workspace.numel(),
+        _stream(dev)))
+
+
 # ------------------------------------------------------- allocating forms
+
+def pack_gate(gate_w: torch.Tensor) -> torch.Tensor:
+    """The packed gate for the prepacked router calls (a new uint8 tensor,
+    or gate_w itself where the router reads the gate as it is)."""
+    H, E = gate_w.shape
+    n = moe_route_workspace_size(H, E, gate_w.dtype)
+    if not n:
+        moe_route_pack_gate(gate_w, None)
+        return gate_w
+    packed = torch.empty((n,), dtype=torch.uint8, device=gate_w.device)
+    moe_route_pack_gate(gate_w, packed)
+    return packed
+
+
+def route_prepacked(x: torch.Tensor, packed_gate: torch.Tensor, E: int, K: int,
+                    bias: Optional[torch.Tensor] = None, with_counts: bool = False):
+    """Allocate outputs and run moe_route_prepacked; returns (ids, w, counts-or-None)."""
+    N = x.shape[0]
+    ids = torch.empty((N, K), dtype=torch.int32, device=x.device)
+    w = torch.empty((N, K), dtype=torch.float32, device=x.device)
+    counts = torch.empty((E,), dtype=torch.int32, device=x.device) if with_counts else None
+    moe_route_prepacked(x, packed_gate, E, bias, K, ids, w, counts)
+    return ids, w, counts
+
+
+def route_dispatch_prepacked(x: torch.Tensor, packed_gate: torch.Tensor, E: int, K: int,
+                             bias: Optional[torch.Tensor] = None, with_rows: bool = True):
+    """Allocate outputs and run moe_route_dispatch_prepacked; returns
+    (ids, w, counts, offsets, perm, inv, x_perm-or-None)."""
+    N, H = x.shape
+    dev = x.device
+    ids = torch.empty((N, K), dtype=torch.int32, device=dev)
+    w = torch.empty((N, K), dtype=torch.float32, device=dev)
+    counts = torch.empty((E,), dtype=torch.int32, device=dev)
+    offsets = torch.empty((E + 1,), dtype=torch.int32, device=dev)
+    perm = torch.empty((N * K,), dtype=torch.int32, device=dev)
+    inv = torch.empty((N * K,), dtype=torch.int32, device=dev)
+    x_perm = torch.empty((N * K, H), dtype=x.dtype, device=dev) if with_rows else None
+    ws = torch.empty((max(1, moe_route_dispatch_workspace_size(N, H, E, K, x.dtype)),),
+                     dtype=torch.uint8, device=dev)
+    moe_route_dispatch_prepacked(x, packed_gate, E, bias, K, ids, w, counts, offsets, perm, inv,
+                                 x_perm, ws)
+    return ids, w, counts, offsets, perm, inv, x_perm
+
 
 def route(x: torch.Tensor, gate_w: torch.Tensor, K: int, bias: Optional[torch.Tensor] = None,
           with_counts: bool = False):

@@ -55,6 +55,52 @@ moe_status_t noalloc_scratch(void** out) {
   return MOE_OK;
 }
 
+// Argument checks of moe_route other than the workspace's.
+moe_status_t check_route(const void* x, const void* gate_w, const float* bias, int64_t N,
+                         int32_t H, int32_t E, int32_t K, moe_dtype_t dtype,
+                         const int32_t* topk_ids, const float* topk_w, const int32_t* counts) {
+  if (!valid_dtype(dtype) || N < 0 || H <= 0 || E <= 0 || K < 1 || K > E)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (N > 0 && (!x || !gate_w || !topk_ids || !topk_w)) return MOE_ERR_INVALID_ARGUMENT;
+  if (E > moe::kMaxExperts || K > moe::kMaxRouteK || N * (int64_t)K >= kMaxSlots ||
+      !row_ok(H, dtype))
+    return MOE_ERR_UNSUPPORTED;
+  if (!aligned(x, 16) || !aligned(gate_w, 16) || !aligned(bias, 4) || !aligned(topk_ids, 4) ||
+      !aligned(topk_w, 4) || !aligned(counts, 4))
+    return MOE_ERR_MISALIGNED;
+  return MOE_OK;
+}
+
+// The launches of moe_route for N > 0.  bf16: the gate is re-laid out into
+// the workspace first unless the router reads gate_w as it is (64 experts)
+// or gate_w already is that layout (prepacked).
+moe_status_t launch_route(const void* x, const void* gate_w, const float* bias, int64_t N,
+                          int32_t H, int32_t E, int32_t K, moe_dtype_t dtype, int32_t* topk_ids,
+                          float* topk_w, int32_t* counts, void* workspace, bool prepacked,
+                          hipStream_t s) {
+  if (dtype == MOE_BF16) {
+    const uint16_t* wgt = reinterpret_cast<const uint16_t*>(gate_w);
+    hipError_t e = hipSuccess;
+    if (moe::route_gate_raw(E) || prepacked) {
+      if (counts) e = moe::launch_fill_i32(counts, E, 0, s);
+    } else {
+      uint16_t* packed = reinterpret_cast<uint16_t*>(workspace);
+      e = moe::launch_gate_transpose(wgt, H, E, packed, counts, s);
+      wgt = packed;
+    }
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    return from_hip(moe::launch_route_bf16(reinterpret_cast<const uint16_t*>(x), wgt, bias, N, H,
+                                           E, K, topk_ids, topk_w, counts, nullptr, nullptr, s));
+  }
+  if (counts) {
+    hipError_t e = moe::launch_fill_i32(counts, E, 0, s);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  }
+  return from_hip(moe::launch_route_f32(reinterpret_cast<const float*>(x),
+                                        reinterpret_cast<const float*>(gate_w), bias, N, H, E, K,
+                                        topk_ids, topk_w, counts, nullptr, nullptr, s));
+}
+
 }  // namespace
 
 extern "C" {
@@ -80,41 +126,42 @@ size_t moe_route_workspace_size(int32_t H, int32_t E, moe_dtype_t dtype) {
 moe_status_t moe_route(const void* x, const void* gate_w, const float* bias, int64_t N, int32_t H,
                        int32_t E, int32_t K, moe_dtype_t dtype, int32_t* topk_ids, float* topk_w,
                        int32_t* counts, void* workspace, size_t workspace_bytes, void* stream) {
-  if (!valid_dtype(dtype) || N < 0 || H <= 0 || E <= 0 || K < 1 || K > E)
-    return MOE_ERR_INVALID_ARGUMENT;
-  if (N > 0 && (!x || !gate_w || !topk_ids || !topk_w)) return MOE_ERR_INVALID_ARGUMENT;
-  if (E > moe::kMaxExperts || K > moe::kMaxRouteK || N * (int64_t)K >= kMaxSlots ||
-      !row_ok(H, dtype))
-    return MOE_ERR_UNSUPPORTED;
-  if (!aligned(x, 16) || !aligned(gate_w, 16) || !aligned(bias, 4) || !aligned(topk_ids, 4) ||
-      !aligned(topk_w, 4) || !aligned(counts, 4) || !aligned(workspace, 16))
-    return MOE_ERR_MISALIGNED;
+  moe_status_t st = check_route(x, gate_w, bias, N, H, E, K, dtype, topk_ids, topk_w, counts);
+  if (st != MOE_OK) return st;
+  if (!aligned(workspace, 16)) return MOE_ERR_MISALIGNED;
   const size_t need = moe_route_workspace_size(H, E, dtype);
   if (need > 0 && (!workspace || workspace_bytes < need)) return MOE_ERR_WORKSPACE_TOO_SMALL;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (N == 0) return counts ? from_hip(moe::launch_fill_i32(counts, E, 0, s)) : MOE_OK;
+  return launch_route(x, gate_w, bias, N, H, E, K, dtype, topk_ids, topk_w, counts, workspace,
+                      false, s);
+}
 
-  if (dtype == MOE_BF16) {
-    const uint16_t* wgt = reinterpret_cast<const uint16_t*>(gate_w);
-    hipError_t e = hipSuccess;
-    if (moe::route_gate_raw(E)) {
-      if (counts) e = moe::launch_fill_i32(counts, E, 0, s);
-    } else {
-      uint16_t* packed = reinterpret_cast<uint16_t*>(workspace);
-      e = moe::launch_gate_transpose(wgt, H, E, packed, counts, s);
-      wgt = packed;
-    }
-    if (e != hipSuccess) return MOE_ERR_HIP;
-    return from_hip(moe::launch_route_bf16(reinterpret_cast<const uint16_t*>(x), wgt, bias, N, H,
-                                           E, K, topk_ids, topk_w, counts, nullptr, nullptr, s));
-  }
-  if (counts) {
-    hipError_t e = moe::launch_fill_i32(counts, E, 0, s);
-    if (e != hipSuccess) return MOE_ERR_HIP;
-  }
-  return from_hip(moe::launch_route_f32(reinterpret_cast<const float*>(x),
-                                        reinterpret_cast<const float*>(gate_w), bias, N, H, E, K,
-                                        topk_ids, topk_w, counts, nullptr, nullptr, s));
+moe_status_t moe_route_pack_gate(const void* gate_w, int32_t H, int32_t E, moe_dtype_t dtype,
+                                 void* packed, size_t packed_bytes, void* stream) {
+  if (!valid_dtype(dtype) || H <= 0 || E <= 0 || !gate_w) return MOE_ERR_INVALID_ARGUMENT;
+  if (E > moe::kMaxExperts || !row_ok(H, dtype)) return MOE_ERR_UNSUPPORTED;
+  const size_t need = moe_route_workspace_size(H, E, dtype);
+  if (need == 0) return MOE_OK;  // the router reads gate_w as it is
+  if (!packed) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned(gate_w, 16) || !aligned(packed, 16)) return MOE_ERR_MISALIGNED;
+  if (packed_bytes < need) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  return from_hip(moe::launch_gate_transpose(reinterpret_cast<const uint16_t*>(gate_w), H, E,
+                                             reinterpret_cast<uint16_t*>(packed), nullptr,
+                                             reinterpret_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_route_prepacked(const void* x, const void* packed_gate, const float* bias,
+                                 int64_t N, int32_t H, int32_t E, int32_t K, moe_dtype_t dtype,
+                                 int32_t* topk_ids, float* topk_w, int32_t* counts,
+                                 void* stream) {
+  moe_status_t st =
+      check_route(x, packed_gate, bias, N, H, E, K, dtype, topk_ids, topk_w, counts);
+  if (st != MOE_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (N == 0) return counts ? from_hip(moe::launch_fill_i32(counts, E, 0, s)) : MOE_OK;
+  return launch_route(x, packed_gate, bias, N, H, E, K, dtype, topk_ids, topk_w, counts, nullptr,
+                      true, s);
 }
 
 namespace {
@@ -246,7 +293,7 @@ moe_status_t launch_route_dispatch(const void* x, const void* gate_w, const floa
                                    int32_t H, int32_t E, int32_t K, moe_dtype_t dtype,
                                    int32_t* topk_ids, float* topk_w, int32_t* counts,
                                    int32_t* offsets, int32_t* perm, int32_t* inv, void* x_perm,
-                                   void* workspace, hipStream_t s) {
+                                   void* workspace, hipStream_t s, bool prepacked = false) {
   const size_t rws = moe_route_workspace_size(H, E, dtype);
   const int bt =
       dtype == MOE_BF16 ? moe::route_tokens_per_block(E, N) : moe::kRouteF32Tokens;
@@ -265,7 +312,7 @@ moe_status_t launch_route_dispatch(const void* x, const void* gate_w, const floa
     int32_t* bpre = reinterpret_cast<int32_t*>(
         base + rws + dispatch_scratch_bytes(N, E, K, bt));
     const uint16_t* wgt = reinterpret_cast<const uint16_t*>(gate_w);
-    if (!moe::route_gate_raw(E)) {
+    if (!moe::route_gate_raw(E) && !prepacked) {
       uint16_t* packed = reinterpret_cast<uint16_t*>(workspace);
       e = moe::launch_gate_transpose(wgt, H, E, packed, nullptr, s);
       if (e != hipSuccess) return MOE_ERR_HIP;
@@ -309,6 +356,25 @@ moe_status_t moe_route_dispatch(const void* x, const void* gate_w, const float* 
     return MOE_ERR_WORKSPACE_TOO_SMALL;
   return launch_route_dispatch(x, gate_w, bias, N, H, E, K, dtype, topk_ids, topk_w, counts,
                                offsets, perm, inv, x_perm, workspace, s);
+}
+
+moe_status_t moe_route_dispatch_prepacked(const void* x, const void* packed_gate,
+                                          const float* bias, int64_t N, int32_t H, int32_t E,
+                                          int32_t K, moe_dtype_t dtype, int32_t* topk_ids,
+                                          float* topk_w, int32_t* counts, int32_t* offsets,
+                                          int32_t* perm, int32_t* inv, void* x_perm,
+                                          void* workspace, size_t workspace_bytes, void* stream) {
+  moe_status_t st = check_route_dispatch(x, packed_gate, bias, N, H, E, K, dtype, topk_ids,
+                                         topk_w, counts, offsets, perm, inv, x_perm);
+  if (st != MOE_OK) return st;
+  if (N > 0 && !workspace) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned(workspace, 16)) return MOE_ERR_MISALIGNED;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (N == 0) return zero_counts_offsets(counts, offsets, E, s);
+  if (workspace_bytes < moe_route_dispatch_workspace_size(N, H, E, K, dtype))
+    return MOE_ERR_WORKSPACE_TOO_SMALL;
+  return launch_route_dispatch(x, packed_gate, bias, N, H, E, K, dtype, topk_ids, topk_w, counts,
+                               offsets, perm, inv, x_perm, workspace, s, true);
 }
 
 moe_status_t moe_route_dispatch_noalloc(const void* x, const void* gate_w, const float* bias,

@@ -149,6 +149,54 @@ def test_route_dispatch_validation(lib):
     assert route_dispatch(lib, wsb=64) == WS_SMALL
 
 
+def pack_gate(lib, gw=A, H=16, E=8, dt=BF16, packed=A, pb=1 << 20):
+    return lib.moe_route_pack_gate(gw, H, E, dt, packed, pb, None)
+
+
+def route_prepacked(lib, x=A, pg=A, bias=None, N=4, H=16, E=8, K=2, dt=BF16, ids=A2, w=A2,
+                    counts=None):
+    return lib.moe_route_prepacked(x, pg, bias, N, H, E, K, dt, ids, w, counts, None)
+
+
+def route_dispatch_prepacked(lib, x=A, pg=A, bias=None, N=4, H=16, E=8, K=2, dt=BF16, ids=A2,
+                             w=A2, counts=A2, offsets=A2, perm=A2, inv=A2, xp=A, ws=A,
+                             wsb=1 << 20):
+    return lib.moe_route_dispatch_prepacked(x, pg, bias, N, H, E, K, dt, ids, w, counts, offsets,
+                                            perm, inv, xp, ws, wsb, None)
+
+
+def test_prepacked_gate_validation(lib):
+    # packing: nothing to do (and nothing checked beyond the sizes) where the
+    # router reads gate_w as it is: fp32, or bf16 at exactly 64 experts
+    assert pack_gate(lib, E=64, packed=None, pb=0) == OK
+    assert pack_gate(lib, dt=F32, H=4, packed=None, pb=0) == OK
+    assert pack_gate(lib, gw=None) == INVALID
+    assert pack_gate(lib, packed=None) == INVALID
+    assert pack_gate(lib, E=0) == INVALID
+    assert pack_gate(lib, E=257) == UNSUPPORTED
+    assert pack_gate(lib, H=12) == UNSUPPORTED
+    assert pack_gate(lib, gw=MIS8) == MISALIGNED
+    assert pack_gate(lib, packed=MIS8) == MISALIGNED
+    assert pack_gate(lib, pb=lib.moe_route_workspace_size(16, 8, BF16) - 1) == WS_SMALL
+    # the prepacked router: moe_route's checks without a workspace
+    assert route_prepacked(lib, K=9) == INVALID
+    assert route_prepacked(lib, pg=None) == INVALID
+    assert route_prepacked(lib, E=300, K=2) == UNSUPPORTED
+    assert route_prepacked(lib, K=17, E=64) == UNSUPPORTED
+    assert route_prepacked(lib, H=12) == UNSUPPORTED
+    assert route_prepacked(lib, x=MIS8) == MISALIGNED
+    assert route_prepacked(lib, pg=MIS8) == MISALIGNED
+    assert route_prepacked(lib, counts=MIS) == MISALIGNED
+    # the prepacked fused call: moe_route_dispatch's checks
+    assert route_dispatch_prepacked(lib, K=9) == INVALID
+    assert route_dispatch_prepacked(lib, pg=None) == INVALID
+    assert route_dispatch_prepacked(lib, ws=None) == INVALID
+    assert route_dispatch_prepacked(lib, E=300, K=2) == UNSUPPORTED
+    assert route_dispatch_prepacked(lib, pg=MIS8) == MISALIGNED
+    assert route_dispatch_prepacked(lib, xp=MIS8) == MISALIGNED
+    assert route_dispatch_prepacked(lib, wsb=64) == WS_SMALL
+
+
 def route_dispatch_noalloc(lib, x=A, gw=A, bias=None, N=4, H=16, E=8, K=2, dt=BF16, ids=A2, w=A2,
                            counts=A2, offsets=A2, perm=A2, inv=A2, xp=A):
     return lib.moe_route_dispatch_noalloc(x, gw, bias, N, H, E, K, dt, ids, w, counts, offsets,

@@ -363,6 +363,47 @@ def test_router_kernel_paths(N, H, E, K, bias, dtype):
     check_route(gids, gw_, ids_o, w_o, logits_o, K, dtype)
 
 
+PREPACKED_CASES = [
+    # (N, H, E, K, bias, dtype): every kernel family, and the sizes where the
+    # router reads gate_w as it is (64 experts bf16, fp32: gate_w is the
+    # packed gate)
+    (1000, 200, 20, 3, True, "bf16"),            # H-split kernel, E padded
+    (5000, 512, 64, 2, False, "bf16"),           # 64 experts: no packed copy
+    (33000, 64, 128, 8, True, "bf16"),           # experts split, 128-token workgroups
+    (9000, 136, 256, 16, False, "bf16"),         # experts split, 256 experts
+    (700, 72, 5, 2, True, "bf16"),
+    (333, 256, 48, 6, True, "f32"),              # fp32: gate_w itself
+]
+
+
+@pytest.mark.parametrize("N,H,E,K,bias,dtype", PREPACKED_CASES)
+def test_prepacked_gate_calls_match_the_plain_ones(N, H, E, K, bias, dtype):
+    # the gate re-laid out once: the prepacked router and fused call give
+    # the plain calls' outputs bit for bit, and packing twice the same bytes
+    print(f"[prepacked] N={N} H={H} E={E} K={K} bias={bias} {dtype}", flush=True)
+    d = I.random_case(N + 3 * E, N, H, E, K, dtype, bias=bias)
+    x, gw = to_dev(d["x"], dtype), to_dev(d["gate_w"], dtype)
+    b = None if d["bias"] is None else torch.from_numpy(d["bias"]).cuda()
+    packed = L.pack_gate(gw)
+    packed2 = L.pack_gate(gw)
+    if L.moe_route_workspace_size(H, E, gw.dtype) == 0:
+        assert packed is gw
+    else:
+        assert packed.dtype == torch.uint8 and packed.data_ptr() != gw.data_ptr()
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(from_dev(packed).view(np.uint8), from_dev(packed2).view(np.uint8))
+    r1 = L.route(x, gw, K, bias=b, with_counts=True)
+    r2 = L.route_prepacked(x, packed, E, K, bias=b, with_counts=True)
+    f1 = L.route_dispatch(x, gw, K, bias=b)
+    f2 = L.route_dispatch_prepacked(x, packed, E, K, bias=b)
+    torch.cuda.synchronize()
+    for a, c in zip(r1 + f1, r2 + f2):
+        ua, uc = from_dev(a), from_dev(c)
+        np.testing.assert_array_equal(ua.view(np.uint8), uc.view(np.uint8))
+    ids_o, w_o, logits_o, _ = O.route(d["x"], d["gate_w"], d["bias"], K, dtype)
+    check_route(from_dev(r2[0]), from_dev(r2[1]), ids_o, w_o, logits_o, K, dtype)
+
+
 TIE_CASES = [
     # (N, H, E, K, dtype): every router kernel family, K from 1 to 16
     (300, 256, 20, 3, "bf16"),      # H-split kernel, E padded
