@@ -15,7 +15,7 @@ once differs from the oracle's exactly rounded sum by at most one unit in the
 last place of the output format plus the fp32 accumulation error
 n * 2^-24 * sum|terms|, and for bf16 outputs all but a few elements in 10^4
 are bit-identical (they differ only where the fp32 error straddles a bf16
-rounding point).  A kernel that accumulated in bf16, rounded a product or a
+rounding point; in outputs too small for that rate, at most three elements).  A kernel that accumulated in bf16, rounded a product or a
 partial sum to bf16, or truncated instead of rounding fails it.
 """
 import numpy as np
@@ -26,6 +26,7 @@ from moe_token_routing_router_amd import inputs as I
 MARGIN = 1e-3
 U32 = 2.0 ** -24           # unit roundoff of fp32
 MIN_EXACT = {"bf16": 0.9995}
+MIN_MISMATCHES = 3          # ... but always this many allowed
 W_TOL = {"bf16": 2e-3, "f32": 1e-5}
 # what fp32 accumulation of the logits (exact bf16 products, or fp32 FMAs)
 # and an fp32 softmax leave in the weights: logit errors of a few 1e-6 at
@@ -163,8 +164,12 @@ def check_sum_tight(out_g, out_o, S, nterms, dtype):
     assert not bad.any(), f"{bad.sum()} elements beyond one ulp plus the fp32 accumulation " \
                           f"error, worst {(err - lim).max()} at " \
                           f"{np.unravel_index(np.argmax(err - lim), err.shape)}"
-    exact = float((np.asarray(out_g) == np.asarray(out_o)).mean()) if np.asarray(out_g).size else 1.0
+    size = np.asarray(out_g).size
+    mism = int((np.asarray(out_g) != np.asarray(out_o)).sum())
+    exact = 1.0 - mism / size if size else 1.0
     print(f"    bit-identical fraction {exact:.6f}", flush=True)
     if dtype in MIN_EXACT:
-        assert exact >= MIN_EXACT[dtype], f"only {exact} of the outputs are bit-identical"
+        # a rate: a handful of boundary cases in a tiny output is not one
+        allowed = max(MIN_MISMATCHES, int((1.0 - MIN_EXACT[dtype]) * size))
+        assert mism <= allowed, f"only {exact} of the outputs are bit-identical ({mism} differ)"
     return exact
