@@ -9,7 +9,7 @@ backward, the router backward with and without dx_perm, the aggregate with
 its residual, and the expert-parallel send metadata over a random number of
 ranks.
 
-The shapes are drawn once from a fixed seed: token counts from 1 to about
+The 30 shapes are drawn once from a fixed seed: token counts from 1 to about
 40000 (so the dispatch takes each of its forms: the small histogram summed
 by the scatter, the block-prefix scatter and the scan kernel), hidden sizes
 that are and are not multiples of 64, expert counts from 1 to 256 and K from
@@ -29,7 +29,7 @@ from tests.test_parity_gpu import _ep_check, _fused_and_check, gpu_dispatch, gpu
 pytestmark = pytest.mark.gpu
 
 
-def _shapes(n_cases=18, seed=2024):
+def _shapes(n_cases=30, seed=2024):
     rng = np.random.default_rng(seed)
     out = []
     for i in range(n_cases):
