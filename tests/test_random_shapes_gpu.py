@@ -51,7 +51,28 @@ def gpu():
     L.library()
 
 
-@pytest.mark.parametrize("N,H,E,K,dtype,bias", _shapes())
+# and the shapes at the library's switch points, one on each side
+THRESHOLD_SHAPES = [
+    # the gathers' workgroup cap: from 16384 tokens, 4 KiB rows, 24 KiB per
+    # workgroup (bf16 H = 2048 and 4096, fp32 H = 1024)
+    (16383, 2048, 64, 2, "bf16", False), (16384, 2048, 64, 4, "bf16", True),
+    (16385, 4096, 64, 2, "bf16", False), (16384, 1024, 32, 2, "f32", True),
+    # router kernel switches: experts split from 8192 tokens at 129..256
+    # experts, 16-token workgroups up to 4096 tokens, 128-token ones from 32768
+    (8191, 64, 200, 4, "bf16", True), (8192, 64, 256, 8, "bf16", False),
+    (4096, 128, 64, 4, "bf16", True), (4097, 128, 64, 5, "bf16", False),
+    (32767, 64, 128, 2, "bf16", False), (32768, 64, 100, 8, "bf16", True),
+    # the scatter's own block sums: K <= 4 and at most 512 router blocks
+    (32768, 72, 64, 4, "bf16", False), (32769, 72, 64, 4, "bf16", True),
+    (2048, 264, 64, 5, "bf16", False),
+    # the row-major gate at exactly 64 experts, packed at 65; fp32 H split
+    # four ways from H = 128
+    (3000, 128, 65, 3, "bf16", True), (3000, 128, 64, 3, "bf16", True),
+    (1000, 124, 16, 2, "f32", False), (1000, 128, 16, 2, "f32", True),
+]
+
+
+@pytest.mark.parametrize("N,H,E,K,dtype,bias", _shapes() + THRESHOLD_SHAPES)
 def test_random_shape_forward(N, H, E, K, dtype, bias):
     print(f"[random] N={N} H={H} E={E} K={K} {dtype} bias={bias}", flush=True)
     d = I.random_case(N * 31 + H * 7 + E, N, H, E, K, dtype, bias=bias)
@@ -76,7 +97,7 @@ def test_random_shape_forward(N, H, E, K, dtype, bias):
     check_sum_tight(from_dev(out), ref, sum_of_abs_terms(d["y"], oi, K, dtype, w=w_o), K, dtype)
 
 
-@pytest.mark.parametrize("N,H,E,K,dtype,bias", _shapes())
+@pytest.mark.parametrize("N,H,E,K,dtype,bias", _shapes() + THRESHOLD_SHAPES)
 def test_random_shape_backward_aggregate_ep(N, H, E, K, dtype, bias):
     print(f"[random bwd] N={N} H={H} E={E} K={K} {dtype} bias={bias}", flush=True)
     d = I.random_case(N * 31 + H * 7 + E, N, H, E, K, dtype, bias=bias)
