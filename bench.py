@@ -500,10 +500,10 @@ def main():
         torch.cuda.synchronize()
         for c, st in zip(calls, sets):
             c.update(
-                route_prepacked=(P(st["x"]), P(packed), P(bias), N, H, E, K, dt, P(st["ids"]),
-                                 P(st["w"]), None, sp),
-                route_dispatch_prepacked=(P(st["x"]), P(packed), P(bias), N, H, E, K, dt,
-                                          P(st["ids"]), P(st["w"]), P(st["counts"]),
+                route_prepacked=(P(st["x"]), P(packed), packed.numel(), P(bias), N, H, E, K, dt,
+                                 P(st["ids"]), P(st["w"]), None, sp),
+                route_dispatch_prepacked=(P(st["x"]), P(packed), packed.numel(), P(bias), N, H,
+                                          E, K, dt, P(st["ids"]), P(st["w"]), P(st["counts"]),
                                           P(st["offsets"]), P(st["perm"]), P(st["inv"]),
                                           P(st["x_perm"]), P(fws), fws.numel(), sp))
         fn.update(route_prepacked=lib.moe_route_prepacked,

@@ -126,14 +126,17 @@ moe_status_t moe_route_pack_gate(const void *gate_w, int32_t H, int32_t E, moe_d
 /*
  * moe_route_prepacked -- moe_route with packed_gate = moe_route_pack_gate's
  * output for (gate_w, H, E, dtype) (gate_w itself when that size is 0) in
- * place of gate_w, and no workspace.  Outputs, limits and status codes are
- * those of moe_route, bit for bit.  A packed_gate that is not such an
- * output gives wrong results (never an access outside it).
+ * place of gate_w, and no workspace.  packed_bytes is the size of the
+ * packed_gate buffer: MOE_ERR_WORKSPACE_TOO_SMALL when it is below
+ * moe_route_workspace_size(H, E, dtype) (not checked when that size is 0).
+ * Outputs, limits and status codes are otherwise those of moe_route, bit
+ * for bit.  Packed bytes that are not moe_route_pack_gate's output for this
+ * gate give wrong results, never an access outside the buffer.
  */
-moe_status_t moe_route_prepacked(const void *x, const void *packed_gate, const float *bias,
-                                 int64_t N, int32_t H, int32_t E, int32_t K, moe_dtype_t dtype,
-                                 int32_t *topk_ids, float *topk_w, int32_t *counts,
-                                 void *stream);
+moe_status_t moe_route_prepacked(const void *x, const void *packed_gate, size_t packed_bytes,
+                                 const float *bias, int64_t N, int32_t H, int32_t E, int32_t K,
+                                 moe_dtype_t dtype, int32_t *topk_ids, float *topk_w,
+                                 int32_t *counts, void *stream);
 
 /*
  * Bytes of device workspace moe_dispatch needs for (N, E, K).
@@ -199,10 +202,12 @@ moe_status_t moe_route_dispatch(const void *x, const void *gate_w, const float *
 /*
  * moe_route_dispatch_prepacked -- moe_route_dispatch with the packed gate of
  * moe_route_pack_gate in place of gate_w (gate_w itself when the packed size
- * is 0).  Workspace as for moe_route_dispatch (its packed-gate part is not
- * used); outputs bit for bit those of moe_route_dispatch.
+ * is 0; packed_bytes as for moe_route_prepacked).  Workspace as for
+ * moe_route_dispatch (its packed-gate part is not used); outputs bit for bit
+ * those of moe_route_dispatch.
  */
 moe_status_t moe_route_dispatch_prepacked(const void *x, const void *packed_gate,
+                                          size_t packed_bytes,
                                           const float *bias, int64_t N, int32_t H, int32_t E,
                                           int32_t K, moe_dtype_t dtype, int32_t *topk_ids,
                                           float *topk_w, int32_t *counts, int32_t *offsets,

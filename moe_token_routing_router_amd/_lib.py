@@ -77,11 +77,11 @@ def library() -> ctypes.CDLL:
         lib.moe_route_dispatch_noalloc.restype = ctypes.c_int
         lib.moe_route_pack_gate.argtypes = [P, i32, i32, ctypes.c_int, P, sz, P]
         lib.moe_route_pack_gate.restype = ctypes.c_int
-        lib.moe_route_prepacked.argtypes = [P, P, P, i64, i32, i32, i32, ctypes.c_int, P, P, P,
-                                            P]
+        lib.moe_route_prepacked.argtypes = [P, P, sz, P, i64, i32, i32, i32, ctypes.c_int, P, P,
+                                            P, P]
         lib.moe_route_prepacked.restype = ctypes.c_int
-        lib.moe_route_dispatch_prepacked.argtypes = [P, P, P, i64, i32, i32, i32, ctypes.c_int,
-                                                     P, P, P, P, P, P, P, P, sz, P]
+        lib.moe_route_dispatch_prepacked.argtypes = [P, P, sz, P, i64, i32, i32, i32,
+                                                     ctypes.c_int, P, P, P, P, P, P, P, P, sz, P]
         lib.moe_route_dispatch_prepacked.restype = ctypes.c_int
         lib.moe_ep_dispatch_workspace_size.argtypes = [i64, i32, i32, i32]
         lib.moe_ep_dispatch_workspace_size.restype = sz
@@ -430,7 +430,7 @@ def moe_route_prepacked(x: torch.Tensor, packed_gate: torch.Tensor, E: int,
     dev = x.device
     _check("moe_route_prepacked", library().moe_route_prepacked(
         _dev(x, "x", x.dtype, N * H, dev), _packed_gate(packed_gate, H, E, x.dtype, dev),
-        _dev(bias, "bias", torch.float32, E, dev), N, H, E, K, _dtype_code(x.dtype),
+        packed_gate.numel() * packed_gate.element_size(), _dev(bias, "bias", torch.float32, E, dev), N, H, E, K, _dtype_code(x.dtype),
         _dev(topk_ids, "topk_ids", torch.int32, N * K, dev),
         _dev(topk_w, "topk_w", torch.float32, N * K, dev),
         _dev(counts, "counts", torch.int32, E, dev), _stream(dev)))
@@ -446,7 +446,7 @@ def moe_route_dispatch_prepacked(x: torch.Tensor, packed_gate: torch.Tensor, E: 
     dev = x.device
     _check("moe_route_dispatch_prepacked", library().moe_route_dispatch_prepacked(
         _dev(x, "x", x.dtype, N * H, dev), _packed_gate(packed_gate, H, E, x.dtype, dev),
-        _dev(bias, "bias", torch.float32, E, dev), N, H, E, K, _dtype_code(x.dtype),
+        packed_gate.numel() * packed_gate.element_size(), _dev(bias, "bias", torch.float32, E, dev), N, H, E, K, _dtype_code(x.dtype),
         _dev(topk_ids, "topk_ids", torch.int32, N * K, dev),
         _dev(topk_w, "topk_w", torch.float32, N * K, dev),
         _dev(counts, "counts", torch.int32, E, dev),

@@ -151,13 +151,14 @@ moe_status_t moe_route_pack_gate(const void* gate_w, int32_t H, int32_t E, moe_d
                                              reinterpret_cast<hipStream_t>(stream)));
 }
 
-moe_status_t moe_route_prepacked(const void* x, const void* packed_gate, const float* bias,
-                                 int64_t N, int32_t H, int32_t E, int32_t K, moe_dtype_t dtype,
-                                 int32_t* topk_ids, float* topk_w, int32_t* counts,
-                                 void* stream) {
+moe_status_t moe_route_prepacked(const void* x, const void* packed_gate, size_t packed_bytes,
+                                 const float* bias, int64_t N, int32_t H, int32_t E, int32_t K,
+                                 moe_dtype_t dtype, int32_t* topk_ids, float* topk_w,
+                                 int32_t* counts, void* stream) {
   moe_status_t st =
       check_route(x, packed_gate, bias, N, H, E, K, dtype, topk_ids, topk_w, counts);
   if (st != MOE_OK) return st;
+  if (packed_bytes < moe_route_workspace_size(H, E, dtype)) return MOE_ERR_WORKSPACE_TOO_SMALL;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (N == 0) return counts ? from_hip(moe::launch_fill_i32(counts, E, 0, s)) : MOE_OK;
   return launch_route(x, packed_gate, bias, N, H, E, K, dtype, topk_ids, topk_w, counts, nullptr,
@@ -359,14 +360,16 @@ moe_status_t moe_route_dispatch(const void* x, const void* gate_w, const float* 
 }
 
 moe_status_t moe_route_dispatch_prepacked(const void* x, const void* packed_gate,
-                                          const float* bias, int64_t N, int32_t H, int32_t E,
-                                          int32_t K, moe_dtype_t dtype, int32_t* topk_ids,
-                                          float* topk_w, int32_t* counts, int32_t* offsets,
-                                          int32_t* perm, int32_t* inv, void* x_perm,
-                                          void* workspace, size_t workspace_bytes, void* stream) {
+                                          size_t packed_bytes, const float* bias, int64_t N,
+                                          int32_t H, int32_t E, int32_t K, moe_dtype_t dtype,
+                                          int32_t* topk_ids, float* topk_w, int32_t* counts,
+                                          int32_t* offsets, int32_t* perm, int32_t* inv,
+                                          void* x_perm, void* workspace, size_t workspace_bytes,
+                                          void* stream) {
   moe_status_t st = check_route_dispatch(x, packed_gate, bias, N, H, E, K, dtype, topk_ids,
                                          topk_w, counts, offsets, perm, inv, x_perm);
   if (st != MOE_OK) return st;
+  if (packed_bytes < moe_route_workspace_size(H, E, dtype)) return MOE_ERR_WORKSPACE_TOO_SMALL;
   if (N > 0 && !workspace) return MOE_ERR_INVALID_ARGUMENT;
   if (!aligned(workspace, 16)) return MOE_ERR_MISALIGNED;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);

@@ -153,16 +153,16 @@ def pack_gate(lib, gw=A, H=16, E=8, dt=BF16, packed=A, pb=1 << 20):
     return lib.moe_route_pack_gate(gw, H, E, dt, packed, pb, None)
 
 
-def route_prepacked(lib, x=A, pg=A, bias=None, N=4, H=16, E=8, K=2, dt=BF16, ids=A2, w=A2,
-                    counts=None):
-    return lib.moe_route_prepacked(x, pg, bias, N, H, E, K, dt, ids, w, counts, None)
+def route_prepacked(lib, x=A, pg=A, pgb=1 << 20, bias=None, N=4, H=16, E=8, K=2, dt=BF16,
+                    ids=A2, w=A2, counts=None):
+    return lib.moe_route_prepacked(x, pg, pgb, bias, N, H, E, K, dt, ids, w, counts, None)
 
 
-def route_dispatch_prepacked(lib, x=A, pg=A, bias=None, N=4, H=16, E=8, K=2, dt=BF16, ids=A2,
-                             w=A2, counts=A2, offsets=A2, perm=A2, inv=A2, xp=A, ws=A,
+def route_dispatch_prepacked(lib, x=A, pg=A, pgb=1 << 20, bias=None, N=4, H=16, E=8, K=2, dt=BF16,
+                             ids=A2, w=A2, counts=A2, offsets=A2, perm=A2, inv=A2, xp=A, ws=A,
                              wsb=1 << 20):
-    return lib.moe_route_dispatch_prepacked(x, pg, bias, N, H, E, K, dt, ids, w, counts, offsets,
-                                            perm, inv, xp, ws, wsb, None)
+    return lib.moe_route_dispatch_prepacked(x, pg, pgb, bias, N, H, E, K, dt, ids, w, counts,
+                                            offsets, perm, inv, xp, ws, wsb, None)
 
 
 def test_prepacked_gate_validation(lib):
@@ -187,6 +187,7 @@ def test_prepacked_gate_validation(lib):
     assert route_prepacked(lib, x=MIS8) == MISALIGNED
     assert route_prepacked(lib, pg=MIS8) == MISALIGNED
     assert route_prepacked(lib, counts=MIS) == MISALIGNED
+    assert route_prepacked(lib, pgb=lib.moe_route_workspace_size(16, 8, BF16) - 1) == WS_SMALL
     # the prepacked fused call: moe_route_dispatch's checks
     assert route_dispatch_prepacked(lib, K=9) == INVALID
     assert route_dispatch_prepacked(lib, pg=None) == INVALID
@@ -195,6 +196,7 @@ def test_prepacked_gate_validation(lib):
     assert route_dispatch_prepacked(lib, pg=MIS8) == MISALIGNED
     assert route_dispatch_prepacked(lib, xp=MIS8) == MISALIGNED
     assert route_dispatch_prepacked(lib, wsb=64) == WS_SMALL
+    assert route_dispatch_prepacked(lib, pgb=16) == WS_SMALL
 
 
 def route_dispatch_noalloc(lib, x=A, gw=A, bias=None, N=4, H=16, E=8, K=2, dt=BF16, ids=A2, w=A2,
