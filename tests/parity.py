@@ -30,8 +30,11 @@ MIN_MISMATCHES = 3          # ... but always this many allowed
 W_TOL = {"bf16": 2e-3, "f32": 1e-5}
 # what fp32 accumulation of the logits (exact bf16 products, or fp32 FMAs)
 # and an fp32 softmax leave in the weights: logit errors of a few 1e-6 at
-# most at these sizes, and |dw| <= max|dl| / 2
+# most for rows of up to 4096 terms, and |dw| <= max|dl| / 2.  Rounding
+# errors of a longer sum grow like the square root of its length on these
+# random inputs, so for H > 4096 the bound is scaled by sqrt(H / 4096).
 W_TIGHT = {"bf16": 1e-5, "f32": 1e-6}
+W_TIGHT_H = 4096
 C_REL = {"bf16": 1e-2, "f32": 1e-5}
 C_ABS = {"bf16": 1e-4, "f32": 1e-6}
 
@@ -61,9 +64,12 @@ def decode(a, dtype):
     return np.asarray(a, np.float64)
 
 
-def check_route(ids_g, w_g, ids_o, w_o, logits_o, K, dtype):
-    """Assert router parity; returns the number of rows exempt by the margin."""
+def check_route(ids_g, w_g, ids_o, w_o, logits_o, K, dtype, H=None):
+    """Assert router parity; returns the number of rows exempt by the margin.
+    H, if given, is the logits' sum length (it widens the tight weight bound
+    beyond W_TIGHT_H terms)."""
     N, E = logits_o.shape
+    w_tight = W_TIGHT[dtype] * (max(1.0, H / W_TIGHT_H) ** 0.5 if H else 1.0)
     assert ids_g.shape == (N, K) and w_g.shape == (N, K)
     assert ids_g.min() >= 0 and ids_g.max() < E, "router id out of range"
     srt = -np.sort(-logits_o, axis=1)
@@ -94,8 +100,8 @@ def check_route(ids_g, w_g, ids_o, w_o, logits_o, K, dtype):
     wo = np.take_along_axis(w_o[rows], oo, 1).astype(np.float64)
     err = np.abs(wg - wo).max() if len(rows) else 0.0
     assert err <= tol, f"router weight error {err} > {tol}"
-    print(f"    router weight error {err:.3g} (tight bound {W_TIGHT[dtype]:g})", flush=True)
-    assert err <= W_TIGHT[dtype], f"router weight error {err} > {W_TIGHT[dtype]}"
+    print(f"    router weight error {err:.3g} (tight bound {w_tight:g})", flush=True)
+    assert err <= w_tight, f"router weight error {err} > {w_tight}"
     # rows inside the margin: valid picks, weights = softmax of the chosen
     # oracle logits, summing to one
     ex = np.nonzero(~sure)[0]
@@ -106,7 +112,7 @@ def check_route(ids_g, w_g, ids_o, w_o, logits_o, K, dtype):
         ref = np.exp(chosen - chosen.max(1, keepdims=True))
         ref /= ref.sum(1, keepdims=True)
         assert np.abs(ref - w_g[ex]).max() <= tol
-        assert np.abs(ref - w_g[ex]).max() <= W_TIGHT[dtype]
+        assert np.abs(ref - w_g[ex]).max() <= w_tight
     assert np.abs(w_g.astype(np.float64).sum(1) - 1).max() <= 1e-5
     return int((~sure).sum())
 

@@ -78,7 +78,7 @@ def test_random_shape_forward(N, H, E, K, dtype, bias):
     d = I.random_case(N * 31 + H * 7 + E, N, H, E, K, dtype, bias=bias)
     ids_o, w_o, logits_o, _ = O.route(d["x"], d["gate_w"], d["bias"], K, dtype)
     ids, w, counts = gpu_route(d)
-    check_route(ids, w, ids_o, w_o, logits_o, K, dtype)
+    check_route(ids, w, ids_o, w_o, logits_o, K, dtype, H=H)
     np.testing.assert_array_equal(counts, np.bincount(ids.ravel(), minlength=E))
     # fused call == two calls == the oracle's counting sort of the GPU's ids
     _fused_and_check(d, K, E, dtype)
