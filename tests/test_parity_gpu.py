@@ -66,7 +66,7 @@ def test_route_full_size(name):
     o = d["o"]
     print(f"[route] {name} N={d['N']} H={d['H']} E={d['E']} K={d['K']}", flush=True)
     ids, w, counts = gpu_route(d)
-    exempt = check_route(ids, w, o["ids"], o["w"], o["logits"], d["K"], d["dtype"])
+    exempt = check_route(ids, w, o["ids"], o["w"], o["logits"], d["K"], d["dtype"], H=d["H"])
     assert exempt <= 0.02 * d["N"]
     # the router's own dispatch counts: bincount of its ids, summing to N*K
     np.testing.assert_array_equal(counts, np.bincount(ids.ravel(), minlength=d["E"]))
@@ -153,7 +153,7 @@ def test_edge_case_full_chain(N, H, E, K, dtype, bias):
     d = I.random_case(N * 7 + H, N, H, E, K, dtype, bias=bias)
     ids_o, w_o, logits_o, _ = O.route(d["x"], d["gate_w"], d["bias"], K, dtype)
     ids, w, counts = gpu_route(d)
-    check_route(ids, w, ids_o, w_o, logits_o, K, dtype)
+    check_route(ids, w, ids_o, w_o, logits_o, K, dtype, H=H)
     np.testing.assert_array_equal(counts, np.bincount(ids.ravel(), minlength=E))
     oc, oo, op, oi = O.dispatch(ids_o, E)
     gc, go, gp, gi, gx = gpu_dispatch(ids_o, d["x"], E, dtype)
@@ -289,7 +289,7 @@ def test_route_dispatch_full_size(name):
     o = d["o"]
     print(f"[route_dispatch] {name}", flush=True)
     gids, gw_ = _fused_and_check(d, d["K"], d["E"], d["dtype"])
-    check_route(gids, gw_, o["ids"], o["w"], o["logits"], d["K"], d["dtype"])
+    check_route(gids, gw_, o["ids"], o["w"], o["logits"], d["K"], d["dtype"], H=d["H"])
 
 
 @pytest.mark.parametrize("N,H,E,K,dtype,bias", EDGE)
@@ -298,7 +298,7 @@ def test_route_dispatch_edge_cases(N, H, E, K, dtype, bias):
     d = I.random_case(N * 7 + H, N, H, E, K, dtype, bias=bias)
     ids_o, w_o, logits_o, _ = O.route(d["x"], d["gate_w"], d["bias"], K, dtype)
     gids, gw_ = _fused_and_check(d, K, E, dtype)
-    check_route(gids, gw_, ids_o, w_o, logits_o, K, dtype)
+    check_route(gids, gw_, ids_o, w_o, logits_o, K, dtype, H=H)
 
 
 # The fused call's two ways to the block bases: for K <= 4 and up to 512
@@ -357,10 +357,10 @@ def test_router_kernel_paths(N, H, E, K, bias, dtype):
     d = I.random_case(N + E, N, H, E, K, dtype, bias=bias)
     ids_o, w_o, logits_o, _ = O.route(d["x"], d["gate_w"], d["bias"], K, dtype)
     ids, w, counts = gpu_route(d)
-    check_route(ids, w, ids_o, w_o, logits_o, K, dtype)
+    check_route(ids, w, ids_o, w_o, logits_o, K, dtype, H=H)
     np.testing.assert_array_equal(counts, np.bincount(ids.ravel(), minlength=E))
     gids, gw_ = _fused_and_check(d, K, E, dtype)
-    check_route(gids, gw_, ids_o, w_o, logits_o, K, dtype)
+    check_route(gids, gw_, ids_o, w_o, logits_o, K, dtype, H=H)
 
 
 PREPACKED_CASES = [
@@ -401,7 +401,7 @@ def test_prepacked_gate_calls_match_the_plain_ones(N, H, E, K, bias, dtype):
         ua, uc = from_dev(a), from_dev(c)
         np.testing.assert_array_equal(ua.view(np.uint8), uc.view(np.uint8))
     ids_o, w_o, logits_o, _ = O.route(d["x"], d["gate_w"], d["bias"], K, dtype)
-    check_route(from_dev(r2[0]), from_dev(r2[1]), ids_o, w_o, logits_o, K, dtype)
+    check_route(from_dev(r2[0]), from_dev(r2[1]), ids_o, w_o, logits_o, K, dtype, H=H)
 
 
 TIE_CASES = [
