@@ -331,6 +331,15 @@ ROUTER_PATHS = [
     # ranks; 514 blocks: the router ranks and the scan kernel runs)
     (32768 + 100, 64, 96, 4, True, "bf16"),
     (65536 + 200, 64, 128, 2, False, "bf16"),
+    # the same workgroups by H: whole steps and a ragged one (more steps
+    # than the copies run ahead), one step and a ragged one, only a ragged one
+    (32768 + 37, 200, 128, 8, True, "bf16"),
+    (32768 + 1, 1000, 120, 2, False, "bf16"),
+    (32768, 72, 128, 4, False, "bf16"),
+    (32768 + 5, 40, 100, 3, True, "bf16"),
+    # 64-token workgroups at 65..128 experts by H: many steps, a ragged one only
+    (16384 + 9, 520, 128, 4, True, "bf16"),
+    (16384 + 2, 24, 128, 2, False, "bf16"),
     (3000, 96, 128, 8, False, "bf16"),          # 65..128 experts, 32-token workgroups
     # 65..128 experts by the number of 64-wide H steps (the prefetch loop
     # takes three steps per pass): 3 (one pass), 4 (a pass and one more),
