@@ -203,6 +203,14 @@ __device__ __forceinline__ void select_topk_store(const float (&v)[U][NT], int r
   }
 }
 
+// LDS token tiles: 16-byte chunk c of row r sits at chunk c ^ tile_swz(r).
+// A 128-bit fragment read has 16 lanes on 16 consecutive rows, one logical
+// chunk; with the row's low three bits alone, rows r and r + 8 land on the
+// same banks when the LDS serves 16 lanes (256 bytes) at once; the fourth
+// row bit flipping the low chunk bit separates them and keeps every aligned
+// group of 8 rows on 8 distinct chunks.
+__device__ __forceinline__ int tile_swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4 u) {
   return __builtin_bit_cast(bf16x8_t, u);
 }
@@ -215,8 +223,8 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4 u) {
 // A operand (token rows): per step, the wave's BM x 64 tile is read with
 // coalesced 16-byte loads (8 lanes cover one 128-byte row segment), written
 // to the wave's own LDS tile with an XOR swizzle (16-byte chunk c of row r is
-// stored at chunk c ^ (r & 7)) and read back in MFMA layout; the swizzle makes
-// both the writes and the fragment reads free of bank conflicts.
+// stored at chunk c ^ tile_swz(r)) and read back in MFMA layout; the swizzle
+// makes both the writes and the fragment reads free of bank conflicts.
 // B operand (gate): the gate has been packed fragment-major by
 // gate_pack_kernel, so the B fragment of (step, expert tile q, half hf) is
 // one contiguous 1 KiB block -- lane l loads bytes [16l, 16l+16).
@@ -281,7 +289,7 @@ __global__ __launch_bounds__(NW * 64) void route_bf16_kernel(
     int64_t t = t0 + row;
     if (t > N - 1) t = N - 1;  // tail rows recompute the last token; never stored
     aptr[j] = x + t * H + 8 * lch;
-    wofs[j] = row * 128 + ((lch ^ (row & 7)) << 4);
+    wofs[j] = row * 128 + ((lch ^ tile_swz(row)) << 4);
   }
   // MFMA fragment reads: tile m, half hf -> (row 16m + r, chunk 2g + hf)
   int rofs[MT][2];
@@ -290,7 +298,7 @@ __global__ __launch_bounds__(NW * 64) void route_bf16_kernel(
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
       const int row = 16 * m + r;
-      rofs[m][hf] = row * 128 + (((2 * g + hf) ^ (row & 7)) << 4);
+      rofs[m][hf] = row * 128 + (((2 * g + hf) ^ tile_swz(row)) << 4);
     }
   char* tile = smem + wid * (TILE + GTILE);
   char* gtile = tile + TILE;
@@ -604,7 +612,7 @@ __global__ __launch_bounds__(NW * 64) void route_bf16_esplit_kernel(
     int64_t t = t0 + row;
     if (t > N - 1) t = N - 1;  // tail rows recompute the last token; never stored
     aptr[j] = x + t * H + 8 * lch;
-    wofs[j] = row * 128 + ((lch ^ (row & 7)) << 4);
+    wofs[j] = row * 128 + ((lch ^ tile_swz(row)) << 4);
   }
   int rofs[MT][2];
 #pragma unroll
@@ -612,7 +620,7 @@ __global__ __launch_bounds__(NW * 64) void route_bf16_esplit_kernel(
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
       const int row = 16 * m + r;
-      rofs[m][hf] = row * 128 + (((2 * g + hf) ^ (row & 7)) << 4);
+      rofs[m][hf] = row * 128 + (((2 * g + hf) ^ tile_swz(row)) << 4);
     }
 
   f32x4_t acc[MT][NTW];
