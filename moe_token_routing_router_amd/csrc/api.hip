@@ -178,6 +178,13 @@ constexpr int64_t kPrefixMaxBlocks = MOE_PREFIX_MAX_BLOCKS;
 #define MOE_PREFIX_MAX_K 4
 #endif
 constexpr int kPrefixMaxK = MOE_PREFIX_MAX_K;
+// The fused call's blocks are the router's (at most 128 tokens), so each slot
+// has fewer earlier slots of its block to rank than in the standalone
+// dispatch, whose count blocks hold up to 4096 / K tokens: there K up to 8.
+#ifndef MOE_PREFIX_MAX_K_FUSED
+#define MOE_PREFIX_MAX_K_FUSED 8
+#endif
+constexpr int kPrefixMaxKFused = MOE_PREFIX_MAX_K_FUSED;
 
 // dispatch scratch: bhist [E][blocks of bt tokens] then lrank [N*K]
 size_t bhist_bytes(int64_t N, int32_t E, int bt) {
@@ -304,12 +311,13 @@ moe_status_t launch_route_dispatch(const void* x, const void* gate_w, const floa
       base + rws + round_up((size_t)moe::dispatch_num_blocks(N, bt) * E * sizeof(int32_t), 256));
   hipError_t e;
   if (dtype == MOE_BF16) {
-    // Few blocks (K <= 4): the router stores each block's histogram and its
+    // Few blocks (K <= 8): the router stores each block's histogram and its
     // exclusive prefix over the experts, and each scatter workgroup finds its
     // slots' positions itself, so neither a ranking pass, a scan kernel nor
     // zeroed counts are needed.  Otherwise the router ranks its picks and the
     // scan kernel runs.
-    const bool prefix = moe::dispatch_num_blocks(N, bt) <= kPrefixMaxBlocks && K <= kPrefixMaxK;
+    const bool prefix =
+        moe::dispatch_num_blocks(N, bt) <= kPrefixMaxBlocks && K <= kPrefixMaxKFused;
     int32_t* bpre = reinterpret_cast<int32_t*>(
         base + rws + dispatch_scratch_bytes(N, E, K, bt));
     const uint16_t* wgt = reinterpret_cast<const uint16_t*>(gate_w);
