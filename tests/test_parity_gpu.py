@@ -301,12 +301,14 @@ def test_route_dispatch_edge_cases(N, H, E, K, dtype, bias):
     check_route(gids, gw_, ids_o, w_o, logits_o, K, dtype, H=H)
 
 
-# The fused call's two ways to the block bases: for K <= 4 and up to 512
+# The fused call's two ways to the block bases: for K <= 8 and up to 512
 # router blocks (64 tokens each) the router stores its blocks' histograms
 # and expert prefixes and the scatter sums them over the blocks and ranks
 # each slot in its block itself (more than 64 blocks: each lane sums
 # several), beyond that the router ranks its picks and the scan kernel runs.
-@pytest.mark.parametrize("N,K,bias", [(30000, 2, True), (20000, 1, False), (40000, 2, False)])
+@pytest.mark.parametrize("N,K,bias", [(30000, 2, True), (20000, 1, False), (40000, 2, False),
+                                      (30000, 8, True), (25000, 5, False), (40000, 6, True),
+                                      (33000, 8, False)])
 def test_route_dispatch_block_counts(N, K, bias):
     print(f"[route_dispatch blocks] N={N} K={K}", flush=True)
     d = I.random_case(N + K, N, 64, 64, K, "bf16", bias=bias)
