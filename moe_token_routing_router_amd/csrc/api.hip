@@ -178,9 +178,10 @@ constexpr int64_t kPrefixMaxBlocks = MOE_PREFIX_MAX_BLOCKS;
 #define MOE_PREFIX_MAX_K 4
 #endif
 constexpr int kPrefixMaxK = MOE_PREFIX_MAX_K;
-// The fused call's blocks are the router's (at most 128 tokens), so each slot
-// has fewer earlier slots of its block to rank than in the standalone
-// dispatch, whose count blocks hold up to 4096 / K tokens: there K up to 8.
+// In the fused call the blocks are the router's (128 tokens at 65..128
+// experts from 32768 tokens), so each slot sums half the block entries it
+// would over the standalone dispatch's 64-token count blocks: there K up to
+// 8 (at K = 8 the standalone dispatch is slower in this form).
 #ifndef MOE_PREFIX_MAX_K_FUSED
 #define MOE_PREFIX_MAX_K_FUSED 8
 #endif
