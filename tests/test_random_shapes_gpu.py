@@ -62,9 +62,11 @@ THRESHOLD_SHAPES = [
     (8191, 64, 200, 4, "bf16", True), (8192, 64, 256, 8, "bf16", False),
     (4096, 128, 64, 4, "bf16", True), (4097, 128, 64, 5, "bf16", False),
     (32767, 64, 128, 2, "bf16", False), (32768, 64, 100, 8, "bf16", True),
-    # the scatter's own block sums: K <= 4 and at most 512 router blocks
+    # the scatter's own block sums: at most 512 blocks and K <= 4 (the
+    # standalone dispatch) or K <= 8 (the fused call)
     (32768, 72, 64, 4, "bf16", False), (32769, 72, 64, 4, "bf16", True),
-    (2048, 264, 64, 5, "bf16", False),
+    (2048, 264, 64, 5, "bf16", False), (2048, 264, 64, 8, "bf16", True),
+    (2048, 264, 64, 9, "bf16", False),
     # the row-major gate at exactly 64 experts, packed at 65; fp32 H split
     # four ways from H = 128
     (3000, 128, 65, 3, "bf16", True), (3000, 128, 64, 3, "bf16", True),
